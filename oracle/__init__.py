@@ -1,0 +1,18 @@
+"""fp64 CPU oracle for prefix-shared tree attention (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library never calls it, and it
+shares no code with the HIP library: both consume the seeded inputs of
+``tree_inputs`` and nothing else.
+
+Parity status of each function is listed in ``oracle/path_expansion.py``.
+"""
+
+from .path_expansion import (  # noqa: F401
+    root_to_leaf_paths,
+    path_multiplicity,
+    causal_attention,
+    tree_attention,
+    query_rows,
+    key_rows,
+)
