@@ -1,0 +1,220 @@
+/*
+ * tree_attn.h -- C ABI of libtree_attn.so: causal attention forward and
+ * backward over a rollout prefix tree on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  Rollouts that share prefixes form a tree whose
+ * root-to-leaf paths are the trajectories (AReaL-DTA, abstract; HARTS,
+ * abstract).  Every unique token is stored once.  A token attends to itself
+ * and to every token before it on its root-to-leaf path: all tokens of its
+ * node's proper ancestors and the earlier tokens of its own node.  The
+ * results equal those of running each trajectory separately through ordinary
+ * causal attention, while each shared prefix is computed once in the forward
+ * and once in the backward pass (Tree Training, listed on the HARTS page:
+ * compute each shared prefix once and reuse it in both passes).  In the
+ * backward pass the gradients of a shared token's K and V are the sums over
+ * every descendant branch.  All branches go through one packed call per
+ * pass (HARTS, abstract: one packed call per round over all branches), and
+ * the loss sees only per-unique-token outputs, so an RL objective keeps its
+ * interface (HARTS, abstract).
+ *
+ * Conventions used by every entry point:
+ *   N    number of unique (packed) tokens      M    number of tree nodes
+ *   Hq   query heads   Hkv  key/value heads    G = Hq / Hkv (GQA group size)
+ *   D    head dimension (64 or 128)
+ *   Q, O, dO, dQ : [N, Hq, D]   row-major, contiguous, element type `dtype`
+ *   K, V, dK, dV : [N, Hkv, D]  row-major, contiguous, element type `dtype`
+ *   LSE          : [Hq, N] fp32, natural log of sum_j exp(scale * q . k_j)
+ *   query head h reads key/value head h / G.
+ *   Pointers to tensors are device pointers owned by the caller; the library
+ *   never frees or retains them past the call.  Calls enqueue work on the
+ *   given HIP stream and return without synchronising; kernel faults surface
+ *   at the caller's next synchronisation.
+ *
+ * Errors: every entry point returns a tree_attn_status_t.  Invalid arguments
+ * are rejected before any device work is enqueued; the reason is available
+ * from tree_attn_last_error() on the calling thread.  No C++ exception or
+ * abort crosses this interface.
+ */
+#ifndef TREE_ATTN_H_
+#define TREE_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TREE_ATTN_OK = 0,
+  TREE_ATTN_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad plan  */
+  TREE_ATTN_ERR_BAD_TREE = 2,     /* parent out of range, self loop, cycle  */
+  TREE_ATTN_ERR_LAYOUT = 3,       /* segments overlap, leave gaps, len < 1  */
+  TREE_ATTN_ERR_UNSUPPORTED = 4,  /* head_dim, dtype or head counts         */
+  TREE_ATTN_ERR_WORKSPACE = 5,    /* workspace missing or too small         */
+  TREE_ATTN_ERR_HIP = 6,          /* a HIP runtime call failed              */
+  TREE_ATTN_ERR_NO_DEVICE_PLAN = 7 /* host-only plan passed to fwd/bwd      */
+} tree_attn_status_t;
+
+typedef enum { TREE_ATTN_BF16 = 0, TREE_ATTN_FP32 = 1 } tree_attn_dtype_t;
+
+typedef struct tree_attn_plan_s* tree_attn_plan_t; /* opaque, immutable */
+
+/*
+ * tree_attn_plan -- validate a node table and build the work plan.
+ *
+ * The node table describes the rollout prefix tree (AReaL-DTA, abstract:
+ * prefix sharing induces a tree over rollouts; HARTS, abstract: planning on
+ * the compact-token work left after prefix compression).  It is read on the
+ * host during this call only:
+ *   parent[i]     parent node of node i, or -1 for a root (a forest of
+ *                 independent trees is allowed);
+ *   seg_start[i]  first packed row of node i's tokens;
+ *   seg_len[i]    number of tokens of node i, >= 1.
+ * The segments must partition [0, num_tokens) exactly; node order and
+ * packing order are otherwise free.  num_nodes == 0 requires
+ * num_tokens == 0 (an empty batch; fwd/bwd then enqueue nothing).
+ *
+ * The plan holds the work items of the forward pass (query tiles with the
+ * key ranges of their ancestors) and of the backward pass (key tiles with
+ * the query ranges of their descendants), ordered longest first.  Its small
+ * device arrays are copied asynchronously on `stream`; the plan may be used
+ * on any stream once `stream` has passed this point, and reused by any
+ * number of fwd/bwd calls (e.g. every layer of a model).
+ *
+ * Returns BAD_TREE or LAYOUT for an invalid table, UNSUPPORTED when
+ * head_dim is not 64 or 128, dtype is unknown, or num_q_heads is not a
+ * positive multiple of num_kv_heads; INVALID_ARG for null pointers or
+ * negative sizes; HIP when device allocation or copy fails.  *out is set
+ * only on success.
+ */
+tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_start,
+                                  const int32_t* seg_len, int32_t num_nodes,
+                                  int32_t num_tokens, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  tree_attn_dtype_t dtype, hipStream_t stream,
+                                  tree_attn_plan_t* out);
+
+/*
+ * tree_attn_plan_host -- the same validation and planning as tree_attn_plan
+ * without touching any GPU.  The resulting plan can be inspected
+ * (tree_attn_plan_stats, tree_attn_plan_export) and sized
+ * (tree_attn_workspace_size) but fwd/bwd reject it with NO_DEVICE_PLAN.
+ * `num_cus` is the compute-unit count the load balancer plans for (256 on
+ * MI355X; values < 1 mean 256).
+ */
+tree_attn_status_t tree_attn_plan_host(const int32_t* parent, const int32_t* seg_start,
+                                       const int32_t* seg_len, int32_t num_nodes,
+                                       int32_t num_tokens, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       tree_attn_dtype_t dtype, int32_t num_cus,
+                                       tree_attn_plan_t* out);
+
+/* Release a plan and its device arrays.  Null is ignored.  The caller must
+ * ensure no enqueued fwd/bwd still uses the plan (synchronise first). */
+void tree_attn_plan_destroy(tree_attn_plan_t plan);
+
+/*
+ * tree_attn_workspace_size -- bytes of device workspace fwd and bwd need.
+ * The backward workspace holds an fp32 dQ accumulator [N, Hq, D], the fp32
+ * row terms D_t = dO_t . O_t [Hq, N] and fp32 partial dK/dV slots of key
+ * tiles whose descendant work was split for load balance.  The forward pass
+ * currently needs none (fwd_bytes = 0).  Either pointer may be null.
+ */
+tree_attn_status_t tree_attn_workspace_size(tree_attn_plan_t plan, size_t* fwd_bytes,
+                                            size_t* bwd_bytes);
+
+/*
+ * tree_attn_fwd -- forward pass.  For every unique token t and query head h:
+ *   s_j = scale * q_{t,h} . k_{j,h/G} over the tokens j that t attends to,
+ *   O_{t,h} = sum_j softmax(s)_j v_{j,h/G},   LSE_{h,t} = log sum_j exp(s_j).
+ * q, k, v: device inputs in the plan's dtype; o: device output [N,Hq,D]
+ * (same dtype, overwritten); lse: device output [Hq,N] fp32 (overwritten).
+ * ws/ws_bytes: device workspace of at least fwd_bytes (may be null when 0).
+ * The softmax scale is typically 1/sqrt(D).  Accumulation is fp32; bf16
+ * outputs are rounded to nearest even.
+ */
+tree_attn_status_t tree_attn_fwd(tree_attn_plan_t plan, const void* q, const void* k,
+                                 const void* v, float softmax_scale, void* o, float* lse,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * tree_attn_bwd -- backward pass of tree_attn_fwd.
+ * dout [N,Hq,D] is the total upstream gradient of each unique output row (a
+ * caller that holds per-trajectory gradients sums them per unique token
+ * first).  o and lse are the forward outputs.  dq [N,Hq,D], dk and dv
+ * [N,Hkv,D] receive the exact gradients with respect to the unique q, k, v:
+ * dK and dV of a shared token are summed over every branch below it and over
+ * the G query heads of its group.  Outputs are overwritten, not accumulated.
+ * ws must hold at least bwd_bytes.  dK and dV are computed without atomics
+ * and are bitwise reproducible; dQ is accumulated with fp32 atomics and may
+ * differ in the last bits between runs.
+ */
+tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const void* k,
+                                 const void* v, const void* o, const float* lse,
+                                 const void* dout, float softmax_scale, void* dq, void* dk,
+                                 void* dv, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Plan statistics for reports and tests (host values, no device access). */
+typedef struct {
+  int64_t num_tokens, num_nodes, num_q_heads, num_kv_heads, head_dim;
+  int64_t pairs;            /* sum over tokens of (ancestor tokens + 1)     */
+  int64_t fwd_tiles;        /* query tiles (per head)                       */
+  int64_t fwd_ranges;       /* key ranges over all query tiles              */
+  int64_t fwd_blocks;       /* workgroups of one forward launch             */
+  int64_t bwd_items;        /* key-tile work items (incl. split chunks)     */
+  int64_t bwd_entries;      /* (head, query range) entries over all items   */
+  int64_t bwd_split_tiles;  /* key tiles whose work was split               */
+  int64_t bwd_slots;        /* fp32 partial dK/dV slots                     */
+  int64_t fwd_tile_rows;    /* query rows per forward tile                  */
+  int64_t fwd_tile_keys;    /* keys per forward key step                    */
+  int64_t bwd_tile_keys;    /* keys per backward key tile                   */
+  int64_t bwd_block_rows;   /* query rows per backward step                 */
+} tree_attn_plan_stats_t;
+
+tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_stats_t* out);
+
+/*
+ * tree_attn_plan_export -- copy the plan's host work arrays (for tests and
+ * debugging).  Each array is int32, row-major with the given number of
+ * columns; pass null to skip one, and the *_count outputs to size buffers:
+ *   fwd_tiles  [fwd_tiles, 4]  : q0, q1, range_begin, range_end
+ *   fwd_ranges [fwd_ranges, 4] : k0, k1, causal, 0
+ *   bwd_items  [bwd_items, 8]  : k0, k1, kv_head, entry_begin, entry_end,
+ *                                slot (-1 = writes dK/dV directly), 0, 0
+ *   bwd_entries[bwd_entries, 4]: q_head, q0, q1, causal
+ * A causal range applies the mask key <= query; a query sees a key in a
+ * non-causal range unconditionally (range rows are ancestors/descendants).
+ */
+tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_tiles,
+                                         int32_t* fwd_ranges, int32_t* bwd_items,
+                                         int32_t* bwd_entries);
+
+/*
+ * Kernel timing for benchmarks and reports.  While enabled, every kernel
+ * that fwd/bwd launch is bracketed by HIP events on the call's stream (no
+ * host synchronisation).  tree_attn_timing_read waits for the recorded
+ * events, and returns per kernel kind the number of launches and their summed
+ * duration in milliseconds since the last reset (reset != 0 clears them).
+ * Kinds: 0 forward, 1 backward preprocess, 2 backward main, 3 backward
+ * reduction + dQ conversion.  Timing is process-wide and not meant for
+ * concurrent callers.
+ */
+typedef struct {
+  int64_t launches[4];
+  double total_ms[4];
+} tree_attn_timing_t;
+
+tree_attn_status_t tree_attn_timing_enable(int enable);
+tree_attn_status_t tree_attn_timing_read(tree_attn_timing_t* out, int reset);
+
+const char* tree_attn_status_string(tree_attn_status_t status);
+const char* tree_attn_last_error(void); /* thread-local detail of the last error */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H_ */

@@ -1,0 +1,203 @@
+"""Prefix-shared tree attention on MI355X: Python binding of libtree_attn.so.
+
+Argument marshalling only: every step of planning and of the forward and
+backward passes runs in the C++/HIP library (include/tree_attn.h).  PyTorch
+provides device memory and the current HIP stream.  Importing the package
+does not need a GPU; calling ``fwd``/``bwd`` needs the built library and a
+GPU, and fails loudly otherwise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import _ffi
+from ._ffi import TreeAttnError, PlanStats  # noqa: F401
+
+__all__ = ["Plan", "plan", "plan_host", "fwd", "bwd", "workspace", "TreeAttnError",
+           "timing_enable", "timing_read"]
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+class Plan:
+    """An immutable work plan for one tree and one head configuration."""
+
+    def __init__(self, handle: int, num_tokens: int, hq: int, hkv: int, head_dim: int,
+                 dtype: str, device: Optional[int]):
+        self._h = ctypes.c_void_p(handle)
+        self.num_tokens, self.hq, self.hkv, self.head_dim = num_tokens, hq, hkv, head_dim
+        self.dtype = dtype
+        self.device = device
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if not self._h:
+            raise ValueError("plan already destroyed")
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            _ffi.lib().tree_attn_plan_destroy(self._h)
+            self._h = ctypes.c_void_p(0)
+
+    def __del__(self):  # pragma: no cover - interpreter shutdown order
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self) -> Tuple[int, int]:
+        f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        _ffi.check(_ffi.lib().tree_attn_workspace_size(self.handle, ctypes.byref(f),
+                                                       ctypes.byref(b)), "workspace_size")
+        return int(f.value), int(b.value)
+
+    def stats(self) -> dict:
+        s = PlanStats()
+        _ffi.check(_ffi.lib().tree_attn_plan_stats(self.handle, ctypes.byref(s)), "plan_stats")
+        return {name: int(getattr(s, name)) for name, _ in PlanStats._fields_}
+
+    def export(self) -> dict:
+        st = self.stats()
+        out = {
+            "fwd_tiles": np.zeros((st["fwd_tiles"], 4), np.int32),
+            "fwd_ranges": np.zeros((st["fwd_ranges"], 4), np.int32),
+            "bwd_items": np.zeros((st["bwd_items"], 8), np.int32),
+            "bwd_entries": np.zeros((st["bwd_entries"], 4), np.int32),
+        }
+        _ffi.check(_ffi.lib().tree_attn_plan_export(
+            self.handle, _ptr(out["fwd_tiles"]), _ptr(out["fwd_ranges"]),
+            _ptr(out["bwd_items"]), _ptr(out["bwd_entries"])), "plan_export")
+        return out
+
+
+def _plan_args(parent, seg_start, seg_len, num_tokens, hq, hkv, head_dim, dtype):
+    par, st, ln = _i32(parent), _i32(seg_start), _i32(seg_len)
+    if not (par.shape == st.shape == ln.shape) or par.ndim != 1:
+        raise ValueError("parent, seg_start and seg_len must be 1-D of equal length")
+    if dtype not in _ffi.DTYPES:
+        raise ValueError(f"dtype must be one of {list(_ffi.DTYPES)}")
+    return par, st, ln, int(par.shape[0])
+
+
+def plan(parent, seg_start, seg_len, num_tokens: int, hq: int, hkv: int, head_dim: int,
+         dtype: str = "bf16", stream=None) -> Plan:
+    """Validates the node table and builds a device plan (tree_attn_plan)."""
+    import torch
+    par, st, ln, m = _plan_args(parent, seg_start, seg_len, num_tokens, hq, hkv, head_dim, dtype)
+    h = ctypes.c_void_p(0)
+    _ffi.check(_ffi.lib().tree_attn_plan(
+        _ptr(par), _ptr(st), _ptr(ln), m, int(num_tokens), int(hq), int(hkv), int(head_dim),
+        _ffi.DTYPES[dtype], ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(h)), "plan")
+    return Plan(h.value, int(num_tokens), hq, hkv, head_dim, dtype, torch.cuda.current_device())
+
+
+def plan_host(parent, seg_start, seg_len, num_tokens: int, hq: int, hkv: int, head_dim: int,
+              dtype: str = "bf16", num_cus: int = 256) -> Plan:
+    """Host-only plan (tree_attn_plan_host): validation, inspection, sizing."""
+    par, st, ln, m = _plan_args(parent, seg_start, seg_len, num_tokens, hq, hkv, head_dim, dtype)
+    h = ctypes.c_void_p(0)
+    _ffi.check(_ffi.lib().tree_attn_plan_host(
+        _ptr(par), _ptr(st), _ptr(ln), m, int(num_tokens), int(hq), int(hkv), int(head_dim),
+        _ffi.DTYPES[dtype], int(num_cus), ctypes.byref(h)), "plan_host")
+    return Plan(h.value, int(num_tokens), hq, hkv, head_dim, dtype, None)
+
+
+_TORCH_DTYPES = {"bf16": "bfloat16", "fp32": "float32"}
+
+
+def _check_tensor(x, name: str, shape, p: Plan):
+    import torch
+    want = getattr(torch, _TORCH_DTYPES[p.dtype]) if name != "lse" else torch.float32
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if x.device.type != "cuda" or x.device.index != p.device:
+        raise ValueError(f"{name} must live on cuda:{p.device}")
+    if x.dtype != want:
+        raise TypeError(f"{name} must be {want}, got {x.dtype}")
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def workspace(p: Plan, which: str = "bwd"):
+    """Allocates a device workspace of the size the plan asks for."""
+    import torch
+    f, b = p.workspace_size()
+    n = b if which == "bwd" else f
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=f"cuda:{p.device}")
+
+
+def fwd(p: Plan, q, k, v, scale: float, o=None, lse=None, ws=None, stream=None):
+    """tree_attn_fwd: returns (o [N,Hq,D], lse [Hq,N] fp32)."""
+    import torch
+    n, hq, hkv, d = p.num_tokens, p.hq, p.hkv, p.head_dim
+    if o is None:
+        o = torch.empty((n, hq, d), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, n), dtype=torch.float32, device=q.device)
+    args = [_check_tensor(q, "q", (n, hq, d), p), _check_tensor(k, "k", (n, hkv, d), p),
+            _check_tensor(v, "v", (n, hkv, d), p)]
+    po = _check_tensor(o, "o", (n, hq, d), p)
+    pl = _check_tensor(lse, "lse", (hq, n), p)
+    wptr, wbytes = (ctypes.c_void_p(ws.data_ptr()), ws.numel()) if ws is not None else (None, 0)
+    _ffi.check(_ffi.lib().tree_attn_fwd(p.handle, *args, ctypes.c_float(scale), po, pl, wptr,
+                                        wbytes, ctypes.c_void_p(_stream_handle(stream))), "fwd")
+    return o, lse
+
+
+def bwd(p: Plan, q, k, v, o, lse, do, scale: float, dq=None, dk=None, dv=None, ws=None,
+        stream=None):
+    """tree_attn_bwd: returns (dq, dk, dv)."""
+    import torch
+    n, hq, hkv, d = p.num_tokens, p.hq, p.hkv, p.head_dim
+    if dq is None:
+        dq = torch.empty((n, hq, d), dtype=q.dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty((n, hkv, d), dtype=q.dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((n, hkv, d), dtype=q.dtype, device=q.device)
+    if ws is None:
+        ws = workspace(p, "bwd")
+    args = [_check_tensor(q, "q", (n, hq, d), p), _check_tensor(k, "k", (n, hkv, d), p),
+            _check_tensor(v, "v", (n, hkv, d), p), _check_tensor(o, "o", (n, hq, d), p),
+            _check_tensor(lse, "lse", (hq, n), p), _check_tensor(do, "do", (n, hq, d), p)]
+    outs = [_check_tensor(dq, "dq", (n, hq, d), p), _check_tensor(dk, "dk", (n, hkv, d), p),
+            _check_tensor(dv, "dv", (n, hkv, d), p)]
+    _ffi.check(_ffi.lib().tree_attn_bwd(
+        p.handle, *args[:5], args[5], ctypes.c_float(scale), *outs,
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+        ctypes.c_void_p(_stream_handle(stream))), "bwd")
+    return dq, dk, dv
+
+
+def timing_enable(enable: bool = True) -> None:
+    """Brackets every library kernel with HIP events (tree_attn_timing_enable)."""
+    _ffi.check(_ffi.lib().tree_attn_timing_enable(1 if enable else 0), "timing_enable")
+
+
+def timing_read(reset: bool = True) -> dict:
+    """Per kernel kind: launches and summed milliseconds (tree_attn_timing_read)."""
+    t = _ffi.Timing()
+    _ffi.check(_ffi.lib().tree_attn_timing_read(ctypes.byref(t), 1 if reset else 0),
+               "timing_read")
+    return {k: {"launches": int(t.launches[i]), "total_ms": float(t.total_ms[i])}
+            for i, k in enumerate(_ffi.TIMING_KINDS)}

@@ -1,0 +1,428 @@
+// C ABI of libtree_attn.so: plan objects, argument checks and launches.
+// The operations are defined in include/tree_attn.h.
+#include "tree_attn.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "planner.h"
+
+using tree_attn::HostPlan;
+using tree_attn::I4;
+using tree_attn::I8;
+using tree_attn::Status;
+
+struct tree_attn_plan_s {
+  HostPlan hp;
+  bool has_device = false;
+  int device = -1;
+  char* dev_buf = nullptr;
+  const I4* d_fwd_tiles = nullptr;
+  const I4* d_fwd_ranges = nullptr;
+  const I8* d_bwd_items = nullptr;
+  const I4* d_bwd_entries = nullptr;
+  const I8* d_bwd_reduce = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tree_attn_status_t report(Status s, const std::string& msg) {
+  g_last_error = msg;
+  return static_cast<tree_attn_status_t>(s);
+}
+
+tree_attn_status_t report_hip(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return TREE_ATTN_ERR_HIP;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct BwdLayout {
+  size_t dq_acc = 0, dvec = 0, dk_slots = 0, dv_slots = 0, total = 0;
+};
+
+BwdLayout bwd_layout(const HostPlan& p) {
+  BwdLayout l;
+  const size_t dq = static_cast<size_t>(p.num_tokens) * p.hq * p.head_dim * 4;
+  const size_t dv = static_cast<size_t>(p.num_tokens) * p.hq * 4;
+  const size_t slot =
+      static_cast<size_t>(p.bwd_slots) * tree_attn::kBwdKeys * p.head_dim * 4;
+  l.dq_acc = 0;
+  l.dvec = align256(dq);
+  l.dk_slots = l.dvec + align256(dv);
+  l.dv_slots = l.dk_slots + align256(slot);
+  l.total = l.dv_slots + align256(slot);
+  if (p.num_tokens == 0) l.total = 0;
+  return l;
+}
+
+tree_attn_status_t make_host_plan(const int32_t* parent, const int32_t* seg_start,
+                                  const int32_t* seg_len, int32_t num_nodes, int32_t num_tokens,
+                                  int32_t hq, int32_t hkv, int32_t head_dim,
+                                  tree_attn_dtype_t dtype, int num_cus, tree_attn_plan_s** out) {
+  if (!out) return report(Status::kInvalidArg, "null output plan pointer");
+  tree_attn_plan_s* p = new (std::nothrow) tree_attn_plan_s();
+  if (!p) return report(Status::kInvalidArg, "out of host memory");
+  std::string err;
+  const Status s = tree_attn::build_plan(parent, seg_start, seg_len, num_nodes, num_tokens, hq,
+                                         hkv, head_dim, static_cast<int>(dtype), num_cus,
+                                         &p->hp, &err);
+  if (s != Status::kOk) {
+    delete p;
+    return report(s, err);
+  }
+  *out = p;
+  return TREE_ATTN_OK;
+}
+
+template <typename V>
+size_t bytes_of(const V& v) {
+  return v.size() * sizeof(typename V::value_type);
+}
+
+// Optional per-kernel timing: HIP events around each launch, read later.
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<hipEvent_t> pool;
+  struct Rec {
+    int kind;
+    hipEvent_t start, stop;
+  };
+  std::vector<Rec> recs;
+  int64_t launches[4] = {0, 0, 0, 0};
+  double total_ms[4] = {0, 0, 0, 0};
+};
+
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+hipEvent_t take_event(Timing& t) {
+  hipEvent_t e = nullptr;
+  if (!t.pool.empty()) {
+    e = t.pool.back();
+    t.pool.pop_back();
+  } else if (hipEventCreate(&e) != hipSuccess) {
+    e = nullptr;
+  }
+  return e;
+}
+
+template <class F>
+hipError_t timed(int kind, hipStream_t s, F&& launch) {
+  Timing& t = timing();
+  hipEvent_t a = nullptr, b = nullptr;
+  {
+    std::lock_guard<std::mutex> g(t.mu);
+    if (t.enabled) {
+      a = take_event(t);
+      b = take_event(t);
+    }
+  }
+  if (!a || !b) return launch();
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  const hipError_t e2 = hipEventRecord(b, s);
+  std::lock_guard<std::mutex> g(t.mu);
+  t.recs.push_back({kind, a, b});
+  return e != hipSuccess ? e : e2;
+}
+
+tree_attn_status_t check_device(const tree_attn_plan_s* p) {
+  if (!p) return report(Status::kInvalidArg, "null plan");
+  if (!p->has_device)
+    return report(Status::kNoDevicePlan, "plan was built with tree_attn_plan_host");
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return report_hip(e, "hipGetDevice");
+  if (dev != p->device)
+    return report(Status::kInvalidArg, "plan belongs to device " + std::to_string(p->device) +
+                                           ", current device is " + std::to_string(dev));
+  return TREE_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tree_attn_status_t tree_attn_plan_host(const int32_t* parent, const int32_t* seg_start,
+                                       const int32_t* seg_len, int32_t num_nodes,
+                                       int32_t num_tokens, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       tree_attn_dtype_t dtype, int32_t num_cus,
+                                       tree_attn_plan_t* out) {
+  return make_host_plan(parent, seg_start, seg_len, num_nodes, num_tokens, num_q_heads,
+                        num_kv_heads, head_dim, dtype, num_cus, out);
+}
+
+tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_start,
+                                  const int32_t* seg_len, int32_t num_nodes,
+                                  int32_t num_tokens, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  tree_attn_dtype_t dtype, hipStream_t stream,
+                                  tree_attn_plan_t* out) {
+  if (!out) return report(Status::kInvalidArg, "null output plan pointer");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return report_hip(e, "hipGetDevice");
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return report_hip(e, "hipDeviceGetAttribute");
+  tree_attn_plan_s* p = nullptr;
+  tree_attn_status_t st = make_host_plan(parent, seg_start, seg_len, num_nodes, num_tokens,
+                                         num_q_heads, num_kv_heads, head_dim, dtype, cus, &p);
+  if (st != TREE_ATTN_OK) return st;
+  const HostPlan& hp = p->hp;
+  const size_t o_ft = 0;
+  const size_t o_fr = o_ft + align256(bytes_of(hp.fwd_tiles));
+  const size_t o_bi = o_fr + align256(bytes_of(hp.fwd_ranges));
+  const size_t o_be = o_bi + align256(bytes_of(hp.bwd_items));
+  const size_t o_br = o_be + align256(bytes_of(hp.bwd_entries));
+  const size_t total = o_br + align256(bytes_of(hp.bwd_reduce));
+  if (total > 0) {
+    e = hipMalloc(reinterpret_cast<void**>(&p->dev_buf), total);
+    if (e != hipSuccess) {
+      delete p;
+      return report_hip(e, "hipMalloc(plan arrays)");
+    }
+    struct Part {
+      size_t off;
+      const void* src;
+      size_t n;
+    } parts[] = {{o_ft, hp.fwd_tiles.data(), bytes_of(hp.fwd_tiles)},
+                 {o_fr, hp.fwd_ranges.data(), bytes_of(hp.fwd_ranges)},
+                 {o_bi, hp.bwd_items.data(), bytes_of(hp.bwd_items)},
+                 {o_be, hp.bwd_entries.data(), bytes_of(hp.bwd_entries)},
+                 {o_br, hp.bwd_reduce.data(), bytes_of(hp.bwd_reduce)}};
+    for (const Part& part : parts) {
+      if (part.n == 0) continue;
+      e = hipMemcpyAsync(p->dev_buf + part.off, part.src, part.n, hipMemcpyHostToDevice, stream);
+      if (e != hipSuccess) {
+        (void)hipFree(p->dev_buf);
+        delete p;
+        return report_hip(e, "hipMemcpyAsync(plan arrays)");
+      }
+    }
+  }
+  p->d_fwd_tiles = reinterpret_cast<const I4*>(p->dev_buf + o_ft);
+  p->d_fwd_ranges = reinterpret_cast<const I4*>(p->dev_buf + o_fr);
+  p->d_bwd_items = reinterpret_cast<const I8*>(p->dev_buf + o_bi);
+  p->d_bwd_entries = reinterpret_cast<const I4*>(p->dev_buf + o_be);
+  p->d_bwd_reduce = reinterpret_cast<const I8*>(p->dev_buf + o_br);
+  p->has_device = true;
+  p->device = dev;
+  *out = p;
+  return TREE_ATTN_OK;
+}
+
+void tree_attn_plan_destroy(tree_attn_plan_t plan) {
+  if (!plan) return;
+  if (plan->dev_buf) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != plan->device) (void)hipSetDevice(plan->device);
+    (void)hipFree(plan->dev_buf);
+    if (cur != plan->device && cur >= 0) (void)hipSetDevice(cur);
+  }
+  delete plan;
+}
+
+tree_attn_status_t tree_attn_workspace_size(tree_attn_plan_t plan, size_t* fwd_bytes,
+                                            size_t* bwd_bytes) {
+  if (!plan) return report(Status::kInvalidArg, "null plan");
+  if (fwd_bytes) *fwd_bytes = 0;
+  if (bwd_bytes) *bwd_bytes = bwd_layout(plan->hp).total;
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_fwd(tree_attn_plan_t plan, const void* q, const void* k,
+                                 const void* v, float softmax_scale, void* o, float* lse,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  tree_attn_status_t st = check_device(plan);
+  if (st != TREE_ATTN_OK) return st;
+  const HostPlan& hp = plan->hp;
+  if (hp.num_tokens == 0) return TREE_ATTN_OK;
+  if (!q || !k || !v || !o || !lse) return report(Status::kInvalidArg, "null tensor pointer");
+  if (!std::isfinite(softmax_scale))
+    return report(Status::kInvalidArg, "softmax_scale must be finite");
+  tree_attn::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.tiles = plan->d_fwd_tiles;
+  a.ranges = plan->d_fwd_ranges;
+  a.n_tokens = hp.num_tokens;
+  a.n_groups = hp.fwd_groups;
+  a.hq = static_cast<int>(hp.hq);
+  a.hkv = static_cast<int>(hp.hkv);
+  a.gsize = static_cast<int>(hp.hq / hp.hkv);
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  const hipError_t e = timed(0, stream, [&] {
+    return tree_attn::launch_fwd(a, hp.dtype, static_cast<int>(hp.head_dim), hp.fwd_blocks,
+                                 stream);
+  });
+  if (e != hipSuccess) return report_hip(e, "forward launch");
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const void* k,
+                                 const void* v, const void* o, const float* lse,
+                                 const void* dout, float softmax_scale, void* dq, void* dk,
+                                 void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  tree_attn_status_t st = check_device(plan);
+  if (st != TREE_ATTN_OK) return st;
+  const HostPlan& hp = plan->hp;
+  if (hp.num_tokens == 0) return TREE_ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return report(Status::kInvalidArg, "null tensor pointer");
+  if (!std::isfinite(softmax_scale))
+    return report(Status::kInvalidArg, "softmax_scale must be finite");
+  const BwdLayout l = bwd_layout(hp);
+  if (!ws || ws_bytes < l.total)
+    return report(Status::kWorkspace, "backward workspace needs " + std::to_string(l.total) +
+                                          " bytes, got " + std::to_string(ws_bytes));
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return report(Status::kWorkspace, "workspace must be 256-byte aligned");
+  char* w = static_cast<char*>(ws);
+  tree_attn::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dq_acc = reinterpret_cast<float*>(w + l.dq_acc);
+  a.dvec = reinterpret_cast<float*>(w + l.dvec);
+  a.dk_slots = reinterpret_cast<float*>(w + l.dk_slots);
+  a.dv_slots = reinterpret_cast<float*>(w + l.dv_slots);
+  a.items = plan->d_bwd_items;
+  a.entries = plan->d_bwd_entries;
+  a.reduce = plan->d_bwd_reduce;
+  a.n_tokens = hp.num_tokens;
+  a.n_items = static_cast<int64_t>(hp.bwd_items.size());
+  a.n_reduce = static_cast<int64_t>(hp.bwd_reduce.size());
+  a.hq = static_cast<int>(hp.hq);
+  a.hkv = static_cast<int>(hp.hkv);
+  a.gsize = static_cast<int>(hp.hq / hp.hkv);
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  const int hd = static_cast<int>(hp.head_dim);
+  hipError_t e = timed(1, stream, [&] { return tree_attn::launch_bwd_pre(a, hp.dtype, hd, stream); });
+  if (e != hipSuccess) return report_hip(e, "backward preprocess launch");
+  e = timed(2, stream, [&] { return tree_attn::launch_bwd_main(a, hp.dtype, hd, stream); });
+  if (e != hipSuccess) return report_hip(e, "backward launch");
+  e = timed(3, stream, [&] { return tree_attn::launch_bwd_post(a, hp.dtype, hd, stream); });
+  if (e != hipSuccess) return report_hip(e, "backward reduction launch");
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_stats_t* out) {
+  if (!plan || !out) return report(Status::kInvalidArg, "null argument");
+  const HostPlan& hp = plan->hp;
+  std::memset(out, 0, sizeof(*out));
+  out->num_tokens = hp.num_tokens;
+  out->num_nodes = hp.num_nodes;
+  out->num_q_heads = hp.hq;
+  out->num_kv_heads = hp.hkv;
+  out->head_dim = hp.head_dim;
+  out->pairs = hp.pairs;
+  out->fwd_tiles = static_cast<int64_t>(hp.fwd_tiles.size());
+  out->fwd_ranges = static_cast<int64_t>(hp.fwd_ranges.size());
+  out->fwd_blocks = hp.fwd_blocks;
+  out->bwd_items = static_cast<int64_t>(hp.bwd_items.size());
+  out->bwd_entries = static_cast<int64_t>(hp.bwd_entries.size());
+  out->bwd_split_tiles = hp.bwd_split_tiles;
+  out->bwd_slots = hp.bwd_slots;
+  out->fwd_tile_rows = tree_attn::kFwdRows;
+  out->fwd_tile_keys = tree_attn::kFwdKeys;
+  out->bwd_tile_keys = tree_attn::kBwdKeys;
+  out->bwd_block_rows = tree_attn::kBwdRows;
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_tiles,
+                                         int32_t* fwd_ranges, int32_t* bwd_items,
+                                         int32_t* bwd_entries) {
+  if (!plan) return report(Status::kInvalidArg, "null plan");
+  const HostPlan& hp = plan->hp;
+  if (fwd_tiles) std::memcpy(fwd_tiles, hp.fwd_tiles.data(), bytes_of(hp.fwd_tiles));
+  if (fwd_ranges) std::memcpy(fwd_ranges, hp.fwd_ranges.data(), bytes_of(hp.fwd_ranges));
+  if (bwd_items) std::memcpy(bwd_items, hp.bwd_items.data(), bytes_of(hp.bwd_items));
+  if (bwd_entries) std::memcpy(bwd_entries, hp.bwd_entries.data(), bytes_of(hp.bwd_entries));
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_timing_enable(int enable) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.enabled = enable != 0;
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_timing_read(tree_attn_timing_t* out, int reset) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  tree_attn_status_t st = TREE_ATTN_OK;
+  for (const Timing::Rec& r : t.recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess && st == TREE_ATTN_OK) st = report_hip(e, "timing events");
+    t.launches[r.kind] += 1;
+    t.total_ms[r.kind] += ms;
+    t.pool.push_back(r.start);
+    t.pool.push_back(r.stop);
+  }
+  t.recs.clear();
+  if (out) {
+    for (int i = 0; i < 4; ++i) {
+      out->launches[i] = t.launches[i];
+      out->total_ms[i] = t.total_ms[i];
+    }
+  }
+  if (reset) {
+    for (int i = 0; i < 4; ++i) {
+      t.launches[i] = 0;
+      t.total_ms[i] = 0;
+    }
+  }
+  return st;
+}
+
+const char* tree_attn_status_string(tree_attn_status_t s) {
+  switch (s) {
+    case TREE_ATTN_OK: return "ok";
+    case TREE_ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case TREE_ATTN_ERR_BAD_TREE: return "invalid tree (parent index or cycle)";
+    case TREE_ATTN_ERR_LAYOUT: return "invalid segment layout";
+    case TREE_ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TREE_ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case TREE_ATTN_ERR_HIP: return "HIP runtime error";
+    case TREE_ATTN_ERR_NO_DEVICE_PLAN: return "plan has no device data";
+  }
+  return "unknown status";
+}
+
+const char* tree_attn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,240 @@
+// Device helpers shared by the tree-attention kernels (gfx950 / CDNA4).
+//
+// Matrix-core conventions (v_mfma_f32_32x32x16_bf16, one 64-lane wave):
+//   A operand (32 x 16): lane l holds A[l % 32][8 * (l / 32) + s], s = 0..7
+//   B operand (16 x 32): lane l holds B[8 * (l / 32) + s][l % 32]
+//   C (32 x 32, fp32):   lane l, register v holds C[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32]
+// The reduction index k can be relabelled freely as long as A and B agree.
+//
+// ds_read_tr16_b64 (gfx950): in each group of 16 lanes, lane L supplies the
+// address of 4 consecutive 16-bit elements; lane j of the group receives
+// element j % 4 of the address given by lane 4 * i + j / 4 as its element i.
+// Reading a row-major [row][col] tile with lane L pointing at
+// (row0 + L / 4, col0 + 4 * (L % 4)) therefore returns, in lane j, the
+// column col0 + j of rows row0 .. row0 + 3: a transposed operand straight
+// from a row-major tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tree_attn {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+
+#define LDS_PTR(T) __attribute__((address_space(3))) T*
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// An MFMA operand fragment.  For fp32 inputs a value x is carried as
+// hi = bf16(x) and lo = bf16(x - hi) and products use hi*hi + hi*lo + lo*hi,
+// the split-bf16 emulation of fp32 products (Henry, Tang, Heinecke,
+// "Leveraging the bfloat16 Artificial Intelligence Datatype For
+// Higher-Precision Computations", ARITH 2019): about 16 mantissa bits.
+template <bool SPLIT>
+struct Frag;
+template <>
+struct Frag<false> {
+  bf16x8 h;
+};
+template <>
+struct Frag<true> {
+  bf16x8 h, l;
+};
+
+template <bool SPLIT>
+__device__ __forceinline__ void mma(f32x16& c, const Frag<SPLIT>& a, const Frag<SPLIT>& b) {
+  c = mfma32(a.h, b.h, c);
+  if constexpr (SPLIT) {
+    c = mfma32(a.h, b.l, c);
+    c = mfma32(a.l, b.h, c);
+  }
+}
+
+__device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
+
+// Packs eight fp32 values into an operand fragment (hi, and lo when split).
+template <bool SPLIT>
+__device__ __forceinline__ Frag<SPLIT> pack8(const float* x) {
+  Frag<SPLIT> f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const __bf16 hi = to_bf16(x[s]);
+    f.h[s] = hi;
+    if constexpr (SPLIT) f.l[s] = to_bf16(x[s] - static_cast<float>(hi));
+  }
+  return f;
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles of bf16 rows with D columns.  16-byte chunk c of row r is stored
+// at chunk c ^ swz(r).  The swizzle makes both access patterns of the kernels
+// free of bank conflicts: 16 lanes reading the same chunk of 16 consecutive
+// rows (row operands, ds_read_b128), and 16-lane transpose reads of 4
+// consecutive rows x 32 bytes (ds_read_tr16_b64).
+template <int D>
+struct TileLayout {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;
+  __device__ __forceinline__ static int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+  // byte offset of the 16-byte chunk c of row r
+  __device__ __forceinline__ static int chunk_off(int r, int c) {
+    return r * kRowBytes + ((c ^ swz(r)) << 4);
+  }
+  // byte offset of element col of row r (col a multiple of 4 for 8-byte reads)
+  __device__ __forceinline__ static int elem_off(int r, int col) {
+    return r * kRowBytes + (((col >> 3) ^ swz(r)) << 4) + ((col & 7) << 1);
+  }
+};
+
+__device__ __forceinline__ bf16x8 lds_read16(const LDS_PTR(char) base, int off) {
+  return *reinterpret_cast<const LDS_PTR(bf16x8)>(base + off);
+}
+__device__ __forceinline__ void lds_write16(LDS_PTR(char) base, int off, const i32x4& v) {
+  *reinterpret_cast<LDS_PTR(i32x4)>(base + off) = v;
+}
+__device__ __forceinline__ bf16x4 lds_read_tr(const LDS_PTR(char) base, int off) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<LDS_PTR(s16x4)>(const_cast<LDS_PTR(char)>(base) + off));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Transposed operand from a row-major LDS tile: returns, for this lane, the 8
+// values tile[row0 + 8 * (lane / 32) + s][col0 + (lane % 32)], s = 0..7 --
+// i.e. an MFMA operand whose lane index runs along the tile's columns and
+// whose reduction slots run along its rows.  `row0` must be a multiple of 8
+// and `col0` a multiple of 32.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const LDS_PTR(char) base, int row0, int col0,
+                                             int lane) {
+  const int grp = lane >> 4, L = lane & 15;
+  const int r = row0 + 8 * (grp >> 1) + (L >> 2);
+  const int c = col0 + 16 * (grp & 1) + 4 * (L & 3);
+  const bf16x4 lo = lds_read_tr(base, TileLayout<D>::elem_off(r, c));
+  const bf16x4 hi = lds_read_tr(base, TileLayout<D>::elem_off(r + 4, c));
+  bf16x8 out;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    out[s] = lo[s];
+    out[s + 4] = hi[s];
+  }
+  return out;
+}
+
+// Row operand from a row-major LDS tile: the 8 values tile[row][c8 * 8 + s].
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const LDS_PTR(char) base, int row, int c8) {
+  return lds_read16(base, TileLayout<D>::chunk_off(row, c8));
+}
+
+// Row index used for the A operand so that output register v of lane half h
+// corresponds to row 16 * (v / 8) + 8 * h + v % 8: bits 2 and 3 of the MFMA
+// row are swapped.  With it, the 16 fp32 outputs of a lane split into two
+// halves of 8 consecutive reduction indices, which is exactly the B/A operand
+// slot order of a following MFMA that reduces over that dimension.
+__device__ __forceinline__ int swap23(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Global memory helpers -----------------------------------------------------
+__device__ __forceinline__ i32x4 gload16(const void* p) {
+  return *reinterpret_cast<const i32x4*>(p);
+}
+
+// 8 consecutive elements of a global row as an operand fragment.
+__device__ __forceinline__ Frag<false> load_frag8(const __bf16* p) {
+  Frag<false> f;
+  f.h = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+__device__ __forceinline__ Frag<true> load_frag8(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return pack8<true>(x);
+}
+
+// Copies rows [row0, row0 + ROWS) of a global tensor (D elements per row
+// starting at `base`, rows `row_stride` elements apart) into a bf16 LDS tile,
+// and for fp32 inputs also the low-order plane (x - bf16(x)).  Rows past
+// `last_row` are clamped to it; callers mask their contributions.  All
+// global loads are issued before the LDS writes.
+template <typename T, int D, int ROWS, int NT>
+__device__ __forceinline__ void load_tile(LDS_PTR(char) hi, LDS_PTR(char) lo, const T* base,
+                                          int64_t row_stride, int64_t row0, int64_t last_row,
+                                          int tid) {
+  constexpr int EPC = 16 / static_cast<int>(sizeof(T));
+  constexpr int CPR = D / EPC;
+  constexpr int TOTAL = ROWS * CPR;
+  static_assert(TOTAL % NT == 0, "tile chunks must divide evenly among threads");
+  constexpr int PER = TOTAL / NT;
+  i32x4 v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + i * NT;
+    const int r = c / CPR, cc = c % CPR;
+    const int64_t row = row0 + r < last_row ? row0 + r : last_row;
+    v[i] = gload16(base + row * row_stride + cc * EPC);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + i * NT;
+    const int r = c / CPR, cc = c % CPR;
+    if constexpr (sizeof(T) == 2) {
+      lds_write16(hi, TileLayout<D>::chunk_off(r, cc), v[i]);
+    } else {
+      const f32x4 f = __builtin_bit_cast(f32x4, v[i]);
+      bf16x4 h, l;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        h[s] = to_bf16(f[s]);
+        l[s] = to_bf16(f[s] - static_cast<float>(h[s]));
+      }
+      *reinterpret_cast<LDS_PTR(bf16x4)>(hi + TileLayout<D>::elem_off(r, cc * 4)) = h;
+      *reinterpret_cast<LDS_PTR(bf16x4)>(lo + TileLayout<D>::elem_off(r, cc * 4)) = l;
+    }
+  }
+}
+
+// Stores four consecutive fp32 values as output elements.
+__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
+  bf16x4 x;
+  x[0] = to_bf16(a);
+  x[1] = to_bf16(b);
+  x[2] = to_bf16(c);
+  x[3] = to_bf16(d);
+  *reinterpret_cast<bf16x4*>(p) = x;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  f32x4 x;
+  x[0] = a;
+  x[1] = b;
+  x[2] = c;
+  x[3] = d;
+  *reinterpret_cast<f32x4*>(p) = x;
+}
+
+template <typename T>
+struct IsSplit {
+  static constexpr bool value = false;
+};
+template <>
+struct IsSplit<float> {
+  static constexpr bool value = true;
+};
+
+}  // namespace tree_attn

@@ -1,0 +1,288 @@
+// Host planner: node-table validation and work-item construction.
+// The prefix tree (AReaL-DTA, abstract) is turned into forward query tiles
+// with ancestor key ranges and backward key tiles with descendant query
+// ranges; work is balanced on compact-token work (HARTS, abstract).
+#include "planner.h"
+
+#include <algorithm>
+#include <numeric>
+#include <sstream>
+
+namespace tree_attn {
+namespace {
+
+struct Range {
+  int64_t b, e;  // [b, e)
+};
+
+// Appends [b, e) to a list of ranges, merging with the last range when the
+// two are contiguous in memory.
+void push_range(std::vector<Range>& v, int64_t b, int64_t e) {
+  if (!v.empty() && v.back().e == b) {
+    v.back().e = e;
+  } else {
+    v.push_back({b, e});
+  }
+}
+
+Status fail(std::string* err, Status s, const std::string& msg) {
+  if (err) *err = msg;
+  return s;
+}
+
+}  // namespace
+
+Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                  int32_t num_nodes, int32_t num_tokens, int32_t num_q_heads,
+                  int32_t num_kv_heads, int32_t head_dim, int dtype, int num_cus,
+                  HostPlan* out, std::string* err) {
+  if (!out) return fail(err, Status::kInvalidArg, "null output plan");
+  if (num_nodes < 0 || num_tokens < 0)
+    return fail(err, Status::kInvalidArg, "negative num_nodes or num_tokens");
+  if (num_nodes > 0 && (!parent || !seg_start || !seg_len))
+    return fail(err, Status::kInvalidArg, "null node-table pointer");
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0)
+    return fail(err, Status::kUnsupported,
+                "num_q_heads must be a positive multiple of num_kv_heads");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(err, Status::kUnsupported, "head_dim must be 64 or 128");
+  if (dtype != 0 && dtype != 1) return fail(err, Status::kUnsupported, "unknown dtype");
+  if (num_nodes == 0 && num_tokens != 0)
+    return fail(err, Status::kLayout, "tokens given but no nodes");
+
+  const int64_t m = num_nodes, n = num_tokens;
+  HostPlan& p = *out;
+  p = HostPlan();
+  p.num_tokens = n;
+  p.num_nodes = m;
+  p.hq = num_q_heads;
+  p.hkv = num_kv_heads;
+  p.head_dim = head_dim;
+  p.dtype = dtype;
+  p.num_cus = num_cus > 0 ? num_cus : 256;
+  if (m == 0) return Status::kOk;
+
+  // ---- validation: parents, segment lengths, exact partition of [0, N)
+  for (int64_t i = 0; i < m; ++i) {
+    const int32_t pa = parent[i];
+    if (pa < -1 || pa >= m || pa == i) {
+      std::ostringstream os;
+      os << "node " << i << " has invalid parent " << pa;
+      return fail(err, Status::kBadTree, os.str());
+    }
+    if (seg_len[i] < 1 || seg_start[i] < 0 ||
+        static_cast<int64_t>(seg_start[i]) + seg_len[i] > n) {
+      std::ostringstream os;
+      os << "node " << i << " has segment [" << seg_start[i] << ", +" << seg_len[i]
+         << ") outside [0, " << n << ") or empty";
+      return fail(err, Status::kLayout, os.str());
+    }
+  }
+  std::vector<int32_t> by_start(m);
+  std::iota(by_start.begin(), by_start.end(), 0);
+  std::sort(by_start.begin(), by_start.end(),
+            [&](int32_t a, int32_t b) { return seg_start[a] < seg_start[b]; });
+  int64_t pos = 0;
+  for (int32_t i : by_start) {
+    if (seg_start[i] != pos) {
+      std::ostringstream os;
+      os << "segments do not tile [0, N): expected a segment at row " << pos
+         << ", found node " << i << " at " << seg_start[i];
+      return fail(err, Status::kLayout, os.str());
+    }
+    pos += seg_len[i];
+  }
+  if (pos != n) return fail(err, Status::kLayout, "segments do not cover [0, N)");
+
+  // ---- children and a root-first order; nodes unreachable from a root lie
+  // on a cycle
+  std::vector<std::vector<int32_t>> children(m);
+  std::vector<int32_t> order;
+  order.reserve(m);
+  for (int64_t i = 0; i < m; ++i) {
+    if (parent[i] >= 0) children[parent[i]].push_back(static_cast<int32_t>(i));
+    else order.push_back(static_cast<int32_t>(i));
+  }
+  for (size_t h = 0; h < order.size(); ++h)
+    for (int32_t c : children[order[h]]) order.push_back(c);
+  if (static_cast<int64_t>(order.size()) != m)
+    return fail(err, Status::kBadTree, "parent pointers contain a cycle");
+
+  // ---- ancestor key ranges (root first, merged when contiguous) and depth
+  // offsets, in root-first order so a parent is done before its children
+  std::vector<std::vector<Range>> anc(m);
+  std::vector<int64_t> depth(m, 0);
+  for (int32_t i : order) {
+    const int32_t pa = parent[i];
+    if (pa < 0) continue;
+    anc[i] = anc[pa];
+    push_range(anc[i], seg_start[pa], static_cast<int64_t>(seg_start[pa]) + seg_len[pa]);
+    depth[i] = depth[pa] + seg_len[pa];
+  }
+  p.pairs = 0;
+  for (int64_t i = 0; i < m; ++i) {
+    const int64_t L = seg_len[i];
+    p.pairs += L * depth[i] + L * (L + 1) / 2;
+  }
+
+  // ---- forward query tiles
+  struct FTile {
+    I4 t;
+    int64_t cost;
+  };
+  std::vector<FTile> ftiles;
+  std::vector<I4> franges;
+  for (int64_t i = 0; i < m; ++i) {
+    const int64_t s = seg_start[i], e = s + seg_len[i];
+    for (int64_t r0 = s; r0 < e; r0 += kFwdRows) {
+      const int64_t r1 = std::min<int64_t>(e, r0 + kFwdRows);
+      const int32_t rb = static_cast<int32_t>(franges.size());
+      int64_t keys = 0;
+      const auto& a = anc[i];
+      for (size_t j = 0; j < a.size(); ++j) {
+        const bool last = j + 1 == a.size();
+        if (last && a[j].e == s) break;  // merged into the causal range below
+        franges.push_back({static_cast<int32_t>(a[j].b), static_cast<int32_t>(a[j].e), 0, 0});
+        keys += a[j].e - a[j].b;
+      }
+      const int64_t cb = (!a.empty() && a.back().e == s) ? a.back().b : s;
+      franges.push_back({static_cast<int32_t>(cb), static_cast<int32_t>(r1), 1, 0});
+      keys += r1 - cb;
+      ftiles.push_back({{static_cast<int32_t>(r0), static_cast<int32_t>(r1), rb,
+                         static_cast<int32_t>(franges.size())},
+                        (r1 - r0) * keys});
+    }
+  }
+  std::stable_sort(ftiles.begin(), ftiles.end(),
+                   [](const FTile& a, const FTile& b) { return a.cost > b.cost; });
+  p.fwd_tiles.reserve(ftiles.size());
+  for (auto& t : ftiles) p.fwd_tiles.push_back(t.t);
+  p.fwd_ranges = std::move(franges);
+  const int64_t gsize = num_q_heads / num_kv_heads;
+  p.fwd_groups = static_cast<int64_t>(p.fwd_tiles.size()) * num_kv_heads;
+  p.fwd_blocks = ((p.fwd_groups + kXcds - 1) / kXcds) * kXcds * gsize;
+
+  // ---- backward key tiles with descendant query ranges
+  // descendant segments of each node, sorted by start and merged
+  std::vector<std::vector<Range>> desc(m);
+  {
+    std::vector<int32_t> stack;
+    for (int64_t i = 0; i < m; ++i) {
+      std::vector<Range> segs;
+      stack.assign(children[i].begin(), children[i].end());
+      while (!stack.empty()) {
+        const int32_t c = stack.back();
+        stack.pop_back();
+        segs.push_back({seg_start[c], static_cast<int64_t>(seg_start[c]) + seg_len[c]});
+        for (int32_t cc : children[c]) stack.push_back(cc);
+      }
+      std::sort(segs.begin(), segs.end(), [](const Range& a, const Range& b) { return a.b < b.b; });
+      for (auto& r : segs) push_range(desc[i], r.b, r.e);
+    }
+  }
+  struct BItem {
+    int64_t k0, k1, g, slot;
+    std::vector<I4> entries;
+    int64_t cost;
+  };
+  std::vector<BItem> items;
+  int64_t total_cost = 0;
+  struct KTile {
+    int64_t k0, k1;
+    std::vector<Range> causal, full;  // query ranges
+    int64_t rows;
+  };
+  std::vector<KTile> ktiles;
+  for (int64_t i = 0; i < m; ++i) {
+    const int64_t s = seg_start[i], e = s + seg_len[i];
+    for (int64_t k0 = s; k0 < e; k0 += kBwdKeys) {
+      KTile kt;
+      kt.k0 = k0;
+      kt.k1 = std::min<int64_t>(e, k0 + kBwdKeys);
+      // own node from the tile's first row on (causal), merged with the
+      // descendants that follow it contiguously in memory
+      Range own{k0, e};
+      size_t j = 0;
+      const auto& d = desc[i];
+      // descendant ranges are sorted; merge those that continue `own`
+      std::vector<Range> rest;
+      for (j = 0; j < d.size(); ++j) {
+        if (d[j].b == own.e) own.e = d[j].e;
+        else rest.push_back(d[j]);
+      }
+      kt.causal.push_back(own);
+      kt.full = rest;
+      kt.rows = own.e - own.b;
+      for (auto& r : rest) kt.rows += r.e - r.b;
+      total_cost += kt.rows * (kt.k1 - kt.k0) * gsize;
+      ktiles.push_back(std::move(kt));
+    }
+  }
+  total_cost *= num_kv_heads;
+  // Split heavy key tiles along their query rows so that no item exceeds
+  // about 1/(8 * num_cus) of the total; split chunks write fp32 partial dK/dV
+  // slots that a fixed-order reduction sums afterwards.
+  const int64_t cap = std::max<int64_t>(total_cost / (8 * static_cast<int64_t>(p.num_cus)),
+                                        static_cast<int64_t>(kBwdKeys) * kBwdRows * 64);
+  int64_t slots = 0;
+  for (const KTile& kt : ktiles) {
+    const int64_t nk = kt.k1 - kt.k0;
+    for (int64_t g = 0; g < num_kv_heads; ++g) {
+      std::vector<I4> all;
+      for (int64_t h = g * gsize; h < (g + 1) * gsize; ++h) {
+        for (auto& r : kt.causal)
+          all.push_back({static_cast<int32_t>(h), static_cast<int32_t>(r.b),
+                         static_cast<int32_t>(r.e), 1});
+        for (auto& r : kt.full)
+          all.push_back({static_cast<int32_t>(h), static_cast<int32_t>(r.b),
+                         static_cast<int32_t>(r.e), 0});
+      }
+      const int64_t cost = kt.rows * gsize * nk;
+      if (cost <= cap) {
+        items.push_back({kt.k0, kt.k1, g, -1, std::move(all), cost});
+        continue;
+      }
+      // chunk the entries (rows cut at kBwdRows boundaries of each entry)
+      const int64_t slot_begin = slots;
+      BItem cur{kt.k0, kt.k1, g, slots, {}, 0};
+      for (const I4& en : all) {
+        int64_t q0 = en.y;
+        while (q0 < en.z) {
+          const int64_t room_rows = std::max<int64_t>(
+              kBwdRows, ((cap - cur.cost) / nk + kBwdRows - 1) / kBwdRows * kBwdRows);
+          const int64_t q1 = std::min<int64_t>(en.z, q0 + room_rows);
+          cur.entries.push_back({en.x, static_cast<int32_t>(q0), static_cast<int32_t>(q1), en.w});
+          cur.cost += (q1 - q0) * nk;
+          q0 = q1;
+          if (cur.cost >= cap) {
+            items.push_back(std::move(cur));
+            ++slots;
+            cur = BItem{kt.k0, kt.k1, g, slots, {}, 0};
+          }
+        }
+      }
+      if (!cur.entries.empty()) {
+        items.push_back(std::move(cur));
+        ++slots;
+      }
+      p.bwd_reduce.push_back({{static_cast<int32_t>(kt.k0), static_cast<int32_t>(kt.k1),
+                               static_cast<int32_t>(g), static_cast<int32_t>(slot_begin),
+                               static_cast<int32_t>(slots - slot_begin), 0, 0, 0}});
+      ++p.bwd_split_tiles;
+    }
+  }
+  p.bwd_slots = slots;
+  std::stable_sort(items.begin(), items.end(),
+                   [](const BItem& a, const BItem& b) { return a.cost > b.cost; });
+  for (auto& it : items) {
+    const int32_t eb = static_cast<int32_t>(p.bwd_entries.size());
+    p.bwd_entries.insert(p.bwd_entries.end(), it.entries.begin(), it.entries.end());
+    p.bwd_items.push_back({{static_cast<int32_t>(it.k0), static_cast<int32_t>(it.k1),
+                            static_cast<int32_t>(it.g), eb,
+                            static_cast<int32_t>(p.bwd_entries.size()),
+                            static_cast<int32_t>(it.slot), 0, 0}});
+  }
+  return Status::kOk;
+}
+
+}  // namespace tree_attn

@@ -1,0 +1,76 @@
+// Host planner for prefix-shared tree attention.
+//
+// Turns a node table (parent, segment start, segment length) into the work
+// items of the forward and backward kernels.  The forward pass works per
+// query tile: a tile of rows inside one node, with the list of key ranges it
+// sees (its ancestors' segments, root first, then its own node up to the
+// tile's last row).  The backward pass works per key tile: a tile of rows
+// inside one node, with the list of query ranges that see it (the rest of its
+// own node and every descendant node's segment).  Work is counted in
+// (query row, key row, head) units -- the compact-token work left after
+// prefix compression, on which HARTS (abstract) plans its batches -- and
+// items are ordered longest first.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace tree_attn {
+
+enum class Status : int {
+  kOk = 0,
+  kInvalidArg = 1,
+  kBadTree = 2,
+  kLayout = 3,
+  kUnsupported = 4,
+  kWorkspace = 5,
+  kHip = 6,
+  kNoDevicePlan = 7,
+};
+
+// Tile shapes shared by the planner and the kernels.
+constexpr int kFwdRows = 128;  // query rows per forward workgroup (4 waves x 32)
+constexpr int kFwdKeys = 64;   // keys per forward step
+constexpr int kBwdKeys = 128;  // keys per backward workgroup (4 waves x 32)
+constexpr int kBwdRows = 32;   // query rows per backward step
+constexpr int kXcds = 8;       // MI355X: 8 accelerator complex dies, 8 L2s
+
+struct I4 {
+  int32_t x, y, z, w;
+};
+struct I8 {
+  int32_t v[8];
+};
+
+struct HostPlan {
+  int64_t num_tokens = 0, num_nodes = 0, hq = 0, hkv = 0, head_dim = 0;
+  int dtype = 0;  // 0 bf16, 1 fp32
+  int num_cus = 256;
+  int64_t pairs = 0;
+
+  // forward: tiles (q0, q1, range_begin, range_end) longest first;
+  // ranges (k0, k1, causal, 0)
+  std::vector<I4> fwd_tiles;
+  std::vector<I4> fwd_ranges;
+  int64_t fwd_groups = 0;  // tiles * hkv
+  int64_t fwd_blocks = 0;  // launch size (padded to whole XCD rounds) * group size
+
+  // backward: items (k0, k1, kv_head, entry_begin, entry_end, slot, 0, 0)
+  // longest first; entries (q_head, q0, q1, causal); reductions of split key
+  // tiles (k0, k1, kv_head, slot_begin, num_slots, 0, 0, 0)
+  std::vector<I8> bwd_items;
+  std::vector<I4> bwd_entries;
+  std::vector<I8> bwd_reduce;
+  int64_t bwd_slots = 0;
+  int64_t bwd_split_tiles = 0;
+};
+
+// Validates the table and fills `out`.  On error returns the status and a
+// message in *err; `out` is then unspecified.
+Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                  int32_t num_nodes, int32_t num_tokens, int32_t num_q_heads,
+                  int32_t num_kv_heads, int32_t head_dim, int dtype, int num_cus,
+                  HostPlan* out, std::string* err);
+
+}  // namespace tree_attn

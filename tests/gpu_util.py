@@ -1,0 +1,57 @@
+"""Helpers for GPU tests: move seeded inputs to the device, run the library,
+compare with the oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+
+from tree_inputs import NodeTable, make_inputs
+
+# Parity bar for this path: relative L2 error <= 1e-2 on O, dQ, dK, dV and
+# max |LSE error| <= 1e-3 against the fp64 oracle.
+REL_L2 = 1e-2
+LSE_ABS = 1e-3
+
+
+def rel_l2(x: np.ndarray, ref: np.ndarray) -> float:
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref.ravel())
+    return float(np.linalg.norm((x - ref).ravel()) / max(den, 1e-300))
+
+
+def to_device(x, dtype: str):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def device_inputs(x, dtype: str):
+    if dtype == "bf16":
+        return {k: to_device(x.bits[k], "bf16") for k in ("q", "k", "v", "do")}
+    return {k: to_device(getattr(x, k), "fp32") for k in ("q", "k", "v", "do")}
+
+
+def run_library(t: NodeTable, x, hq: int, hkv: int, d: int, dtype: str, scale: float,
+                backward: bool = True):
+    """Plans, runs fwd (and bwd) through the C ABI; returns host fp64 arrays."""
+    import torch
+    import prefix_shared_tree_attn_amd as ta
+    dev = device_inputs(x, dtype)
+    p = ta.plan(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, d, dtype)
+    o, lse = ta.fwd(p, dev["q"], dev["k"], dev["v"], scale)
+    out = {"o": o, "lse": lse}
+    if backward:
+        dq, dk, dv = ta.bwd(p, dev["q"], dev["k"], dev["v"], o, lse, dev["do"], scale)
+        out.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    res = {k: v.float().cpu().numpy().astype(np.float64) for k, v in out.items()}
+    p.close()
+    return res
+
+
+def make(t: NodeTable, hq: int, hkv: int, d: int, dtype: str, do_std: float = 1e-2,
+         seed_offset: int = 0):
+    return make_inputs(t.num_tokens, hq, hkv, d, dtype=dtype, do_std=do_std,
+                       seed_offset=seed_offset)

@@ -1,0 +1,193 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Bar: relative L2 error <= 1e-2 on O, dQ, dK, dV and max |LSE error| <= 1e-3.
+Small trees are compared element by element over whole tensors; they span
+several tiles and ragged tails (segments that are not multiples of the 128
+-row query tiles, 64-key forward steps or 128-key backward tiles).  The five
+workload trees are run at full size in the launch configuration of the
+benchmark and compared on sampled rows and keys that the oracle computes one
+by one, plus closed-form properties over the whole tensors.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tree_inputs import (NodeTable, binary_tree, chain_tree, config_spec, config_tree,
+                         random_tree, star_tree, trunk_tree)
+from gpu_util import LSE_ABS, REL_L2, make, rel_l2, run_library
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare_full(t: NodeTable, hq, hkv, d, dtype, scale=None, do_std=1e-2, seed_offset=0):
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    x = make(t, hq, hkv, d, dtype, do_std=do_std, seed_offset=seed_offset)
+    print(f"case: N={t.num_tokens} nodes={t.num_nodes} hq={hq} hkv={hkv} d={d} {dtype}",
+          flush=True)
+    got = run_library(t, x, hq, hkv, d, dtype, scale)
+    ref = oracle.tree_attention(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len, scale)
+    errs = {k: rel_l2(got[k], ref[k]) for k in ("o", "dq", "dk", "dv")}
+    errs["lse"] = float(np.abs(got["lse"] - ref["lse"]).max())
+    print("errors:", errs, flush=True)
+    for k in ("o", "dq", "dk", "dv"):
+        assert errs[k] <= REL_L2, (k, errs)
+    assert errs["lse"] <= LSE_ABS, errs
+    return errs
+
+
+def _random(seed, nodes, max_len, roots=1):
+    return random_tree(np.random.default_rng(seed), nodes, max_len=max_len, n_roots=roots)
+
+
+CASES = {
+    "single-token": (chain_tree([1]), 1, 1, 128, "bf16"),
+    "chain-1000": (chain_tree([1000]), 2, 1, 128, "bf16"),
+    "chain-ragged": (chain_tree([70, 1, 129, 64, 200]), 4, 2, 128, "bf16"),
+    "star": (star_tree(300, 5, 257), 4, 2, 128, "bf16"),
+    "binary-ragged": (binary_tree(129, 97, 3), 4, 2, 128, "bf16"),
+    "random-a": (_random(1, 9, 300), 4, 2, 128, "bf16"),
+    "random-b": (_random(2, 12, 200), 8, 1, 128, "bf16"),
+    "forest": (_random(3, 10, 260, roots=3), 6, 2, 128, "bf16"),
+    "gqa7": (_random(4, 7, 300), 7, 1, 128, "bf16"),
+    "mha": (_random(5, 6, 250), 3, 3, 128, "bf16"),
+    "d64-bf16": (_random(6, 9, 300), 4, 2, 64, "bf16"),
+    "d64-fp32": (_random(7, 8, 200), 2, 1, 64, "fp32"),
+    "d128-fp32": (_random(8, 6, 200), 2, 2, 128, "fp32"),
+    "heavy-prompt-split": (star_tree(1024, 16, 64), 4, 2, 128, "bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_small_tree_elementwise(name):
+    t, hq, hkv, d, dtype = CASES[name]
+    _compare_full(t, hq, hkv, d, dtype, do_std=1.0 if dtype == "fp32" else 1e-2)
+
+
+def test_split_case_really_splits():
+    import prefix_shared_tree_attn_amd as ta
+    t, hq, hkv, d, dtype = CASES["heavy-prompt-split"]
+    p = ta.plan(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, d, dtype)
+    assert p.stats()["bwd_split_tiles"] > 0
+
+
+def test_config1_full():
+    t = config_tree(1)
+    sp = config_spec(1)
+    errs = _compare_full(t, sp["heads_q"], sp["heads_kv"], sp["head_dim"], sp["dtype"],
+                         scale=sp["scale"], do_std=sp["do_std"])
+    # fp32 inputs go through split-bf16 products: well inside the bar
+    assert errs["lse"] < 1e-4 and errs["o"] < 1e-4
+
+
+def test_scaled_down_workloads():
+    """Smaller trees of the same shapes as the benchmark workloads."""
+    _compare_full(star_tree(512, 8, 640), 8, 2, 128, "bf16")
+    _compare_full(binary_tree(96, 96, 5), 7, 1, 128, "bf16")
+    _compare_full(trunk_tree(seed=1, trunk=3000, n_branches=8, branch_len=200), 8, 1, 128,
+                  "bf16")
+
+
+def test_empty_tree_is_a_no_op():
+    import torch
+    import prefix_shared_tree_attn_amd as ta
+    p = ta.plan([], [], [], 0, 2, 1, 128)
+    z = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    zk = torch.empty((0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    o, lse = ta.fwd(p, z, zk, zk, 0.1)
+    dq, dk, dv = ta.bwd(p, z, zk, zk, o, lse, z, 0.1)
+    torch.cuda.synchronize()
+    assert o.shape == (0, 2, 128) and dk.shape == (0, 1, 128)
+
+
+def test_repeat_runs_are_deterministic_where_promised():
+    import torch
+    import prefix_shared_tree_attn_amd as ta
+    from gpu_util import device_inputs
+    t = star_tree(1024, 16, 64)
+    x = make(t, 4, 2, 128, "bf16")
+    dev = device_inputs(x, "bf16")
+    p = ta.plan(t.parent, t.seg_start, t.seg_len, t.num_tokens, 4, 2, 128)
+    runs = []
+    for _ in range(2):
+        o, lse = ta.fwd(p, dev["q"], dev["k"], dev["v"], 0.088)
+        dq, dk, dv = ta.bwd(p, dev["q"], dev["k"], dev["v"], o, lse, dev["do"], 0.088)
+        torch.cuda.synchronize()
+        runs.append([a.clone() for a in (o, lse, dq, dk, dv)])
+    for i in (0, 1, 3, 4):  # o, lse, dk, dv bitwise
+        assert torch.equal(runs[0][i], runs[1][i]), i
+    assert rel_l2(runs[0][2].float().cpu().numpy(), runs[1][2].float().cpu().numpy()) < 1e-2
+
+
+# ------------------------------------------------------------------ full size
+
+def _sample_keys(t: NodeTable, rng, cfg: int):
+    """Key rows whose descendant work the oracle can afford: tokens of leaf
+    nodes, of the smallest inner subtree, and (except for the long trunk) the
+    first token of the root."""
+    m = t.num_nodes
+    has_child = np.zeros(m, bool)
+    for i in range(m):
+        if t.parent[i] >= 0:
+            has_child[t.parent[i]] = True
+    leaves = np.nonzero(~has_child)[0]
+    keys = []
+    for leaf in rng.choice(leaves, size=min(3, len(leaves)), replace=False):
+        s, l = int(t.seg_start[leaf]), int(t.seg_len[leaf])
+        keys += [s, s + l // 2, s + l - 1]
+    inner = np.nonzero(has_child)[0]
+    if len(inner):
+        # the inner node with the fewest descendant tokens
+        sizes = []
+        for i in inner:
+            stack, tot = [int(i)], 0
+            while stack:
+                n = stack.pop()
+                tot += int(t.seg_len[n])
+                stack += [c for c in range(m) if t.parent[c] == n]
+            sizes.append(tot)
+        i = int(inner[int(np.argmin(sizes))])
+        keys += [int(t.seg_start[i] + t.seg_len[i] - 1)]
+    if cfg != 5:
+        keys.append(int(t.seg_start[np.nonzero(t.parent < 0)[0][0]]))
+    return sorted(set(keys))
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled(cfg):
+    t = config_tree(cfg)
+    sp = config_spec(cfg)
+    hq, hkv, d, dtype, scale = sp["heads_q"], sp["heads_kv"], sp["head_dim"], sp["dtype"], sp["scale"]
+    print(f"config {cfg}: N={t.num_tokens} nodes={t.num_nodes}", flush=True)
+    x = make(t, hq, hkv, d, dtype, do_std=sp["do_std"])
+    got = run_library(t, x, hq, hkv, d, dtype, scale)
+    rng = np.random.default_rng(100 + cfg)
+    rows = sorted(set([0, t.num_tokens - 1] + list(rng.integers(0, t.num_tokens, 14))))
+    heads = sorted(set(int(h) for h in rng.integers(0, hq, 3)))
+    o, lse, dq = oracle.query_rows(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len,
+                                   scale, rows, heads)
+    e_o = rel_l2(got["o"][rows][:, heads], o)
+    e_dq = rel_l2(got["dq"][rows][:, heads], dq)
+    e_lse = float(np.abs(got["lse"][heads][:, rows] - lse).max())
+    g = int(heads[0]) // (hq // hkv)
+    keys = _sample_keys(t, rng, cfg)
+    dk, dv = oracle.key_rows(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len, scale,
+                             keys, g)
+    e_dk = rel_l2(got["dk"][keys, g], dk)
+    e_dv = rel_l2(got["dv"][keys, g], dv)
+    print(f"sampled errors: o={e_o:.2e} lse={e_lse:.2e} dq={e_dq:.2e} dk={e_dk:.2e} "
+          f"dv={e_dv:.2e}", flush=True)
+    assert max(e_o, e_dq, e_dk, e_dv) <= REL_L2
+    assert e_lse <= LSE_ABS
+    # closed forms over whole tensors (every softmax row sums to one and is
+    # shift invariant; scores depend on q.k only)
+    gs = hq // hkv
+    do64 = x.do.astype(np.float64)
+    for gg in range(hkv):
+        want = do64[:, gg * gs:(gg + 1) * gs].sum((0, 1))
+        assert rel_l2(got["dv"][:, gg].sum(0), want) <= REL_L2
+        assert np.linalg.norm(got["dk"][:, gg].sum(0)) <= 1e-2 * np.linalg.norm(got["dk"][:, gg])
+    lhs = float(np.sum(got["dq"] * x.q))
+    rhs = float(np.sum(got["dk"] * x.k))
+    assert abs(lhs - rhs) <= 1e-2 * max(abs(lhs), abs(rhs), 1e-30)
+    assert np.isfinite(got["o"]).all() and np.isfinite(got["dq"]).all()

@@ -1,0 +1,228 @@
+"""Host-side tests of libtree_attn.so: exports, validation and the planner.
+
+These run without a GPU: tree_attn_plan_host validates and plans on the CPU
+and the plan's work arrays are exported and checked here against the
+ancestor relation computed independently in Python.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import prefix_shared_tree_attn_amd as ta
+from prefix_shared_tree_attn_amd import _ffi
+from tree_inputs import NodeTable, binary_tree, chain_tree, config_tree, random_tree, star_tree, tree_stats
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tree_attn.h")
+
+
+def test_library_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(tree_attn_[a-z_]+)\s*\(", text))
+    assert declared == set(_ffi.EXPORTS)
+    lib = _ffi.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _visible(t: NodeTable):
+    """Set of (q, key) pairs: key is in an ancestor node of q's node, or in
+    q's node at or before q (built from parent pointers directly)."""
+    m = t.num_nodes
+    node_of = np.empty(t.num_tokens, np.int64)
+    for i in range(m):
+        node_of[t.seg_start[i]:t.seg_start[i] + t.seg_len[i]] = i
+    anc = [set() for _ in range(m)]
+    for i in range(m):
+        a = int(t.parent[i])
+        while a >= 0:
+            anc[i].add(a)
+            a = int(t.parent[a])
+    vis = set()
+    for q in range(t.num_tokens):
+        n = int(node_of[q])
+        for a in anc[n]:
+            for key in range(int(t.seg_start[a]), int(t.seg_start[a] + t.seg_len[a])):
+                vis.add((q, key))
+        for key in range(int(t.seg_start[n]), q + 1):
+            vis.add((q, key))
+    return vis
+
+
+def _fwd_pairs(ex, hq, hkv):
+    pairs = {}
+    for q0, q1, rb, re_ in ex["fwd_tiles"]:
+        for k0, k1, causal, _ in ex["fwd_ranges"][rb:re_]:
+            for q in range(q0, q1):
+                for key in range(k0, k1):
+                    if causal and key > q:
+                        continue
+                    pairs[(q, key)] = pairs.get((q, key), 0) + 1
+    return pairs
+
+
+def _bwd_triples(ex):
+    trip = {}
+    for it in ex["bwd_items"]:
+        k0, k1, g, eb, ee = it[:5]
+        for h, q0, q1, causal in ex["bwd_entries"][eb:ee]:
+            for q in range(q0, q1):
+                for key in range(k0, k1):
+                    if causal and key > q:
+                        continue
+                    trip[(q, key, h)] = trip.get((q, key, h), 0) + 1
+    return trip
+
+
+def _trees():
+    rng = np.random.default_rng(0)
+    out = [chain_tree([5]), chain_tree([130, 1, 200]), star_tree(100, 3, 150),
+           binary_tree(40, 70, 3), config_tree(1)]
+    for seed in range(6):
+        r = np.random.default_rng(seed)
+        out.append(random_tree(r, int(r.integers(1, 14)), max_len=300,
+                               n_roots=int(r.integers(1, 3))))
+    return out
+
+
+@pytest.mark.parametrize("idx", range(11))
+def test_plan_covers_every_visible_pair_once(idx):
+    t = _trees()[idx]
+    hq, hkv = 4, 2
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, 64, "bf16",
+                     num_cus=4)
+    ex = p.export()
+    vis = _visible(t)
+    fp = _fwd_pairs(ex, hq, hkv)
+    assert set(fp) == vis and set(fp.values()) == {1}
+    bt = _bwd_triples(ex)
+    want = {(q, key, h) for (q, key) in vis for h in range(hq)}
+    assert set(bt) == want and set(bt.values()) == {1}
+    # every backward item's heads belong to its kv head
+    for it in ex["bwd_items"]:
+        hs = ex["bwd_entries"][it[3]:it[4], 0]
+        assert np.all(hs // (hq // hkv) == it[2])
+    st = p.stats()
+    assert st["pairs"] == tree_stats(t)["pairs"] == len(vis)
+
+
+def test_forward_block_mapping_covers_tiles_and_heads_once():
+    """The forward launch maps workgroup b to (tile, head) as: slot = b / 8,
+    group = (slot / G) * 8 + b % 8, tile = group / Hkv, head = (group % Hkv) * G
+    + slot % G; every (tile, head) must come up exactly once."""
+    t = binary_tree(100, 90, 3)
+    for hq, hkv in ((28, 4), (8, 8), (3, 1)):
+        p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, 128)
+        st = p.stats()
+        gs = hq // hkv
+        ngroups = st["fwd_tiles"] * hkv
+        seen = {}
+        for b in range(st["fwd_blocks"]):
+            slot = b // 8
+            gi = (slot // gs) * 8 + b % 8
+            if gi >= ngroups:
+                continue
+            key = (gi // hkv, (gi % hkv) * gs + slot % gs)
+            seen[key] = seen.get(key, 0) + 1
+        assert set(seen) == {(ti, h) for ti in range(st["fwd_tiles"]) for h in range(hq)}
+        assert set(seen.values()) == {1}
+
+
+def test_items_longest_first_and_split_heavy_tiles():
+    t = config_tree(2)  # star: the prompt's key tiles are seen by every response
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, 32, 8, 128)
+    ex = p.export()
+    st = p.stats()
+    assert st["bwd_split_tiles"] > 0 and st["bwd_slots"] > 0
+    costs = []
+    for it in ex["bwd_items"]:
+        rows = (ex["bwd_entries"][it[3]:it[4], 2] - ex["bwd_entries"][it[3]:it[4], 1]).sum()
+        costs.append(int(rows) * int(it[1] - it[0]))
+    assert all(a >= b for a, b in zip(costs, costs[1:]))
+    fcost = []
+    for q0, q1, rb, re_ in ex["fwd_tiles"]:
+        keys = sum(int(k1 - k0) for k0, k1, _, _ in ex["fwd_ranges"][rb:re_])
+        fcost.append((q1 - q0) * keys)
+    assert all(a >= b for a, b in zip(fcost, fcost[1:]))
+    # split chunks of one key tile carry distinct slots; unsplit items use -1
+    slots = ex["bwd_items"][:, 5]
+    assert len(set(slots[slots >= 0])) == st["bwd_slots"]
+
+
+def test_workspace_size():
+    t = config_tree(2)
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, 32, 8, 128)
+    f, b = p.workspace_size()
+    st = p.stats()
+    n = t.num_tokens
+    al = lambda x: (x + 255) // 256 * 256
+    slot = st["bwd_slots"] * 128 * 128 * 4
+    assert f == 0
+    assert b == al(n * 32 * 128 * 4) + al(n * 32 * 4) + 2 * al(slot)
+
+
+def test_empty_tree():
+    p = ta.plan_host([], [], [], 0, 2, 1, 64)
+    st = p.stats()
+    assert st["num_tokens"] == 0 and st["fwd_tiles"] == 0 and st["bwd_items"] == 0
+    assert p.workspace_size() == (0, 0)
+
+
+@pytest.mark.parametrize("parent,start,length,n,hq,hkv,d,dtype,status", [
+    ([-1, 5], [0, 4], [4, 4], 8, 1, 1, 64, "bf16", "BAD_TREE"),      # parent out of range
+    ([-1, 1], [0, 4], [4, 4], 8, 1, 1, 64, "bf16", "BAD_TREE"),      # self loop
+    ([2, 0, 1], [0, 4, 8], [4, 4, 4], 12, 1, 1, 64, "bf16", "BAD_TREE"),  # cycle
+    ([-1, 0], [0, 3], [4, 4], 8, 1, 1, 64, "bf16", "LAYOUT"),        # overlap
+    ([-1, 0], [0, 5], [4, 4], 9, 1, 1, 64, "bf16", "LAYOUT"),        # gap
+    ([-1, 0], [0, 4], [4, 0], 8, 1, 1, 64, "bf16", "LAYOUT"),        # empty segment
+    ([-1, 0], [0, 4], [4, 4], 9, 1, 1, 64, "bf16", "LAYOUT"),        # uncovered tail
+    ([-1, 0], [0, 4], [4, 5], 8, 1, 1, 64, "bf16", "LAYOUT"),        # past the end
+    ([-1], [0], [4], 4, 3, 2, 64, "bf16", "UNSUPPORTED"),            # Hq % Hkv
+    ([-1], [0], [4], 4, 2, 1, 96, "bf16", "UNSUPPORTED"),            # head_dim
+    ([-1], [0], [4], 4, 0, 1, 64, "bf16", "UNSUPPORTED"),            # no heads
+    ([], [], [], 4, 1, 1, 64, "bf16", "LAYOUT"),                     # tokens, no nodes
+])
+def test_validation_errors(parent, start, length, n, hq, hkv, d, dtype, status):
+    with pytest.raises(ta.TreeAttnError) as ei:
+        ta.plan_host(parent, start, length, n, hq, hkv, d, dtype)
+    assert ei.value.status == status
+    assert len(str(ei.value)) > len(status) + 10  # carries a detail message
+
+
+def test_raw_abi_rejects_null_and_negative():
+    lib = _ffi.lib()
+    h = ctypes.c_void_p(0)
+    st = lib.tree_attn_plan_host(None, None, None, 2, 8, 1, 1, 64, 0, 0, ctypes.byref(h))
+    assert _ffi.STATUS[st] == "INVALID_ARG"
+    one = (ctypes.c_int32 * 1)(0)
+    st = lib.tree_attn_plan_host(one, one, one, -1, 8, 1, 1, 64, 0, 0, ctypes.byref(h))
+    assert _ffi.STATUS[st] == "INVALID_ARG"
+    st = lib.tree_attn_plan_host(one, one, one, 1, 8, 1, 1, 64, 7, 0, ctypes.byref(h))
+    assert _ffi.STATUS[st] == "UNSUPPORTED"
+    assert lib.tree_attn_workspace_size(None, None, None) == 1
+    assert lib.tree_attn_status_string(3) == b"invalid segment layout"
+    lib.tree_attn_plan_destroy(None)  # ignored
+
+
+def test_host_plan_rejected_by_fwd():
+    t = chain_tree([8])
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, 8, 1, 1, 64)
+    lib = _ffi.lib()
+    st = lib.tree_attn_fwd(p.handle, None, None, None, ctypes.c_float(1.0), None, None, None, 0,
+                           None)
+    assert _ffi.STATUS[st] == "NO_DEVICE_PLAN"
+
+
+def test_config_plans_build_quickly():
+    for i in (1, 2, 3, 4, 5):
+        t = config_tree(i)
+        from tree_inputs import config_spec
+        sp = config_spec(i)
+        p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, sp["heads_q"],
+                         sp["heads_kv"], sp["head_dim"], sp["dtype"])
+        st = p.stats()
+        assert st["pairs"] == tree_stats(t)["pairs"]
+        assert st["fwd_tiles"] > 0 and st["bwd_items"] > 0
