@@ -1,0 +1,258 @@
+"""Benchmark: prefix-shared tree attention forward + backward on one MI355X.
+
+One step is one pass of the whole path over one batch: build the plan for
+the tree (host planning + upload of its work arrays), the forward pass and
+the backward pass (preprocess, main, reductions).  Throughput is unique
+tokens per second and TFLOP/s counted on the deduplicated tree work,
+14 * D * Hq * sum_t (d(t) + 1) per step (forward 4, backward 10, in the
+usual attention convention with the backward's recomputation).
+
+Prints one JSON line.  Default workload: the GRPO-style star tree (one
+1024-token prompt, 16 responses of 2048 tokens; 32 query / 8 kv heads,
+head dim 128, bf16).  ``--config`` selects another of the five workload
+trees.  Only one GPU is used; ``--gpus`` above 1 is refused.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP32_TFLOPS = 157.3    # dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0
+METRIC = "tree-attn fwd+bwd unique tokens/s and TFLOP/s (% of bf16 MFMA peak), 1 GPU"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the oracle on the host")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def _traffic_from_profile(workload: str):
+    """HBM bytes per launch of the backward main kernel from the committed
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"bwd_main_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "prefix_shared_tree_attn_amd", "csrc", "bwd.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("bwd_hip_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(t, spec, budget_heads: int | None = None):
+    """Times the fp64 oracle on the host over one kv-head group of the same
+    workload and scales it to unique tokens/s of the whole workload."""
+    import oracle
+    from tree_inputs import make_inputs
+    from threadpoolctl import threadpool_info
+    hq, hkv, d = spec["heads_q"], spec["heads_kv"], spec["head_dim"]
+    x = make_inputs(t.num_tokens, hq, hkv, d, dtype=spec["dtype"], do_std=spec["do_std"])
+    t0 = time.perf_counter()
+    oracle.tree_attention(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len,
+                          spec["scale"], kv_heads=[0])
+    dt = time.perf_counter() - t0
+    threads = sum(int(p.get("num_threads", 0)) for p in threadpool_info()
+                  if p.get("user_api") == "blas") or 1
+    return {
+        "value": t.num_tokens / (dt * hkv),
+        "unit": "unique tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"kv-head group 0 of {hkv} ({hq // hkv} query heads), full tree, "
+                   f"fwd+bwd in fp64: {dt:.2f} s, scaled by {hkv} groups"),
+    }
+
+
+def main() -> int:
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; multi-GPU sharding is design-only)", file=sys.stderr)
+        return 2
+    import torch
+    import prefix_shared_tree_attn_amd as ta
+    from tree_inputs import config_spec, config_tree, make_inputs, tree_stats
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = args.config
+    t = config_tree(cfg)
+    spec = config_spec(cfg)
+    st = tree_stats(t)
+    hq, hkv, d, dtype = spec["heads_q"], spec["heads_kv"], spec["head_dim"], spec["dtype"]
+    scale = spec["scale"]
+    n = t.num_tokens
+    log(f"workload {spec['name']}: N={n} nodes={t.num_nodes} pairs={st['pairs']} "
+        f"hq={hq} hkv={hkv} d={d} {dtype}")
+
+    x = make_inputs(n, hq, hkv, d, dtype=dtype, do_std=spec["do_std"])
+    log("inputs generated")
+
+    def up(name):
+        if dtype == "bf16":
+            a = torch.from_numpy(x.bits[name].view(np.int16)).view(torch.bfloat16)
+        else:
+            a = torch.from_numpy(getattr(x, name))
+        return a.to(dev)
+
+    q, k, v, do = up("q"), up("k"), up("v"), up("do")
+    tdt = q.dtype
+    o = torch.empty((n, hq, d), dtype=tdt, device=dev)
+    lse = torch.empty((hq, n), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    probe = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype)
+    ws = ta.workspace(probe, "bwd")
+    pstats = probe.stats()
+    probe.close()
+    del x
+    log("device buffers ready")
+
+    plans = []
+
+    def step():
+        p = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype)
+        ta.fwd(p, q, k, v, scale, o=o, lse=lse)
+        ta.bwd(p, q, k, v, o, lse, do, scale, dq=dq, dk=dk, dv=dv, ws=ws)
+        plans.append(p)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for p in plans:
+        p.close()
+    plans.clear()
+    log(f"warmup done ({args.warmup} steps)")
+
+    ta.timing_read(reset=True)
+    ta.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ta.timing_enable(False)
+    kt = ta.timing_read(reset=True)
+    for p in plans:
+        p.close()
+    plans.clear()
+    log(f"timed {args.steps} steps: {wall:.3f} s")
+
+    if args.copy_probe_mib > 0:
+        nb = args.copy_probe_mib << 20
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy probe: {nb} bytes read + {nb} bytes written")
+
+    ms_step = 1e3 * wall / args.steps
+    pairs = st["pairs"]
+    fwd_flop = 4.0 * d * hq * pairs
+    bwd_flop = 10.0 * d * hq * pairs
+    step_flop = fwd_flop + bwd_flop
+    tflops = step_flop / (ms_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    def avg_ms(kind):
+        r = kt[kind]
+        return r["total_ms"] / max(r["launches"], 1)
+
+    bwd_main_ms = avg_ms("bwd_main")
+    fwd_ms = avg_ms("fwd")
+    bwd_achieved = bwd_flop / (bwd_main_ms * 1e-3) / 1e12
+    fwd_achieved = fwd_flop / (fwd_ms * 1e-3) / 1e12
+    esize = 2 if dtype == "bf16" else 4
+    # backward preprocess: reads O and dO, writes D_t and zeroes the fp32 dQ accumulator
+    pre_bytes = n * hq * d * (2 * esize + 4) + n * hq * 4
+    post_bytes = n * hq * d * (4 + esize) + 2 * pstats["bwd_slots"] * 128 * d * 4
+    workload = spec["name"]
+    result = {
+        "metric": METRIC,
+        "value": n / (ms_step * 1e-3),
+        "unit": "unique tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{workload}: " + {
+                1: "binary tree, root 32 + 3 levels of 16-token segments",
+                2: "GRPO star, 1024-token prompt + 16 x 2048-token responses",
+                3: "irregular 8-level agent tree, ~32K tokens",
+                4: "segment search tree, 512-token segments, 6 binary levels",
+                5: "32768-token trunk + 64 x 2048-token branches"}[cfg],
+            "unique_tokens": n, "nodes": t.num_nodes, "pairs": pairs,
+            "heads_q": hq, "heads_kv": hkv, "head_dim": d, "softmax_scale": scale,
+            "global_batch": 1, "seq_len": st["max_path"], "parallelism": "none (1 GPU)",
+        },
+        "tflops": tflops,
+        "frac_of_peak": tflops / peak,
+        "dense_per_path_flop_ratio": st["dense_ratio"],
+        "kernels_ms": {kk: avg_ms(kk) for kk in kt},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "tree_attn_bwd_kernel (backward main)",
+            "achieved": bwd_achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": bwd_achieved / peak,
+            "traffic": _traffic_from_profile(workload),
+            "flop_per_launch": bwd_flop,
+        },
+        "roofline_fwd": {
+            "bound": "mfma", "kernel": "tree_attn_fwd_kernel", "achieved": fwd_achieved,
+            "peak": peak, "unit": "TFLOP/s", "frac": fwd_achieved / peak,
+            "flop_per_launch": fwd_flop,
+        },
+        "hbm_passes_GBps": {
+            "bwd_pre": pre_bytes / (avg_ms("bwd_pre") * 1e-3) / 1e9,
+            "bwd_post": post_bytes / (avg_ms("bwd_post") * 1e-3) / 1e9,
+            "peak": PEAK_HBM_GBS,
+        },
+        "plan": {k: pstats[k] for k in ("fwd_tiles", "bwd_items", "bwd_split_tiles", "bwd_slots")},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (cpu baseline)")
+        result["cpu_baseline"] = cpu_baseline(t, spec)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

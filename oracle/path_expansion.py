@@ -311,6 +311,9 @@ def key_rows(q, k, v, do, parent, seg_start, seg_len, scale: float,
                 pr = e / e.sum(axis=1, keepdims=True)
                 dp = dop[r0:r1] @ vp[:r1].T
                 ds = pr * (dp - (pr * dp).sum(axis=1, keepdims=True))
-                dk[kidx] += scale * (ds[:, kpos].T @ qp[r0:r1])
-                dv[kidx] += pr[:, kpos].T @ dop[r0:r1]
+                # keys at path positions >= r1 are not seen by these rows
+                live = kpos < r1
+                kl, pl = kidx[live], kpos[live]
+                dk[kl] += scale * (ds[:, pl].T @ qp[r0:r1])
+                dv[kl] += pr[:, pl].T @ dop[r0:r1]
     return dk, dv

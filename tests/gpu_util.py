@@ -33,9 +33,10 @@ def device_inputs(x, dtype: str):
     return {k: to_device(getattr(x, k), "fp32") for k in ("q", "k", "v", "do")}
 
 
-def run_library(t: NodeTable, x, hq: int, hkv: int, d: int, dtype: str, scale: float,
-                backward: bool = True):
-    """Plans, runs fwd (and bwd) through the C ABI; returns host fp64 arrays."""
+def run_library_device(t: NodeTable, x, hq: int, hkv: int, d: int, dtype: str,
+                       scale: float, backward: bool = True):
+    """Plans, runs fwd (and bwd) through the C ABI; returns device tensors
+    (outputs and the device copies of the inputs)."""
     import torch
     import prefix_shared_tree_attn_amd as ta
     dev = device_inputs(x, dtype)
@@ -46,9 +47,15 @@ def run_library(t: NodeTable, x, hq: int, hkv: int, d: int, dtype: str, scale: f
         dq, dk, dv = ta.bwd(p, dev["q"], dev["k"], dev["v"], o, lse, dev["do"], scale)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
-    res = {k: v.float().cpu().numpy().astype(np.float64) for k, v in out.items()}
     p.close()
-    return res
+    return out, dev
+
+
+def run_library(t: NodeTable, x, hq: int, hkv: int, d: int, dtype: str, scale: float,
+                backward: bool = True):
+    """As run_library_device, returning host fp64 arrays of the outputs."""
+    out, _ = run_library_device(t, x, hq, hkv, d, dtype, scale, backward)
+    return {k: v.float().cpu().numpy().astype(np.float64) for k, v in out.items()}
 
 
 def make(t: NodeTable, hq: int, hkv: int, d: int, dtype: str, do_std: float = 1e-2,

@@ -381,11 +381,17 @@ def test_sampled_rows_match_full():
     np.testing.assert_allclose(o, r["o"][rows][:, [0, 3]], atol=1e-12)
     np.testing.assert_allclose(lse, r["lse"][[0, 3]][:, rows], atol=1e-12)
     np.testing.assert_allclose(dq, r["dq"][rows][:, [0, 3]], atol=1e-12)
-    keys = [0, 5, t.num_tokens - 2]
+    # every token as a key, with row blocks much shorter than the paths
+    keys = list(range(t.num_tokens))
     dk, dv = oracle.key_rows(q, k, v, do, t.parent, t.seg_start, t.seg_len, 0.3, keys, 1,
                              row_block=7)
     np.testing.assert_allclose(dk, r["dk"][keys, 1], atol=1e-12)
     np.testing.assert_allclose(dv, r["dv"][keys, 1], atol=1e-12)
+    for kk in ([0], [t.num_tokens - 1], [3, t.num_tokens // 2]):
+        dk, dv = oracle.key_rows(q, k, v, do, t.parent, t.seg_start, t.seg_len, 0.3, kk, 0,
+                                 row_block=5)
+        np.testing.assert_allclose(dk, r["dk"][kk, 0], atol=1e-12)
+        np.testing.assert_allclose(dv, r["dv"][kk, 0], atol=1e-12)
 
 
 def test_head_subset_and_row_blocking():
