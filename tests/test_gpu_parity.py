@@ -199,9 +199,20 @@ def test_full_size_sampled(cfg):
         assert float((have - want).norm() / want.norm()) <= REL_L2
         dkg = got["dk"][:, gg].double()
         assert float(dkg.sum(0).norm()) <= 1e-2 * float(dkg.norm())
-    lhs = float(sum((got["dq"][:, h].double() * dev["q"][:, h].double()).sum() for h in range(hq)))
-    rhs = float(sum((got["dk"][:, g_].double() * dev["k"][:, g_].double()).sum()
-                    for g_ in range(hkv)))
-    assert abs(lhs - rhs) <= 1e-2 * max(abs(lhs), abs(rhs), 1e-30)
+    # <dQ, Q> = <dK, K> cancels heavily; each bf16 output element carries a
+    # rounding error of up to 2^-9 relative, so the two sums may differ by a
+    # few standard deviations u / sqrt(3) * ||x * y||_2 of that noise
+    lhs = rhs = n_l = n_r = 0.0
+    for h in range(hq):
+        pr = got["dq"][:, h].double() * dev["q"][:, h].double()
+        lhs += float(pr.sum())
+        n_l += float((pr * pr).sum())
+    for g_ in range(hkv):
+        pr = got["dk"][:, g_].double() * dev["k"][:, g_].double()
+        rhs += float(pr.sum())
+        n_r += float((pr * pr).sum())
+    noise = (2.0 ** -9 / np.sqrt(3.0)) * np.sqrt(n_l + n_r)
+    print(f"<dQ,Q>={lhs:.6e} <dK,K>={rhs:.6e} rounding-noise std={noise:.3e}", flush=True)
+    assert abs(lhs - rhs) <= 6.0 * noise + 1e-2 * max(abs(lhs), abs(rhs))
     for name in ("o", "dq", "dk", "dv", "lse"):
         assert bool(torch.isfinite(got[name]).all()), name
