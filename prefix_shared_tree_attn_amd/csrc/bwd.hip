@@ -29,40 +29,54 @@ namespace tree_attn {
 
 namespace {
 
-// dS tile: [kBwdKeys keys][kBwdRows queries] bf16, rows of 64 bytes, no
-// swizzle (transpose reads of 4 rows x 32 bytes are conflict free).
-constexpr int kDsRowBytes = kBwdRows * 2;
-
-__device__ __forceinline__ bf16x8 ds_tr_operand(const LDS_PTR(char) base, int row0, int lane) {
-  const int grp = lane >> 4, L = lane & 15;
-  const int r = row0 + 8 * (grp >> 1) + (L >> 2);
-  const int c = 16 * (grp & 1) + 4 * (L & 3);
-  const bf16x4 lo = lds_read_tr(base, r * kDsRowBytes + 2 * c);
-  const bf16x4 hi = lds_read_tr(base, (r + 4) * kDsRowBytes + 2 * c);
-  bf16x8 out;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    out[s] = lo[s];
-    out[s + 4] = hi[s];
-  }
-  return out;
-}
-
+// Shared-memory layout of the main kernel.  QB query rows per step (two
+// 32-row sub-blocks for bf16; one for fp32 inputs, whose hi/lo planes double
+// every tile).  Q / dO / (LSE, D) have NBUF buffers: with two, the next
+// step's rows stream in while the current step computes.  dS always has two
+// buffers: step i writes dS(i) and step i + 1 forms dQ(i) from it.
 template <typename T, int D>
-struct BwdSmem {
+struct BwdCfg {
   static constexpr bool SPLIT = IsSplit<T>::value;
   static constexpr int NP = SPLIT ? 2 : 1;
+  static constexpr int QB = SPLIT ? 32 : 64;
+  static constexpr int NSUB = QB / 32;
+  static constexpr int NBUF = (SPLIT && D == 128) ? 1 : 2;
+  static constexpr int KC = D / 16;
+  static constexpr int DB = D / 32;
   static constexpr int K_PLANE = kBwdKeys * D * 2;
-  static constexpr int Q_PLANE = kBwdRows * D * 2;
-  static constexpr int DS_PLANE = kBwdKeys * kDsRowBytes;
+  static constexpr int Q_PLANE = QB * D * 2;
+  static constexpr int DS_PLANE = kBwdKeys * QB * 2;
+  static constexpr int LD_BYTES = QB * 8;  // LSE * log2(e), then D
   static constexpr int K_OFF = 0;
   static constexpr int Q_OFF = K_OFF + NP * K_PLANE;
-  static constexpr int DO_OFF = Q_OFF + NP * Q_PLANE;
-  static constexpr int DS_OFF = DO_OFF + NP * Q_PLANE;
-  static constexpr int LSE_OFF = DS_OFF + NP * DS_PLANE;
-  static constexpr int DV_OFF = LSE_OFF + kBwdRows * 4;
-  static constexpr int BYTES = DV_OFF + kBwdRows * 4;
+  static constexpr int DO_OFF = Q_OFF + NBUF * NP * Q_PLANE;
+  static constexpr int DS_OFF = DO_OFF + NBUF * NP * Q_PLANE;
+  static constexpr int LD_OFF = DS_OFF + 2 * NP * DS_PLANE;
+  static constexpr int BYTES = LD_OFF + NBUF * LD_BYTES;
 };
+
+// One step of work: rows [qb, min(qb + QB, qe)) of query head h.
+struct Blk {
+  int h, qb, qe, causal, e;
+};
+
+__device__ __forceinline__ bool load_entry(Blk& b, int e, int ee, const I4* entries) {
+  if (e >= ee) return false;
+  const I4 en = entries[e];
+  b.h = en.x;
+  b.qb = en.y;
+  b.qe = en.z;
+  b.causal = en.w;
+  b.e = e;
+  return true;
+}
+
+template <int QB>
+__device__ __forceinline__ bool advance(Blk& b, int ee, const I4* entries) {
+  b.qb += QB;
+  if (b.qb < b.qe) return true;
+  return load_entry(b, b.e + 1, ee, entries);
+}
 
 }  // namespace
 
@@ -113,39 +127,105 @@ __global__ __launch_bounds__(256) void tree_attn_bwd_pre_kernel(BwdArgs a) {
 // 2. main
 template <typename T, int D>
 __global__ __launch_bounds__(256, 1) void tree_attn_bwd_kernel(BwdArgs a) {
-  using L = BwdSmem<T, D>;
-  constexpr bool SPLIT = L::SPLIT;
-  constexpr int KC = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int WPD = 4 / DB;                      // waves per dQ column block
-  constexpr int DQ_CHUNKS = kBwdKeys / 16 / WPD;   // 16-key chunks per wave in dQ
+  using C = BwdCfg<T, D>;
+  constexpr bool SPLIT = C::SPLIT;
+  constexpr int QB = C::QB, NSUB = C::NSUB, NBUF = C::NBUF, KC = C::KC, DB = C::DB;
+  constexpr int WPD = 4 / DB;                     // waves per dQ column block
+  constexpr int DQ_CHUNKS = kBwdKeys / 16 / WPD;  // 16-key chunks per wave in dQ
+  using KT = Tile<D, kBwdKeys>;   // K tile (dQ operand)
+  using QT = Tile<D, QB>;         // Q / dO tiles of a step
+  using ST = Tile<QB, kBwdKeys>;  // dS tile [key][query]
   extern __shared__ __attribute__((aligned(16))) char smem_dyn[];
   LDS_PTR(char) lds = (LDS_PTR(char))(smem_dyn);
-  LDS_PTR(char) k_hi = lds + L::K_OFF;
-  LDS_PTR(char) k_lo = k_hi + L::K_PLANE;
-  LDS_PTR(char) q_hi = lds + L::Q_OFF;
-  LDS_PTR(char) q_lo = q_hi + L::Q_PLANE;
-  LDS_PTR(char) do_hi = lds + L::DO_OFF;
-  LDS_PTR(char) do_lo = do_hi + L::Q_PLANE;
-  LDS_PTR(char) ds_hi = lds + L::DS_OFF;
-  LDS_PTR(char) ds_lo = ds_hi + L::DS_PLANE;
-  LDS_PTR(float) lse_s = (LDS_PTR(float))(lds + L::LSE_OFF);
-  LDS_PTR(float) dvec_s = (LDS_PTR(float))(lds + L::DV_OFF);
+  LDS_PTR(char) k_hi = lds + C::K_OFF;
+  LDS_PTR(char) k_lo = k_hi + C::K_PLANE;
 
   const I8 it = a.items[blockIdx.x];
   const int k0 = it.v[0], k1 = it.v[1], g = it.v[2], eb = it.v[3], ee = it.v[4];
   const int slot = it.v[5];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int64_t last = a.n_tokens - 1;
   const int64_t qs = static_cast<int64_t>(a.hq) * D;
   const int64_t ks = static_cast<int64_t>(a.hkv) * D;
   const T* Kg = static_cast<const T*>(a.k) + static_cast<int64_t>(g) * D;
   const T* Vg = static_cast<const T*>(a.v) + static_cast<int64_t>(g) * D;
+  const T* Qall = static_cast<const T*>(a.q);
+  const T* dOall = static_cast<const T*>(a.dout);
   const int key = k0 + 32 * wave + l32;  // this lane's key (column of S)
-  const int kmax = (k1 < k0 + kBwdKeys ? k1 : k0 + kBwdKeys) - 1;
 
-  // K tile for dQ (transposed reads) and this wave's K / V operands
+  auto q_tile = [&](int buf, int plane) {
+    return lds + C::Q_OFF + (buf * C::NP + plane) * C::Q_PLANE;
+  };
+  auto do_tile = [&](int buf, int plane) {
+    return lds + C::DO_OFF + (buf * C::NP + plane) * C::Q_PLANE;
+  };
+  auto ds_tile = [&](int buf, int plane) {
+    return lds + C::DS_OFF + (buf * C::NP + plane) * C::DS_PLANE;
+  };
+  auto ld_tile = [&](int buf) { return (LDS_PTR(float))(lds + C::LD_OFF + buf * C::LD_BYTES); };
+
+  // Prefetch state for the next step: Q / dO rows (buffer loads straight to
+  // LDS for bf16, through registers for fp32) and one LSE or D value per
+  // thread.
+  constexpr int SPLIT_PER = SPLIT ? QB * D / 4 / 256 : 1;
+  i32x4 qreg[SPLIT_PER], dreg[SPLIT_PER];
+  float ld_reg = 0.f;
+  TileLoader<D, QB, 4> tl;
+  if constexpr (!SPLIT) tl.init(static_cast<int>(qs * sizeof(T)), wave, lane);
+  const T* Qend = Qall + a.n_tokens * qs;
+  const T* dOend = dOall + a.n_tokens * qs;
+  auto issue = [&](const Blk& b, int buf) {
+    const int64_t r0 = b.qb;
+    const T* Qh = Qall + static_cast<int64_t>(b.h) * D;
+    const T* dOh = dOall + static_cast<int64_t>(b.h) * D;
+    if constexpr (!SPLIT) {
+      tl.issue(q_tile(buf, 0), make_rsrc(Qh + r0 * qs, Qend));
+      tl.issue(do_tile(buf, 0), make_rsrc(dOh + r0 * qs, dOend));
+    } else {
+      constexpr int CPR = D / 4;
+#pragma unroll
+      for (int i = 0; i < SPLIT_PER; ++i) {
+        const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
+        const int64_t row = r0 + r < last ? r0 + r : last;
+        qreg[i] = gload16(Qh + row * qs + cc * 4);
+        dreg[i] = gload16(dOh + row * qs + cc * 4);
+      }
+    }
+    if (tid < 2 * QB) {
+      const int r = tid % QB;
+      const int64_t row = r0 + r < last ? r0 + r : last;
+      const float* src = tid < QB ? a.lse : a.dvec;
+      ld_reg = src[static_cast<int64_t>(b.h) * a.n_tokens + row];
+    }
+  };
+  auto commit = [&](int buf) {
+    if constexpr (SPLIT) {
+      constexpr int CPR = D / 4;
+#pragma unroll
+      for (int i = 0; i < SPLIT_PER; ++i) {
+        const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f32x4 f = __builtin_bit_cast(f32x4, t ? dreg[i] : qreg[i]);
+          bf16x4 h, l;
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            h[s2] = to_bf16(f[s2]);
+            l[s2] = to_bf16(f[s2] - static_cast<float>(h[s2]));
+          }
+          LDS_PTR(char) hi = t ? do_tile(buf, 0) : q_tile(buf, 0);
+          LDS_PTR(char) lo = t ? do_tile(buf, 1) : q_tile(buf, 1);
+          *reinterpret_cast<LDS_PTR(bf16x4)>(hi + QT::elem_off(r, cc * 4)) = h;
+          *reinterpret_cast<LDS_PTR(bf16x4)>(lo + QT::elem_off(r, cc * 4)) = l;
+        }
+      }
+    }
+    if (tid < 2 * QB) ld_tile(buf)[tid] = tid < QB ? ld_reg * kLog2e : ld_reg;
+  };
+
+  // K tile (for dQ) and this wave's K / V operands
   load_tile<T, D, kBwdKeys, 256>(k_hi, k_lo, Kg, ks, k0, last, tid);
   Frag<SPLIT> kf[KC], vf[KC];
   {
@@ -168,28 +248,78 @@ __global__ __launch_bounds__(256, 1) void tree_attn_bwd_kernel(BwdArgs a) {
   const int dq_kc0 = (wave % WPD) * DQ_CHUNKS;  // first 16-key chunk of this wave
   const int qrow_a = swap23(l32);               // A-operand row of S / dP
 
-  for (int e = eb; e < ee; ++e) {
-    const I4 en = a.entries[e];
-    const int h = en.x, qa = en.y, qe = en.z;
-    const bool causal = en.w != 0;
-    const T* Qh = static_cast<const T*>(a.q) + static_cast<int64_t>(h) * D;
-    const T* dOh = static_cast<const T*>(a.dout) + static_cast<int64_t>(h) * D;
-    const float* lse_h = a.lse + static_cast<int64_t>(h) * a.n_tokens;
-    const float* dvec_h = a.dvec + static_cast<int64_t>(h) * a.n_tokens;
-    float* dq_h = a.dq_acc + static_cast<int64_t>(h) * D;
-    for (int qb = qa; qb < qe; qb += kBwdRows) {
-      __syncthreads();  // previous block's LDS readers are done
-      load_tile<T, D, kBwdRows, 256>(q_hi, q_lo, Qh, qs, qb, last, tid);
-      load_tile<T, D, kBwdRows, 256>(do_hi, do_lo, dOh, qs, qb, last, tid);
-      if (tid < kBwdRows) {
-        const int64_t r = qb + tid < last ? qb + tid : last;
-        lse_s[tid] = lse_h[r] * kLog2e;
-        dvec_s[tid] = dvec_h[r];
+  // dQ[q][d] += scale * sum_key dS[q][key] K[key][d] for a finished step,
+  // from its dS buffer; lane holds column d, query rows in registers.  The
+  // fp32 adds go through a buffer resource based at the step's first row:
+  // rows past the last token fall outside its range and are dropped, rows
+  // past the step's range add exact zeros (their dS is zero).
+  const int dq_voff = (4 * half * static_cast<int>(qs) + 32 * dq_db + l32) * 4;
+  const float* dq_end = a.dq_acc + a.n_tokens * qs;
+  auto dq_step = [&](const Blk& b, int dbuf) {
+    const rsrc_t rs = make_rsrc(a.dq_acc + static_cast<int64_t>(b.qb) * qs +
+                                    static_cast<int64_t>(b.h) * D, dq_end);
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+      f32x16 qacc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) qacc[v] = 0.f;
+#pragma unroll
+      for (int c = 0; c < DQ_CHUNKS; ++c) {
+        const int kc = dq_kc0 + c;
+        Frag<SPLIT> af, bf;
+        af.h = tr_operand<ST>(ds_tile(dbuf, 0), 16 * kc, 32 * sb, lane);
+        bf.h = tr_operand<KT>(k_hi, 16 * kc, 32 * dq_db, lane);
+        if constexpr (SPLIT) {
+          af.l = tr_operand<ST>(ds_tile(dbuf, 1), 16 * kc, 32 * sb, lane);
+          bf.l = tr_operand<KT>(k_lo, 16 * kc, 32 * dq_db, lane);
+        }
+        mma<SPLIT>(qacc, af, bf);
       }
-      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 32 * sb + 8 * (v >> 2) + (v & 3);  // plus 4 half (in dq_voff)
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+            a.scale * qacc[v], rs, dq_voff, row * static_cast<int>(qs) * 4, 0);
+      }
+    }
+  };
 
-      // S = Q K^T and dP = dO V^T for this wave's 32 keys.  Register v of
-      // this lane is query row 16 (v / 8) + 8 half + v % 8 of the block.
+  Blk cur;
+  load_entry(cur, eb, ee, a.entries);
+  Blk prev = cur;
+  bool has_prev = false;
+  issue(cur, 0);
+  commit(0);
+  int step = 0;
+  while (true) {
+    Blk nxt = cur;
+    const bool has_next = advance<QB>(nxt, ee, a.entries);
+    const int buf = NBUF == 2 ? (step & 1) : 0;
+    wait_vm();
+    __syncthreads();  // step's rows are in LDS; dS of the previous step is complete
+    if (NBUF == 2 && has_next) issue(nxt, buf ^ 1);
+    if (has_prev) dq_step(prev, (step - 1) & 1);
+
+    LDS_PTR(float) ldv = ld_tile(buf);
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+      const int qs0 = cur.qb + 32 * sb;           // first row of the sub-block
+      const int wk0 = k0 + 32 * wave;             // first key of this wave
+      // wave-uniform: no row of the sub-block sees any key of this wave
+      const bool skip = qs0 >= cur.qe || wk0 >= k1 || (cur.causal && wk0 > qs0 + 31);
+      const int r_ds = 32 * wave + l32;           // this lane's row of the dS tile
+      if (skip) {
+        const bf16x8 z = {};
+#pragma unroll
+        for (int pl = 0; pl < C::NP; ++pl) {
+          LDS_PTR(char) t = ds_tile(step & 1, pl);
+          *reinterpret_cast<LDS_PTR(bf16x8)>(t + ST::chunk_off(r_ds, 4 * sb + half)) = z;
+          *reinterpret_cast<LDS_PTR(bf16x8)>(t + ST::chunk_off(r_ds, 4 * sb + 2 + half)) = z;
+        }
+        continue;
+      }
+      // S = Q K^T and dP = dO V^T for this wave's 32 keys and 32 query rows;
+      // register v of this lane is query row 32 sb + 16 (v / 8) + 8 half + v % 8.
       f32x16 sacc, pacc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -199,87 +329,89 @@ __global__ __launch_bounds__(256, 1) void tree_attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         Frag<SPLIT> qa_f, da_f;
-        qa_f.h = row_operand<D>(q_hi, qrow_a, 2 * kc + half);
-        da_f.h = row_operand<D>(do_hi, qrow_a, 2 * kc + half);
+        qa_f.h = row_operand<QT>(q_tile(buf, 0), 32 * sb + qrow_a, 2 * kc + half);
+        da_f.h = row_operand<QT>(do_tile(buf, 0), 32 * sb + qrow_a, 2 * kc + half);
         if constexpr (SPLIT) {
-          qa_f.l = row_operand<D>(q_lo, qrow_a, 2 * kc + half);
-          da_f.l = row_operand<D>(do_lo, qrow_a, 2 * kc + half);
+          qa_f.l = row_operand<QT>(q_tile(buf, 1), 32 * sb + qrow_a, 2 * kc + half);
+          da_f.l = row_operand<QT>(do_tile(buf, 1), 32 * sb + qrow_a, 2 * kc + half);
         }
         mma<SPLIT>(sacc, qa_f, kf[kc]);
         mma<SPLIT>(pacc, da_f, vf[kc]);
       }
-      const bool need_mask = (qb + kBwdRows > qe) || (kmax >= k1) || (k1 - k0 < kBwdKeys) ||
-                             (causal && kmax > qb);
+      // P = 2^(c s - LSE log2 e) recomputed from the saved LSE; masked where
+      // a row is past the range, a key past the tile, or (causal) key > row.
+      const bool need_mask = qs0 + 32 > cur.qe || wk0 + 32 > k1 || (cur.causal && wk0 + 31 > qs0);
       float p[16], ds[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int ql = 16 * (v >> 3) + 8 * half + (v & 7);
-        float pv = __builtin_amdgcn_exp2f(sacc[v] * a.scale_log2 - lse_s[ql]);
-        if (need_mask) {
-          const int q = qb + ql;
-          const bool ok = q < qe && key < k1 && (!causal || key <= q);
-          pv = ok ? pv : 0.f;
+        const int ql = 32 * sb + 16 * (v >> 3) + 8 * half + (v & 7);
+        p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], a.scale_log2, -ldv[ql]));
+      }
+      if (need_mask) {
+        const int qlim = cur.qe - cur.qb;                       // local rows < qlim
+        const int kq = cur.causal ? key - cur.qb : -(1 << 30);  // local rows >= kq
+        const bool kok = key < k1;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int ql = 32 * sb + 16 * (v >> 3) + 8 * half + (v & 7);
+          p[v] = (kok && ql < qlim && ql >= kq) ? p[v] : 0.f;
         }
-        p[v] = pv;
-        ds[v] = pv * (pacc[v] - dvec_s[ql]);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ql = 32 * sb + 16 * (v >> 3) + 8 * half + (v & 7);
+        ds[v] = p[v] * (pacc[v] - ldv[QB + ql]);
       }
       const Frag<SPLIT> pf0 = pack8<SPLIT>(p), pf1 = pack8<SPLIT>(p + 8);
       const Frag<SPLIT> sf0 = pack8<SPLIT>(ds), sf1 = pack8<SPLIT>(ds + 8);
 
-      // dV += P^T dO, dK += dS^T Q (operands dO, Q transposed from LDS)
+      // dV += P^T dO, dK += dS^T Q (dO, Q read transposed from LDS)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int qc = 0; qc < 2; ++qc) {
           Frag<SPLIT> bo, bq;
-          bo.h = tr_operand<D>(do_hi, 16 * qc, 32 * db, lane);
-          bq.h = tr_operand<D>(q_hi, 16 * qc, 32 * db, lane);
+          bo.h = tr_operand<QT>(do_tile(buf, 0), 32 * sb + 16 * qc, 32 * db, lane);
+          bq.h = tr_operand<QT>(q_tile(buf, 0), 32 * sb + 16 * qc, 32 * db, lane);
           if constexpr (SPLIT) {
-            bo.l = tr_operand<D>(do_lo, 16 * qc, 32 * db, lane);
-            bq.l = tr_operand<D>(q_lo, 16 * qc, 32 * db, lane);
+            bo.l = tr_operand<QT>(do_tile(buf, 1), 32 * sb + 16 * qc, 32 * db, lane);
+            bq.l = tr_operand<QT>(q_tile(buf, 1), 32 * sb + 16 * qc, 32 * db, lane);
           }
           mma<SPLIT>(dv_acc[db], qc ? pf1 : pf0, bo);
           mma<SPLIT>(dk_acc[db], qc ? sf1 : sf0, bq);
         }
       }
 
-      // dS -> LDS as [key][query]
-      {
-        const int r = 32 * wave + l32;
-        *reinterpret_cast<LDS_PTR(bf16x8)>(ds_hi + r * kDsRowBytes + 16 * half) = sf0.h;
-        *reinterpret_cast<LDS_PTR(bf16x8)>(ds_hi + r * kDsRowBytes + 32 + 16 * half) = sf1.h;
+      // dS -> LDS as [key][query] for the next step's dQ
+#pragma unroll
+      for (int pl = 0; pl < C::NP; ++pl) {
+        LDS_PTR(char) t = ds_tile(step & 1, pl);
+        bf16x8 x0, x1;
         if constexpr (SPLIT) {
-          *reinterpret_cast<LDS_PTR(bf16x8)>(ds_lo + r * kDsRowBytes + 16 * half) = sf0.l;
-          *reinterpret_cast<LDS_PTR(bf16x8)>(ds_lo + r * kDsRowBytes + 32 + 16 * half) = sf1.l;
+          x0 = pl ? sf0.l : sf0.h;
+          x1 = pl ? sf1.l : sf1.h;
+        } else {
+          x0 = sf0.h;
+          x1 = sf1.h;
         }
-      }
-      __syncthreads();
-
-      // dQ[q][d] += scale * sum_key dS[q][key] K[key][d] for this wave's
-      // column block and key chunks; lane holds column d, rows in registers
-      f32x16 qacc;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) qacc[v] = 0.f;
-#pragma unroll
-      for (int c = 0; c < DQ_CHUNKS; ++c) {
-        const int kc = dq_kc0 + c;
-        Frag<SPLIT> af, bf;
-        af.h = ds_tr_operand(ds_hi, 16 * kc, lane);
-        bf.h = tr_operand<D>(k_hi, 16 * kc, 32 * dq_db, lane);
-        if constexpr (SPLIT) {
-          af.l = ds_tr_operand(ds_lo, 16 * kc, lane);
-          bf.l = tr_operand<D>(k_lo, 16 * kc, 32 * dq_db, lane);
-        }
-        mma<SPLIT>(qacc, af, bf);
-      }
-      const int d = 32 * dq_db + l32;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int q = qb + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (q < qe) atomicAdd(dq_h + static_cast<int64_t>(q) * qs + d, a.scale * qacc[v]);
+        *reinterpret_cast<LDS_PTR(bf16x8)>(t + ST::chunk_off(r_ds, 4 * sb + half)) = x0;
+        *reinterpret_cast<LDS_PTR(bf16x8)>(t + ST::chunk_off(r_ds, 4 * sb + 2 + half)) = x1;
       }
     }
+
+    if (!has_next) break;
+    if (NBUF == 1) {
+      __syncthreads();  // everyone is done with the single Q / dO buffer
+      issue(nxt, 0);
+    }
+    commit(NBUF == 2 ? buf ^ 1 : 0);
+    prev = cur;
+    has_prev = true;
+    cur = nxt;
+    ++step;
   }
+  __syncthreads();  // dS of the last step is complete
+  dq_step(cur, step & 1);
 
   // dK, dV of this wave's keys: lane holds column d, key rows in registers
 #pragma unroll
@@ -357,7 +489,7 @@ static hipError_t pre_t(const BwdArgs& a, hipStream_t s) {
 template <typename T, int D>
 static hipError_t main_t(const BwdArgs& a, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
-  constexpr int bytes = BwdSmem<T, D>::BYTES;
+  constexpr int bytes = BwdCfg<T, D>::BYTES;
   auto kern = tree_attn_bwd_kernel<T, D>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);

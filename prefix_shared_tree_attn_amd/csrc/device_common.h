@@ -78,26 +78,29 @@ __device__ __forceinline__ Frag<SPLIT> pack8(const float* x) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles of bf16 rows with D columns.  16-byte chunk c of row r is stored
-// at chunk c ^ swz(r).  The swizzle makes both access patterns of the kernels
-// free of bank conflicts: 16 lanes reading the same chunk of 16 consecutive
-// rows (row operands, ds_read_b128), and 16-lane transpose reads of 4
-// consecutive rows x 32 bytes (ds_read_tr16_b64).
-template <int D>
-struct TileLayout {
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = D / 8;
-  __device__ __forceinline__ static int swz(int r) {
-    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  }
-  // byte offset of the 16-byte chunk c of row r
+// LDS tiles: ROWS rows x D bf16 columns, stored as D / 32 sub-tiles of 32
+// columns, each with 64-byte rows.  The 16-byte chunk cc (0..3) of row r in a
+// sub-tile sits at chunk cc ^ ((r >> 2) & 3).  Four consecutive rows share a
+// 256-byte bank line, so
+//  * 16 lanes reading the same chunk of 16 consecutive rows (row operands,
+//    ds_read_b128) hit 16 distinct 16-byte slots, and
+//  * a 16-lane transpose read of 4 consecutive rows x 32 bytes plus its
+//    neighbour group's next 32 bytes (ds_read_tr16_b64) fill one bank line,
+// both free of bank conflicts; and because the swizzle depends only on bits
+// 2..3 of the row, the sub-tile and any row offset that is a multiple of 16
+// stay compile-time immediates of the LDS instructions.
+template <int D, int ROWS>
+struct Tile {
+  static constexpr int SUB = ROWS * 64;  // bytes of one 32-column sub-tile
+  static constexpr int BYTES = (D / 32) * SUB;
+  __device__ __forceinline__ static int swz(int r) { return (r >> 2) & 3; }
+  // byte offset of the 16-byte chunk c (columns 8c .. 8c + 7) of row r
   __device__ __forceinline__ static int chunk_off(int r, int c) {
-    return r * kRowBytes + ((c ^ swz(r)) << 4);
+    return (c >> 2) * SUB + r * 64 + (((c & 3) ^ swz(r)) << 4);
   }
   // byte offset of element col of row r (col a multiple of 4 for 8-byte reads)
   __device__ __forceinline__ static int elem_off(int r, int col) {
-    return r * kRowBytes + (((col >> 3) ^ swz(r)) << 4) + ((col & 7) << 1);
+    return (col >> 5) * SUB + r * 64 + ((((col >> 3) & 3) ^ swz(r)) << 4) + ((col & 7) << 1);
   }
 };
 
@@ -113,19 +116,18 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const LDS_PTR(char) base, int off)
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// Transposed operand from a row-major LDS tile: returns, for this lane, the 8
-// values tile[row0 + 8 * (lane / 32) + s][col0 + (lane % 32)], s = 0..7 --
-// i.e. an MFMA operand whose lane index runs along the tile's columns and
-// whose reduction slots run along its rows.  `row0` must be a multiple of 8
-// and `col0` a multiple of 32.
-template <int D>
+// Transposed operand from an LDS tile: returns, for this lane, the 8 values
+// tile[row0 + 8 * (lane / 32) + s][col0 + (lane % 32)], s = 0..7 -- an MFMA
+// operand whose lane index runs along the tile's columns and whose reduction
+// slots run along its rows.  `row0` must be a multiple of 16 and `col0` of 32.
+template <class TL>
 __device__ __forceinline__ bf16x8 tr_operand(const LDS_PTR(char) base, int row0, int col0,
                                              int lane) {
   const int grp = lane >> 4, L = lane & 15;
   const int r = row0 + 8 * (grp >> 1) + (L >> 2);
   const int c = col0 + 16 * (grp & 1) + 4 * (L & 3);
-  const bf16x4 lo = lds_read_tr(base, TileLayout<D>::elem_off(r, c));
-  const bf16x4 hi = lds_read_tr(base, TileLayout<D>::elem_off(r + 4, c));
+  const bf16x4 lo = lds_read_tr(base, TL::elem_off(r, c));
+  const bf16x4 hi = lds_read_tr(base, TL::elem_off(r + 4, c));
   bf16x8 out;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -135,10 +137,10 @@ __device__ __forceinline__ bf16x8 tr_operand(const LDS_PTR(char) base, int row0,
   return out;
 }
 
-// Row operand from a row-major LDS tile: the 8 values tile[row][c8 * 8 + s].
-template <int D>
+// Row operand from an LDS tile: the 8 values tile[row][c8 * 8 + s].
+template <class TL>
 __device__ __forceinline__ bf16x8 row_operand(const LDS_PTR(char) base, int row, int c8) {
-  return lds_read16(base, TileLayout<D>::chunk_off(row, c8));
+  return lds_read16(base, TL::chunk_off(row, c8));
 }
 
 // Row index used for the A operand so that output register v of lane half h
@@ -195,7 +197,7 @@ __device__ __forceinline__ void load_tile(LDS_PTR(char) hi, LDS_PTR(char) lo, co
     const int c = tid + i * NT;
     const int r = c / CPR, cc = c % CPR;
     if constexpr (sizeof(T) == 2) {
-      lds_write16(hi, TileLayout<D>::chunk_off(r, cc), v[i]);
+      lds_write16(hi, Tile<D, ROWS>::chunk_off(r, cc), v[i]);
     } else {
       const f32x4 f = __builtin_bit_cast(f32x4, v[i]);
       bf16x4 h, l;
@@ -204,11 +206,85 @@ __device__ __forceinline__ void load_tile(LDS_PTR(char) hi, LDS_PTR(char) lo, co
         h[s] = to_bf16(f[s]);
         l[s] = to_bf16(f[s] - static_cast<float>(h[s]));
       }
-      *reinterpret_cast<LDS_PTR(bf16x4)>(hi + TileLayout<D>::elem_off(r, cc * 4)) = h;
-      *reinterpret_cast<LDS_PTR(bf16x4)>(lo + TileLayout<D>::elem_off(r, cc * 4)) = l;
+      *reinterpret_cast<LDS_PTR(bf16x4)>(hi + Tile<D, ROWS>::elem_off(r, cc * 4)) = h;
+      *reinterpret_cast<LDS_PTR(bf16x4)>(lo + Tile<D, ROWS>::elem_off(r, cc * 4)) = l;
     }
   }
 }
+
+// Direct global -> LDS loads (gfx950 global_load_lds_dwordx4): issues the
+// loads of rows [row0, row0 + ROWS) of a bf16 tensor (rows `stride` elements
+// apart, clamped to `last`) into a swizzled LDS tile.  The instruction writes
+// lane l's 16 bytes to LDS base + 16 l, so each lane fetches the logical
+// chunk that the swizzle places at its slot.  Completion is tracked by
+// vmcnt; callers wait (wait_vm) and synchronise before reading the tile.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void issue_tile_lds(LDS_PTR(char) tile, const __bf16* base,
+                                               int64_t stride, int64_t row0, int64_t last,
+                                               int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int PER = ROWS * CPR / (64 * NW);
+  static_assert(ROWS * CPR % (64 * NW) == 0, "tile must split into whole wave loads");
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int slot = (wave * PER + j) * 64;
+    const int p = slot + lane;  // 16-byte LDS slot this lane fills
+    const int sub = p / (ROWS * 4), rem = p % (ROWS * 4);
+    const int r = rem >> 2;
+    const int c = sub * 4 + ((rem & 3) ^ Tile<D, ROWS>::swz(r));
+    const int64_t row = row0 + r < last ? row0 + r : last;
+    __builtin_amdgcn_global_load_lds(base + row * stride + c * 8,
+                                     (LDS_PTR(void))(tile + slot * 16), 16, 0, 0);
+  }
+}
+
+// Buffer resources (V#): a 64-bit base in scalar registers, no stride, and a
+// byte range; loads past the range return zero and stores / atomics past it
+// are dropped (the scalar offset counts toward the range).  Row tiles near
+// the end of a tensor therefore need no clamping.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;  // raw 32-bit buffer, gfx9 family
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, const void* end) {
+  const int64_t n = static_cast<const char*>(end) - static_cast<const char*>(base);
+  const uint32_t r = n <= 0 ? 0u : (n >= 0xFFFFFFFFll ? 0xFFFFFFFFu : static_cast<uint32_t>(n));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(r), kRsrcFlags);
+}
+
+// Loads a ROWS x D bf16 row tile into a swizzled LDS tile (Tile<D, ROWS>)
+// with buffer loads straight to LDS: the wave's lanes fill consecutive
+// 16-byte LDS slots, each lane fetching the logical chunk the swizzle puts at
+// its slot.  Per-lane byte offsets are fixed for a given row stride, so a
+// step only changes the buffer base.
+template <int D, int ROWS, int NW>
+struct TileLoader {
+  static constexpr int PER = ROWS * (D / 8) / (64 * NW);
+  static_assert(ROWS * (D / 8) % (64 * NW) == 0, "tile must split into whole wave loads");
+  int voff[PER];
+  int lds0;
+  __device__ __forceinline__ void init(int row_stride_bytes, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int p = (wave * PER + j) * 64 + lane;
+      const int sub = p / (ROWS * 4), rem = p % (ROWS * 4);
+      const int r = rem >> 2;
+      const int c = sub * 4 + ((rem & 3) ^ Tile<D, ROWS>::swz(r));
+      voff[j] = r * row_stride_bytes + c * 16;
+    }
+    lds0 = wave * PER * 1024;
+  }
+  __device__ __forceinline__ void issue(LDS_PTR(char) tile, rsrc_t rs) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_PTR(void))(tile + lds0 + j * 1024), 16,
+                                               voff[j], 0, 0, 0);
+  }
+};
+
+// Waits until this wave's vector memory operations (loads, direct-to-LDS
+// loads, stores, atomics) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Stores four consecutive fp32 values as output elements.
 __device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {

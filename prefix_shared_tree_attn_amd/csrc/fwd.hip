@@ -21,18 +21,29 @@
 namespace tree_attn {
 
 template <typename T, int D>
+struct FwdCfg {
+  static constexpr bool SPLIT = IsSplit<T>::value;
+  static constexpr int NP = SPLIT ? 2 : 1;
+  // K / V buffers: two (the next key tile streams in while the current one
+  // is used) unless fp32 hi/lo planes at D = 128 would not fit.
+  static constexpr int NBUF = (SPLIT && D == 128) ? 1 : 2;
+  static constexpr int PLANE = kFwdKeys * D * 2;
+  static constexpr int BYTES = NBUF * 2 * NP * PLANE;
+};
+
+template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
-  constexpr bool SPLIT = IsSplit<T>::value;
-  constexpr int NP = SPLIT ? 2 : 1;
+  using C = FwdCfg<T, D>;
+  constexpr bool SPLIT = C::SPLIT;
+  constexpr int NP = C::NP, NBUF = C::NBUF;
   constexpr int KC = D / 16;  // 16-wide reduction chunks of q.k
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  constexpr int PLANE = kFwdKeys * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * NP * PLANE];
-  LDS_PTR(char) lds = (LDS_PTR(char))(smem);
-  LDS_PTR(char) k_hi = lds;
-  LDS_PTR(char) k_lo = lds + PLANE;
-  LDS_PTR(char) v_hi = lds + NP * PLANE;
-  LDS_PTR(char) v_lo = lds + NP * PLANE + PLANE;
+  constexpr int PLANE = C::PLANE;
+  using KT = Tile<D, kFwdKeys>;  // K and V tiles of a key step
+  extern __shared__ __attribute__((aligned(16))) char smem_dyn[];
+  LDS_PTR(char) lds = (LDS_PTR(char))(smem_dyn);
+  auto k_tile = [&](int buf, int plane) { return lds + ((buf * 2 + 0) * NP + plane) * PLANE; };
+  auto v_tile = [&](int buf, int plane) { return lds + ((buf * 2 + 1) * NP + plane) * PLANE; };
 
   // Workgroup -> (query tile, kv head, query head).  Workgroup b runs on XCD
   // b % 8; the query heads of one kv group get consecutive slots on the same
@@ -48,7 +59,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   const I4 t = a.tiles[tile];
   const int q0 = t.x, q1 = t.y;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int64_t last = a.n_tokens - 1;
   const int64_t qs = static_cast<int64_t>(a.hq) * D;   // row stride of Q / O
@@ -67,6 +79,52 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
     for (int kc = 0; kc < KC; ++kc) qf[kc] = load_frag8(qp + 16 * kc);
   }
 
+  // Key-tile prefetch: buffer loads straight to LDS for bf16, through
+  // registers (hi/lo split) for fp32.
+  constexpr int SPLIT_PER = SPLIT ? kFwdKeys * D / 4 / 256 : 1;
+  i32x4 kreg[SPLIT_PER], vreg[SPLIT_PER];
+  TileLoader<D, kFwdKeys, 4> tl;
+  if constexpr (!SPLIT) tl.init(static_cast<int>(ks * sizeof(T)), wave, lane);
+  const T* Kend = static_cast<const T*>(a.k) + a.n_tokens * ks;
+  const T* Vend = static_cast<const T*>(a.v) + a.n_tokens * ks;
+  auto issue = [&](int kt, int buf) {
+    if constexpr (!SPLIT) {
+      tl.issue(k_tile(buf, 0), make_rsrc(K + static_cast<int64_t>(kt) * ks, Kend));
+      tl.issue(v_tile(buf, 0), make_rsrc(V + static_cast<int64_t>(kt) * ks, Vend));
+    } else {
+      constexpr int CPR = D / 4;
+#pragma unroll
+      for (int i = 0; i < SPLIT_PER; ++i) {
+        const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
+        const int64_t row = kt + r < last ? kt + r : last;
+        kreg[i] = gload16(K + row * ks + cc * 4);
+        vreg[i] = gload16(V + row * ks + cc * 4);
+      }
+    }
+  };
+  auto commit = [&](int buf) {
+    if constexpr (SPLIT) {
+      constexpr int CPR = D / 4;
+#pragma unroll
+      for (int i = 0; i < SPLIT_PER; ++i) {
+        const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
+#pragma unroll
+        for (int tv = 0; tv < 2; ++tv) {
+          const f32x4 f = __builtin_bit_cast(f32x4, tv ? vreg[i] : kreg[i]);
+          bf16x4 hi, lo;
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            hi[s2] = to_bf16(f[s2]);
+            lo[s2] = to_bf16(f[s2] - static_cast<float>(hi[s2]));
+          }
+          const int off = KT::elem_off(r, cc * 4);
+          *reinterpret_cast<LDS_PTR(bf16x4)>((tv ? v_tile(buf, 0) : k_tile(buf, 0)) + off) = hi;
+          *reinterpret_cast<LDS_PTR(bf16x4)>((tv ? v_tile(buf, 1) : k_tile(buf, 1)) + off) = lo;
+        }
+      }
+    }
+  };
+
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -75,87 +133,126 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   float m = -INFINITY;  // running max of base-2 scaled scores of row qrow
   float lsum = 0.f;     // running sum over this lane's keys
 
-  for (int ri = t.z; ri < t.w; ++ri) {
-    const I4 rg = a.ranges[ri];
-    const int k0 = rg.x, k1 = rg.y;
+  // Key tiles in order: the tile's ranges (ancestors root first, then the
+  // causal range of its own node), kFwdKeys keys at a time.
+  int ri = t.z;
+  I4 rg = a.ranges[ri];
+  int kt = rg.x;
+  issue(kt, 0);
+  commit(0);
+  int step = 0;
+  while (true) {
+    // the following key tile, if any
+    int nri = ri, nkt = kt + kFwdKeys;
+    I4 nrg = rg;
+    bool has_next = true;
+    if (nkt >= rg.y) {
+      nri = ri + 1;
+      has_next = nri < t.w;
+      if (has_next) {
+        nrg = a.ranges[nri];
+        nkt = nrg.x;
+      }
+    }
+    const int buf = NBUF == 2 ? (step & 1) : 0;
+    wait_vm();
+    __syncthreads();  // this tile is in LDS; everyone is done with the other buffer
+    if (NBUF == 2 && has_next) issue(nkt, buf ^ 1);
+
+    const int k1 = rg.y;
     const bool causal = rg.z != 0;
-    for (int kt = k0; kt < k1; kt += kFwdKeys) {
-      __syncthreads();  // all waves are done reading the previous tile
-      load_tile<T, D, kFwdKeys, 256>(k_hi, k_lo, K, ks, kt, last, tid);
-      load_tile<T, D, kFwdKeys, 256>(v_hi, v_lo, V, ks, kt, last, tid);
-      __syncthreads();
-
-      // S^T for keys kt + 32 kb + (0..31); A row r holds key swap23(r) so
-      // that register v of this lane is key 16 (v / 8) + 8 half + v % 8.
-      f32x16 sacc[2];
+    // every key of the tile lies past every row of this wave: nothing to do
+    const bool skip = causal && kt > wave_q0 + 31;
+    if (!skip) {
+    // S^T for keys kt + 32 kb + (0..31); A row r holds key swap23(r) so
+    // that register v of this lane is key 16 (v / 8) + 8 half + v % 8.
+    f32x16 sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-        const int krow = 32 * kb + swap23(l32);
+      for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+      const int krow = 32 * kb + swap23(l32);
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          Frag<SPLIT> af;
-          af.h = row_operand<D>(k_hi, krow, 2 * kc + half);
-          if constexpr (SPLIT) af.l = row_operand<D>(k_lo, krow, 2 * kc + half);
-          mma<SPLIT>(sacc[kb], af, qf[kc]);
-        }
+      for (int kc = 0; kc < KC; ++kc) {
+        Frag<SPLIT> af;
+        af.h = row_operand<KT>(k_tile(buf, 0), krow, 2 * kc + half);
+        if constexpr (SPLIT) af.l = row_operand<KT>(k_tile(buf, 1), krow, 2 * kc + half);
+        mma<SPLIT>(sacc[kb], af, qf[kc]);
       }
+    }
 
-      // scale, mask, online softmax
-      const bool need_mask = (kt + kFwdKeys > k1) || (causal && kt + kFwdKeys - 1 > wave_q0);
-      float mx = -INFINITY;
+    // Mask only on tiles that reach past the range or cross the diagonal of
+    // this wave's rows (wave-uniform test): key inside the range, and key <=
+    // query in the causal range.
+    const bool need_mask = (kt + kFwdKeys > k1) || (causal && kt + kFwdKeys - 1 > wave_q0);
+    if (need_mask) {
+      const int klim = (causal ? (k1 < qrow + 1 ? k1 : qrow + 1) : k1) - kt;  // local keys < klim
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float s = sacc[kb][v] * a.scale_log2;
-          if (need_mask) {
-            const int key = kt + 32 * kb + 16 * (v >> 3) + 8 * half + (v & 7);
-            const bool ok = key < k1 && (!causal || key <= qrow);
-            s = ok ? s : -INFINITY;
-          }
-          sacc[kb][v] = s;
-          mx = fmaxf(mx, s);
+          const int kl = 32 * kb + 16 * (v >> 3) + 8 * half + (v & 7);
+          sacc[kb][v] = kl < klim ? sacc[kb][v] : -INFINITY;
         }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+    }
+    // Online softmax in base 2.  The row max is taken on raw scores (the
+    // scale is positive) and the running reference m is moved only when the
+    // max grows by more than 8: p = 2^(c s - m) then stays below 2^8, and O
+    // and l always share the same m, so the result is exact either way.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    if (__any(mx > m + 8.f)) {
       const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       m = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(sacc[kb][v] - m_use);
-          sacc[kb][v] = p;
-          psum += p;
-        }
-      }
-      lsum = lsum * alpha + psum;
+      lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-
-      // O^T += V^T P^T over four 16-key chunks
+    }
+    const float neg_m = -m;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float pv[8];
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) pv[s] = sacc[c >> 1][8 * (c & 1) + s];
-        const Frag<SPLIT> pf = pack8<SPLIT>(pv);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          Frag<SPLIT> vf;
-          vf.h = tr_operand<D>(v_hi, 16 * c, 32 * db, lane);
-          if constexpr (SPLIT) vf.l = tr_operand<D>(v_lo, 16 * c, 32 * db, lane);
-          mma<SPLIT>(oacc[db], vf, pf);
-        }
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], a.scale_log2, neg_m));
+        sacc[kb][v] = p;
+        lsum += p;
       }
     }
+
+    // O^T += V^T P^T over four 16-key chunks
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float pv[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) pv[s] = sacc[c >> 1][8 * (c & 1) + s];
+      const Frag<SPLIT> pf = pack8<SPLIT>(pv);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        Frag<SPLIT> vf;
+        vf.h = tr_operand<KT>(v_tile(buf, 0), 16 * c, 32 * db, lane);
+        if constexpr (SPLIT) vf.l = tr_operand<KT>(v_tile(buf, 1), 16 * c, 32 * db, lane);
+        mma<SPLIT>(oacc[db], vf, pf);
+      }
+    }
+    }  // !skip
+
+    if (!has_next) break;
+    if (NBUF == 1) {
+      __syncthreads();  // everyone is done with the single K / V buffer
+      issue(nkt, 0);
+    }
+    commit(NBUF == 2 ? buf ^ 1 : 0);
+    ri = nri;
+    rg = nrg;
+    kt = nkt;
+    ++step;
   }
 
   // finalize: O = O^T / l, LSE = ln 2 * (m + log2 l)
@@ -175,21 +272,27 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+template <typename T, int D>
+static hipError_t fwd_t(const FwdArgs& a, int64_t n_blocks, hipStream_t s) {
+  constexpr int bytes = FwdCfg<T, D>::BYTES;
+  auto kern = tree_attn_fwd_kernel<T, D>;
+  if (bytes > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_blocks)), dim3(256), bytes, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, int64_t n_blocks,
                       hipStream_t stream) {
   if (n_blocks <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(n_blocks)), block(256);
-  if (dtype == 0 && head_dim == 128)
-    hipLaunchKernelGGL((tree_attn_fwd_kernel<__bf16, 128>), grid, block, 0, stream, a);
-  else if (dtype == 0 && head_dim == 64)
-    hipLaunchKernelGGL((tree_attn_fwd_kernel<__bf16, 64>), grid, block, 0, stream, a);
-  else if (dtype == 1 && head_dim == 128)
-    hipLaunchKernelGGL((tree_attn_fwd_kernel<float, 128>), grid, block, 0, stream, a);
-  else if (dtype == 1 && head_dim == 64)
-    hipLaunchKernelGGL((tree_attn_fwd_kernel<float, 64>), grid, block, 0, stream, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (dtype == 0 && head_dim == 128) return fwd_t<__bf16, 128>(a, n_blocks, stream);
+  if (dtype == 0 && head_dim == 64) return fwd_t<__bf16, 64>(a, n_blocks, stream);
+  if (dtype == 1 && head_dim == 128) return fwd_t<float, 128>(a, n_blocks, stream);
+  if (dtype == 1 && head_dim == 64) return fwd_t<float, 64>(a, n_blocks, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tree_attn
