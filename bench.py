@@ -51,19 +51,27 @@ def _args():
     return ap.parse_args()
 
 
-def _traffic_from_profile(workload: str):
-    """HBM bytes per launch of the backward main kernel from the committed
-    counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"bwd_main_{workload}_traffic.json")
+def _traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch of a kernel from the committed counter summary,
+    if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "prefix_shared_tree_attn_amd", "csrc", "bwd.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("bwd_hip_sha256") != sha:
+    if rec.get("sources_sha256") != _sources_sha():
         return None
     return rec.get("bytes_per_launch")
+
+
+def _sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "prefix_shared_tree_attn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
 
 
 def cpu_baseline(t, spec, budget_heads: int | None = None):
@@ -188,14 +196,29 @@ def main() -> int:
         r = kt[kind]
         return r["total_ms"] / max(r["launches"], 1)
 
-    bwd_main_ms = avg_ms("bwd_main")
-    fwd_ms = avg_ms("fwd")
-    bwd_achieved = bwd_flop / (bwd_main_ms * 1e-3) / 1e12
-    fwd_achieved = fwd_flop / (fwd_ms * 1e-3) / 1e12
     esize = 2 if dtype == "bf16" else 4
-    # backward preprocess: reads O and dO, writes D_t and zeroes the fp32 dQ accumulator
-    pre_bytes = n * hq * d * (2 * esize + 4) + n * hq * 4
-    post_bytes = n * hq * d * (4 + esize) + 2 * pstats["bwd_slots"] * 128 * d * 4
+    # Algorithmic work of each kernel (2 D FLOP per (query, key, head) and
+    # product): the dK/dV kernel forms S, dP, dV and dK (8 D); the dQ kernel
+    # forms S, dP and dQ (6 D) -- it recomputes S and dP instead of receiving
+    # dS through an atomic reduction.
+    kern_flop = {"fwd": 4.0 * d * hq * pairs, "bwd_dkdv": 8.0 * d * hq * pairs,
+                 "bwd_dq": 6.0 * d * hq * pairs}
+    kern_name = {"fwd": "tree_attn_fwd_kernel", "bwd_dkdv": "tree_attn_dkdv_kernel",
+                 "bwd_dq": "tree_attn_dq_kernel"}
+
+    def roof(kind):
+        ach = kern_flop[kind] / (avg_ms(kind) * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": kern_name[kind], "achieved": ach, "peak": peak,
+                "unit": "TFLOP/s", "frac": ach / peak, "flop_per_launch": kern_flop[kind],
+                "avg_ms": avg_ms(kind)}
+
+    dominant = max(("fwd", "bwd_dkdv", "bwd_dq"), key=avg_ms)
+    main_roof = roof(dominant)
+    main_roof["traffic"] = _traffic_from_profile(dominant, spec["name"])
+    # HBM-bound passes: preprocess reads O and dO and writes D; the reduction
+    # reads the fp32 partial slots and writes the split tiles' dK and dV
+    pre_bytes = n * hq * d * 2 * esize + n * hq * 4
+    red_bytes = 2 * pstats["bwd_slots"] * 128 * d * 4 + 2 * pstats["bwd_split_tiles"] * 128 * d * esize
     workload = spec["name"]
     result = {
         "metric": METRIC,
@@ -224,25 +247,13 @@ def main() -> int:
         "tflops": tflops,
         "frac_of_peak": tflops / peak,
         "dense_per_path_flop_ratio": st["dense_ratio"],
-        "kernels_ms": {kk: avg_ms(kk) for kk in kt},
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "tree_attn_bwd_kernel (backward main)",
-            "achieved": bwd_achieved,
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": bwd_achieved / peak,
-            "traffic": _traffic_from_profile(workload),
-            "flop_per_launch": bwd_flop,
-        },
-        "roofline_fwd": {
-            "bound": "mfma", "kernel": "tree_attn_fwd_kernel", "achieved": fwd_achieved,
-            "peak": peak, "unit": "TFLOP/s", "frac": fwd_achieved / peak,
-            "flop_per_launch": fwd_flop,
-        },
+        "kernels_ms": {kk: avg_ms(kk) for kk in kt if kt[kk]["launches"]},
+        "roofline": main_roof,
+        "roofline_kernels": {k: roof(k) for k in ("fwd", "bwd_dkdv", "bwd_dq")},
         "hbm_passes_GBps": {
             "bwd_pre": pre_bytes / (avg_ms("bwd_pre") * 1e-3) / 1e9,
-            "bwd_post": post_bytes / (avg_ms("bwd_post") * 1e-3) / 1e9,
+            "bwd_reduce": (red_bytes / (avg_ms("bwd_reduce") * 1e-3) / 1e9
+                           if kt["bwd_reduce"]["launches"] else None),
             "peak": PEAK_HBM_GBS,
         },
         "plan": {k: pstats[k] for k in ("fwd_tiles", "bwd_items", "bwd_split_tiles", "bwd_slots")},

@@ -118,10 +118,10 @@ void tree_attn_plan_destroy(tree_attn_plan_t plan);
 
 /*
  * tree_attn_workspace_size -- bytes of device workspace fwd and bwd need.
- * The backward workspace holds an fp32 dQ accumulator [N, Hq, D], the fp32
- * row terms D_t = dO_t . O_t [Hq, N] and fp32 partial dK/dV slots of key
- * tiles whose descendant work was split for load balance.  The forward pass
- * currently needs none (fwd_bytes = 0).  Either pointer may be null.
+ * The backward workspace holds the fp32 row terms D_t = dO_t . O_t [Hq, N]
+ * and fp32 partial dK/dV slots of key tiles whose descendant work was split
+ * for load balance.  The forward pass needs none (fwd_bytes = 0).  Either
+ * pointer may be null.
  */
 tree_attn_status_t tree_attn_workspace_size(tree_attn_plan_t plan, size_t* fwd_bytes,
                                             size_t* bwd_bytes);
@@ -148,9 +148,8 @@ tree_attn_status_t tree_attn_fwd(tree_attn_plan_t plan, const void* q, const voi
  * [N,Hkv,D] receive the exact gradients with respect to the unique q, k, v:
  * dK and dV of a shared token are summed over every branch below it and over
  * the G query heads of its group.  Outputs are overwritten, not accumulated.
- * ws must hold at least bwd_bytes.  dK and dV are computed without atomics
- * and are bitwise reproducible; dQ is accumulated with fp32 atomics and may
- * differ in the last bits between runs.
+ * ws must hold at least bwd_bytes (256-byte aligned).  No atomics are used:
+ * dQ, dK and dV are bitwise reproducible from run to run.
  */
 tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const void* k,
                                  const void* v, const void* o, const float* lse,
@@ -198,13 +197,13 @@ tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_til
  * host synchronisation).  tree_attn_timing_read waits for the recorded
  * events, and returns per kernel kind the number of launches and their summed
  * duration in milliseconds since the last reset (reset != 0 clears them).
- * Kinds: 0 forward, 1 backward preprocess, 2 backward main, 3 backward
- * reduction + dQ conversion.  Timing is process-wide and not meant for
- * concurrent callers.
+ * Kinds: 0 forward, 1 backward preprocess, 2 backward dK/dV, 3 backward
+ * partial-slot reduction, 4 backward dQ; 5..7 unused.  Timing is
+ * process-wide and not meant for concurrent callers.
  */
 typedef struct {
-  int64_t launches[4];
-  double total_ms[4];
+  int64_t launches[8];
+  double total_ms[8];
 } tree_attn_timing_t;
 
 tree_attn_status_t tree_attn_timing_enable(int enable);

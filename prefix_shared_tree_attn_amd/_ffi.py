@@ -31,10 +31,10 @@ class PlanStats(ctypes.Structure):
 
 
 class Timing(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int64 * 4), ("total_ms", ctypes.c_double * 4)]
+    _fields_ = [("launches", ctypes.c_int64 * 8), ("total_ms", ctypes.c_double * 8)]
 
 
-TIMING_KINDS = ("fwd", "bwd_pre", "bwd_main", "bwd_post")
+TIMING_KINDS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_reduce", "bwd_dq")
 
 
 class TreeAttnError(RuntimeError):

@@ -48,18 +48,16 @@ tree_attn_status_t report_hip(hipError_t e, const char* what) {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct BwdLayout {
-  size_t dq_acc = 0, dvec = 0, dk_slots = 0, dv_slots = 0, total = 0;
+  size_t dvec = 0, dk_slots = 0, dv_slots = 0, total = 0;
 };
 
 BwdLayout bwd_layout(const HostPlan& p) {
   BwdLayout l;
-  const size_t dq = static_cast<size_t>(p.num_tokens) * p.hq * p.head_dim * 4;
   const size_t dv = static_cast<size_t>(p.num_tokens) * p.hq * 4;
   const size_t slot =
       static_cast<size_t>(p.bwd_slots) * tree_attn::kBwdKeys * p.head_dim * 4;
-  l.dq_acc = 0;
-  l.dvec = align256(dq);
-  l.dk_slots = l.dvec + align256(dv);
+  l.dvec = 0;
+  l.dk_slots = align256(dv);
   l.dv_slots = l.dk_slots + align256(slot);
   l.total = l.dv_slots + align256(slot);
   if (p.num_tokens == 0) l.total = 0;
@@ -91,6 +89,7 @@ size_t bytes_of(const V& v) {
 }
 
 // Optional per-kernel timing: HIP events around each launch, read later.
+constexpr int kTimingKinds = 8;
 struct Timing {
   std::mutex mu;
   bool enabled = false;
@@ -100,8 +99,8 @@ struct Timing {
     hipEvent_t start, stop;
   };
   std::vector<Rec> recs;
-  int64_t launches[4] = {0, 0, 0, 0};
-  double total_ms[4] = {0, 0, 0, 0};
+  int64_t launches[kTimingKinds] = {};
+  double total_ms[kTimingKinds] = {};
 };
 
 Timing& timing() {
@@ -311,16 +310,19 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.dq_acc = reinterpret_cast<float*>(w + l.dq_acc);
   a.dvec = reinterpret_cast<float*>(w + l.dvec);
   a.dk_slots = reinterpret_cast<float*>(w + l.dk_slots);
   a.dv_slots = reinterpret_cast<float*>(w + l.dv_slots);
   a.items = plan->d_bwd_items;
   a.entries = plan->d_bwd_entries;
   a.reduce = plan->d_bwd_reduce;
+  a.tiles = plan->d_fwd_tiles;
+  a.ranges = plan->d_fwd_ranges;
   a.n_tokens = hp.num_tokens;
   a.n_items = static_cast<int64_t>(hp.bwd_items.size());
   a.n_reduce = static_cast<int64_t>(hp.bwd_reduce.size());
+  a.n_groups = hp.fwd_groups;
+  a.dq_blocks = hp.fwd_blocks;
   a.hq = static_cast<int>(hp.hq);
   a.hkv = static_cast<int>(hp.hkv);
   a.gsize = static_cast<int>(hp.hq / hp.hkv);
@@ -329,10 +331,12 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
   const int hd = static_cast<int>(hp.head_dim);
   hipError_t e = timed(1, stream, [&] { return tree_attn::launch_bwd_pre(a, hp.dtype, hd, stream); });
   if (e != hipSuccess) return report_hip(e, "backward preprocess launch");
-  e = timed(2, stream, [&] { return tree_attn::launch_bwd_main(a, hp.dtype, hd, stream); });
-  if (e != hipSuccess) return report_hip(e, "backward launch");
+  e = timed(2, stream, [&] { return tree_attn::launch_bwd_dkdv(a, hp.dtype, hd, stream); });
+  if (e != hipSuccess) return report_hip(e, "backward dK/dV launch");
   e = timed(3, stream, [&] { return tree_attn::launch_bwd_post(a, hp.dtype, hd, stream); });
   if (e != hipSuccess) return report_hip(e, "backward reduction launch");
+  e = timed(4, stream, [&] { return tree_attn::launch_bwd_dq(a, hp.dtype, hd, stream); });
+  if (e != hipSuccess) return report_hip(e, "backward dQ launch");
   return TREE_ATTN_OK;
 }
 
@@ -395,13 +399,13 @@ tree_attn_status_t tree_attn_timing_read(tree_attn_timing_t* out, int reset) {
   }
   t.recs.clear();
   if (out) {
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kTimingKinds; ++i) {
       out->launches[i] = t.launches[i];
       out->total_ms[i] = t.total_ms[i];
     }
   }
   if (reset) {
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kTimingKinds; ++i) {
       t.launches[i] = 0;
       t.total_ms[i] = 0;
     }

@@ -272,6 +272,13 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// Every kernel variant is instantiated explicitly so that the host pass
+// always emits its launch stub.
+template __global__ void tree_attn_fwd_kernel<__bf16, 128>(FwdArgs);
+template __global__ void tree_attn_fwd_kernel<__bf16, 64>(FwdArgs);
+template __global__ void tree_attn_fwd_kernel<float, 128>(FwdArgs);
+template __global__ void tree_attn_fwd_kernel<float, 64>(FwdArgs);
+
 template <typename T, int D>
 static hipError_t fwd_t(const FwdArgs& a, int64_t n_blocks, hipStream_t s) {
   constexpr int bytes = FwdCfg<T, D>::BYTES;

@@ -32,16 +32,19 @@ struct BwdArgs {
   void* dk;
   void* dv;
   void* dq;
-  float* dq_acc;     // [N, Hq, D] fp32
   float* dvec;       // [Hq, N] fp32: sum_d dO * O
   float* dk_slots;   // [slots, kBwdKeys, D] fp32
   float* dv_slots;   // [slots, kBwdKeys, D] fp32
-  const I8* items;   // (k0, k1, g, entry_begin, entry_end, slot, 0, 0)
-  const I4* entries; // (h, q0, q1, causal)
+  const I8* items;   // dK/dV: (k0, k1, g, entry_begin, entry_end, slot, 0, 0)
+  const I4* entries; // dK/dV: (h, q0, q1, causal)
   const I8* reduce;  // (k0, k1, g, slot_begin, n_slots, 0, 0, 0)
+  const I4* tiles;   // dQ: forward query tiles (q0, q1, range_begin, range_end)
+  const I4* ranges;  // dQ: forward key ranges (k0, k1, causal, 0)
   int64_t n_tokens;
   int64_t n_items;
   int64_t n_reduce;
+  int64_t n_groups;  // dQ: tiles * hkv
+  int64_t dq_blocks; // dQ launch size
   int hq, hkv, gsize;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
@@ -51,7 +54,8 @@ struct BwdArgs {
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, int64_t n_blocks,
                       hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
-hipError_t launch_bwd_main(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_post(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 
 }  // namespace tree_attn

@@ -114,9 +114,8 @@ def test_repeat_runs_are_deterministic_where_promised():
         dq, dk, dv = ta.bwd(p, dev["q"], dev["k"], dev["v"], o, lse, dev["do"], 0.088)
         torch.cuda.synchronize()
         runs.append([a.clone() for a in (o, lse, dq, dk, dv)])
-    for i in (0, 1, 3, 4):  # o, lse, dk, dv bitwise
+    for i in range(5):  # o, lse, dq, dk, dv: no atomics, bitwise reproducible
         assert torch.equal(runs[0][i], runs[1][i]), i
-    assert rel_l2(runs[0][2].float().cpu().numpy(), runs[1][2].float().cpu().numpy()) < 1e-2
 
 
 # ------------------------------------------------------------------ full size
