@@ -177,10 +177,13 @@ def main() -> int:
     log(f"timed {args.steps} steps: {wall:.3f} s")
 
     if args.copy_probe_mib > 0:
+        # a plain elementwise kernel of known traffic, to calibrate HBM byte
+        # counters: reads nb bytes and writes nb bytes
         nb = args.copy_probe_mib << 20
-        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        a = torch.ones(nb // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
+        torch.cuda.synchronize()
+        torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
         log(f"copy probe: {nb} bytes read + {nb} bytes written")
 
