@@ -118,8 +118,9 @@ void tree_attn_plan_destroy(tree_attn_plan_t plan);
 
 /*
  * tree_attn_workspace_size -- bytes of device workspace fwd and bwd need.
- * The backward workspace holds the fp32 row terms D_t = dO_t . O_t [Hq, N]
- * and fp32 partial dK/dV slots of key tiles whose descendant work was split
+ * The backward workspace holds two fp32 row-term arrays [Hq, N] (-D_t with
+ * D_t = dO_t . O_t, and -LSE_t * log2 e), each padded to 256 bytes, and fp32
+ * partial dK/dV slots of key tiles whose descendant work was split
  * for load balance.  The forward pass needs none (fwd_bytes = 0).  Either
  * pointer may be null.
  */

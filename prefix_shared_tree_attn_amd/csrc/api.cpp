@@ -48,7 +48,7 @@ tree_attn_status_t report_hip(hipError_t e, const char* what) {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct BwdLayout {
-  size_t dvec = 0, dk_slots = 0, dv_slots = 0, total = 0;
+  size_t neg_d = 0, neg_lse2 = 0, dk_slots = 0, dv_slots = 0, total = 0;
 };
 
 BwdLayout bwd_layout(const HostPlan& p) {
@@ -56,8 +56,9 @@ BwdLayout bwd_layout(const HostPlan& p) {
   const size_t dv = static_cast<size_t>(p.num_tokens) * p.hq * 4;
   const size_t slot =
       static_cast<size_t>(p.bwd_slots) * tree_attn::kBwdKeys * p.head_dim * 4;
-  l.dvec = 0;
-  l.dk_slots = align256(dv);
+  l.neg_d = 0;
+  l.neg_lse2 = align256(dv);
+  l.dk_slots = l.neg_lse2 + align256(dv);
   l.dv_slots = l.dk_slots + align256(slot);
   l.total = l.dv_slots + align256(slot);
   if (p.num_tokens == 0) l.total = 0;
@@ -310,7 +311,8 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.dvec = reinterpret_cast<float*>(w + l.dvec);
+  a.neg_d = reinterpret_cast<float*>(w + l.neg_d);
+  a.neg_lse2 = reinterpret_cast<float*>(w + l.neg_lse2);
   a.dk_slots = reinterpret_cast<float*>(w + l.dk_slots);
   a.dv_slots = reinterpret_cast<float*>(w + l.dv_slots);
   a.items = plan->d_bwd_items;

@@ -44,7 +44,7 @@ struct DkdvCfg {
   static constexpr int KC = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int Q_PLANE = QB * D * 2;
-  static constexpr int LD_BYTES = QB * 8;  // LSE * log2(e), then D
+  static constexpr int LD_BYTES = QB * 8;  // -LSE * log2(e), then -D
   static constexpr int Q_OFF = 0;
   static constexpr int DO_OFF = Q_OFF + 2 * NP * Q_PLANE;
   static constexpr int LD_OFF = DO_OFF + 2 * NP * Q_PLANE;
@@ -103,7 +103,9 @@ __global__ __launch_bounds__(256) void tree_attn_bwd_pre_kernel(BwdArgs a) {
   for (int w = TPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
   if (row < rows && part == 0) {
     const int64_t t = row / a.hq, h = row % a.hq;
-    a.dvec[h * a.n_tokens + t] = acc;
+    const int64_t o = h * a.n_tokens + t;
+    a.neg_d[o] = -acc;
+    a.neg_lse2[o] = -a.lse[o] * kLog2e;
   }
 }
 
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     if (tid < 2 * QB) {
       const int r = tid % QB;
       const int64_t row = r0 + r < last ? r0 + r : last;
-      const float* src = tid < QB ? a.lse : a.dvec;
+      const float* src = tid < QB ? a.neg_lse2 : a.neg_d;
       ld_reg = src[static_cast<int64_t>(b.h) * a.n_tokens + row];
     }
   };
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
         }
       }
     }
-    if (tid < 2 * QB) ld_tile(buf)[tid] = tid < QB ? ld_reg * kLog2e : ld_reg;
+    if (tid < 2 * QB) ld_tile(buf)[tid] = ld_reg;
   };
 
   // this wave's K / V operands (B operands of S = Q K^T and dP = dO V^T)
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
       const int qs0 = cur.qb + 32 * sb;  // first row of the sub-block
       // wave-uniform: no row of the sub-block sees any key of this wave
       if (qs0 >= cur.qe || wk0 >= k1 || (cur.causal && wk0 > qs0 + 31)) continue;
-      // LSE * log2(e) and D of the 16 rows this lane holds: rows
+      // -LSE * log2(e) and -D of the 16 rows this lane holds: rows
       // 32 sb + 8 half + (0..7) and 32 sb + 16 + 8 half + (0..7)
       f32x4 lse4[4], dv4[4];
 #pragma unroll
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         p[v] = __builtin_amdgcn_exp2f(
-            __builtin_fmaf(sacc[v], a.scale_log2, -lse4[v >> 2][v & 3]));
+            __builtin_fmaf(sacc[v], a.scale_log2, lse4[v >> 2][v & 3]));
       if (need_mask) {
         const int qlim = cur.qe - cur.qb;                       // local rows < qlim
         const int kq = cur.causal ? key - cur.qb : -(1 << 30);  // local rows >= kq
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) ds[v] = p[v] * (pacc[v] - dv4[v >> 2][v & 3]);
+      for (int v = 0; v < 16; ++v) ds[v] = p[v] * (pacc[v] + dv4[v >> 2][v & 3]);
       const Frag<SPLIT> pf0 = pack8<SPLIT>(p), pf1 = pack8<SPLIT>(p + 8);
       const Frag<SPLIT> sf0 = pack8<SPLIT>(ds), sf1 = pack8<SPLIT>(ds + 8);
 
@@ -357,6 +359,390 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// 2b. dK / dV for bf16 inputs, software-pipelined over 32-row query steps.
+//
+// The work of step j splits into three independent parts: A(j), the products
+// S = Q K^T and dP = dO V^T; B(j), the element-wise P = 2^(c S - LSE log2 e)
+// and dS = P (dP - D); and C(j), the updates dV += P^T dO and dK += dS^T Q.
+// Iteration j issues C(j-1) and A(j+1) on the matrix cores while the vector
+// ALUs run B(j), so the element-wise work of a wave hides under its own
+// MFMAs.  Q, dO and the row terms of step j + 2 are loaded into registers
+// during iteration j and written to a ring of four LDS buffers before the
+// next barrier (one barrier per step).  Loads go through registers rather
+// than straight to LDS: the compiler cannot tell a direct-to-LDS load from
+// the transposed LDS reads and would drain every prefetch before them.
+//
+// No branch masks anything inside the loop:
+//  * rows past a query range read as zeros (each buffer resource ends at the
+//    range), so Q = dO = 0 and -LSE log2 e = -D = 0 there; P = 1 but
+//    dP - D = 0 and dO = 0, so neither dK nor dV changes;
+//  * keys past the tile only reach rows of dK / dV that are never stored;
+//  * under the causal mask S starts from -inf where key > row, so P = 0.
+template <int D>
+struct DkdvPipeCfg {
+  static constexpr int KC = D / 16, DB = D / 32;
+  static constexpr int ROWS = 32;                // query rows per step
+  static constexpr int NB = 4;                   // LDS ring buffers
+  static constexpr int TILE = ROWS * D * 2;      // one bf16 Q or dO tile
+  static constexpr int Q_OFF = 0, DO_OFF = TILE;
+  static constexpr int NL_OFF = 2 * TILE;        // -LSE log2 e (64 floats, 32 used)
+  static constexpr int ND_OFF = 2 * TILE + 256;  // -D (64 floats, 32 used)
+  static constexpr int BUF = 2 * TILE + 512;
+  static constexpr int BYTES = NB * BUF;
+  static constexpr int PER = ROWS * (D / 8) / 256;  // 16-byte chunks per thread and tile
+};
+
+namespace {
+
+// A 32-row query step of a backward item: rows [r0, min(r0 + 32, qe)) of
+// query head h, taken from entry e.  e == entry_end marks "no step".
+struct Step {
+  int e, r0, qe, h, causal;
+};
+
+// Plan arrays are read-only while a kernel runs: reading them through the
+// constant address space gives uniform scalar loads.
+#define CONST_PTR(T) __attribute__((address_space(4))) const T*
+
+__device__ __forceinline__ void step_at(Step& s, int e, int ee, const I4* entries) {
+  s.e = e;
+  if (e < ee) {
+    CONST_PTR(int) en = (CONST_PTR(int))(entries) + 4 * static_cast<int64_t>(e);
+    s.h = en[0];
+    s.r0 = en[1];
+    s.qe = en[2];
+    s.causal = en[3];
+  } else {
+    s.h = 0;
+    s.r0 = 0;
+    s.qe = 0;
+    s.causal = 0;
+  }
+}
+
+__device__ __forceinline__ void step_next(Step& s, int ee, const I4* entries) {
+  s.r0 += 32;
+  if (s.r0 >= s.qe) step_at(s, s.e < ee ? s.e + 1 : ee, ee, entries);
+}
+
+// P and dS of one step packed as A operands of the dV / dK products: p[c] /
+// s[c] hold this lane's key against rows 16 c + 8 (lane / 32) + (0..7).
+struct PdsPack {
+  bf16x8 p[2], s[2];
+};
+
+// Empty asm use: the value must be computed before this point, which keeps
+// the compiler from sinking element-wise work out of its MFMA slot.
+__device__ __forceinline__ void keep(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void keep(const bf16x8& x) { asm volatile("" ::"v"(x)); }
+
+__device__ __forceinline__ rsrc_t make_rsrc_n(const void* base, int64_t bytes) {
+  const uint32_t r =
+      bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(r), kRsrcFlags);
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) {
+  using C = DkdvPipeCfg<D>;
+  constexpr int KC = C::KC, DB = C::DB, NB = C::NB, BUF = C::BUF;
+  using QT = Tile<D, 32>;
+  extern __shared__ __attribute__((aligned(16))) char smem_dyn[];
+  LDS_PTR(char) lds = (LDS_PTR(char))(smem_dyn);
+
+  const I8 it = a.items[blockIdx.x];
+  const int k0 = it.v[0], k1 = it.v[1], g = it.v[2], eb = it.v[3], ee = it.v[4];
+  const int slot = it.v[5];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int64_t last = a.n_tokens - 1;
+  const int64_t qs = static_cast<int64_t>(a.hq) * D;
+  const int64_t ks = static_cast<int64_t>(a.hkv) * D;
+  const __bf16* Qall = static_cast<const __bf16*>(a.q);
+  const __bf16* dOall = static_cast<const __bf16*>(a.dout);
+  const int wk0 = k0 + 32 * wave;  // first key of this wave
+  const int key = wk0 + l32;       // this lane's key (column of S)
+
+  // Per-lane LDS offsets; every other term of an operand address is a
+  // compile-time immediate (see Tile): row operands of chunk pair kc / 2,
+  // transposed operands of rows (16 qc ..) and columns (32 db ..).
+  const int qrow_a = swap23(l32);
+  int ro[2];
+  ro[0] = QT::chunk_off(qrow_a, half);
+  ro[1] = QT::chunk_off(qrow_a, 2 + half);
+  int tro[2];
+  {
+    const int grp = lane >> 4, L = lane & 15;
+    const int r = 8 * (grp >> 1) + (L >> 2);
+    const int c = 16 * (grp & 1) + 4 * (L & 3);
+    tro[0] = QT::elem_off(r, c);
+    tro[1] = QT::elem_off(r + 4, c);
+  }
+  const int ldo = 32 * half;  // byte offset of row 8 * half in a row-term array
+
+  // The first iteration's dK / dV products read the last ring buffer with
+  // zero P / dS; clear it so that stale LDS bits cannot form NaNs.
+  {
+    const i32x4 z = {0, 0, 0, 0};
+    for (int i = tid; i < BUF / 16; i += 256) lds_write16(lds + (NB - 1) * BUF, 16 * i, z);
+  }
+
+  // Loads of one step into registers: C::PER 16-byte chunks of Q and of dO
+  // per thread, and for waves 0 / 1 one -LSE log2 e / -D row term per lane.
+  // Resources end at the step's last row, so rows past a query range, and
+  // steps past the end (empty resources), load zeros.
+  constexpr int PER = C::PER;
+  int voff[PER], loff[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + 256 * i, r = c / (D / 8), cc = c % (D / 8);
+    voff[i] = r * static_cast<int>(qs * 2) + cc * 16;
+    loff[i] = QT::chunk_off(r, cc);
+  }
+  i32x4 qreg[PER], dreg[PER];
+  int treg = 0;
+  const float* rterm = wave == 1 ? a.neg_d : a.neg_lse2;
+  const int rterm_off = wave == 1 ? C::ND_OFF : C::NL_OFF;
+  auto issue = [&](const Step& s) {
+    const bool valid = s.e < ee;
+    const int64_t rows = valid ? (s.qe - s.r0 < 32 ? s.qe - s.r0 : 32) : 0;
+    const int64_t base = static_cast<int64_t>(s.r0) * qs + static_cast<int64_t>(s.h) * D;
+    const rsrc_t rq = make_rsrc_n(Qall + base, rows * qs * 2);
+    const rsrc_t rd = make_rsrc_n(dOall + base, rows * qs * 2);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      qreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff[i], 0, 0);
+      dreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rd, voff[i], 0, 0);
+    }
+    if (wave < 2) {
+      const rsrc_t rr =
+          make_rsrc_n(rterm + static_cast<int64_t>(s.h) * a.n_tokens + s.r0, rows * 4);
+      treg = __builtin_amdgcn_raw_buffer_load_b32(rr, 4 * lane, 0, 0);
+    }
+  };
+  auto commit = [&](int buf) {
+    LDS_PTR(char) b = lds + buf * BUF;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      lds_write16(b + C::Q_OFF, loff[i], qreg[i]);
+      lds_write16(b + C::DO_OFF, loff[i], dreg[i]);
+    }
+    if (wave < 2) *reinterpret_cast<LDS_PTR(int)>(b + rterm_off + 4 * lane) = treg;
+  };
+
+  // this wave's K / V operands (B operands of S = Q K^T and dP = dO V^T)
+  bf16x8 kf[KC], vf[KC];
+  {
+    const int64_t r = key < last ? key : last;
+    const __bf16* kp = static_cast<const __bf16*>(a.k) + r * ks + static_cast<int64_t>(g) * D;
+    const __bf16* vp = static_cast<const __bf16*>(a.v) + r * ks + static_cast<int64_t>(g) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      kf[kc] = *reinterpret_cast<const bf16x8*>(kp + 16 * kc + 8 * half);
+      vf[kc] = *reinterpret_cast<const bf16x8*>(vp + 16 * kc + 8 * half);
+    }
+  }
+  f32x16 dk_acc[DB], dv_acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      dk_acc[db][v] = 0.f;
+      dv_acc[db][v] = 0.f;
+    }
+
+  auto nextb = [](int b) { return b + 1 == NB ? 0 : b + 1; };
+
+  // MFMA slots of one iteration: first the dV / dK updates of the previous
+  // step (slot i < NC: column block i / 4, row chunk (i / 2) % 2, dV for even
+  // i and dK for odd i), then S and dP of the next step (slot NC + 2 kc for S,
+  // NC + 2 kc + 1 for dP).
+  constexpr int NC = 4 * DB, NS = NC + 2 * KC;
+  constexpr int LA = 3;  // operands are read this many slots ahead
+  auto fetch = [&](int i, LDS_PTR(char) bprev, LDS_PTR(char) bnext) -> bf16x8 {
+    if (i < NC) {
+      const int imm = (i >> 2) * QT::SUB + ((i >> 1) & 1) * 1024;
+      LDS_PTR(char) t = bprev + ((i & 1) ? C::Q_OFF : C::DO_OFF);
+      const bf16x4 lo = lds_read_tr(t, tro[0] + imm);
+      const bf16x4 hi = lds_read_tr(t, tro[1] + imm);
+      bf16x8 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r[e] = lo[e];
+        r[e + 4] = hi[e];
+      }
+      return r;
+    }
+    const int kc = (i - NC) >> 1;
+    LDS_PTR(char) t = bnext + (((i - NC) & 1) ? C::DO_OFF : C::Q_OFF);
+    return lds_read16(t, ro[kc & 1] + (kc >> 1) * QT::SUB);
+  };
+  // S and dP of the step whose element-wise part runs next; P / dS of the
+  // step whose updates run next
+  f32x16 sacc, pacc;
+  PdsPack pk;
+  const f32x16 zero16 = {};
+  auto mfma_slot = [&](int i, const bf16x8& op) {
+    if (i < NC) {
+      const int db = i >> 2, qc = (i >> 1) & 1;
+      if (i & 1) dk_acc[db] = mfma32(pk.s[qc], op, dk_acc[db]);
+      else dv_acc[db] = mfma32(pk.p[qc], op, dv_acc[db]);
+    } else {
+      const int kc = (i - NC) >> 1;
+      if ((i - NC) & 1) pacc = mfma32(op, vf[kc], kc == 0 ? zero16 : pacc);
+      else sacc = mfma32(op, kf[kc], kc == 0 ? zero16 : sacc);
+    }
+  };
+
+  // One pipelined iteration j: C(j-1) then A(j+1) on the matrix cores, B(j)
+  // on the vector ALUs beside them.  During the C slots each element's S and
+  // dP leave the accumulators (x = c s - LSE log2 e, y = dP - D), so the A
+  // slots may overwrite them; during the A slots P = 2^x, dS = P y and the
+  // bf16 packs are formed, after the last C slot has read the old packs.
+  // The fences keep this order.  Under the causal mask (rare steps) x is set
+  // to -inf where key > row between the halves.
+  auto iteration = [&](int bp, int bc, int bn, bool masked, int delta) {
+    LDS_PTR(char) bprev = lds + bp * BUF;
+    LDS_PTR(char) bcur = lds + bc * BUF;
+    LDS_PTR(char) bnext = lds + bn * BUF;
+    f32x4 nl[4], nd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int off = ldo + 64 * (i >> 1) + 16 * (i & 1);
+      nl[i] = *reinterpret_cast<const LDS_PTR(f32x4)>(bcur + C::NL_OFF + off);
+      nd[i] = *reinterpret_cast<const LDS_PTR(f32x4)>(bcur + C::ND_OFF + off);
+    }
+    bf16x8 op[NS];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) op[i] = fetch(i, bprev, bnext);
+    float x[16], y[16];
+    constexpr int EC = 16 / NC;       // elements per C slot
+    constexpr int EA = 16 / (NS - NC);  // elements per A slot
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      op[i + LA] = fetch(i + LA, bprev, bnext);
+      mfma_slot(i, op[i]);
+#pragma unroll
+      for (int e = EC * i; e < EC * (i + 1); ++e) {
+        x[e] = __builtin_fmaf(sacc[e], a.scale_log2, nl[e >> 2][e & 3]);
+        y[e] = pacc[e] + nd[e >> 2][e & 3];
+        keep(x[e]);
+        keep(y[e]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (masked) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 16 * (v >> 3) + 8 * half + (v & 7);
+        x[v] = l32 - r > delta ? -__builtin_inff() : x[v];
+      }
+    }
+#pragma unroll
+    for (int i = NC; i < NS; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + LA < NS) op[i + LA] = fetch(i + LA, bprev, bnext);
+      mfma_slot(i, op[i]);
+#pragma unroll
+      for (int e = EA * (i - NC); e < EA * (i - NC + 1); ++e) {
+        const float pe = __builtin_amdgcn_exp2f(x[e]);
+        pk.p[e >> 3][e & 7] = to_bf16(pe);
+        pk.s[e >> 3][e & 7] = to_bf16(pe * y[e]);
+      }
+      if ((EA * (i - NC + 1)) % 8 == 0) {
+        const int c = (EA * (i - NC + 1)) / 8 - 1;
+        keep(pk.p[c]);
+        keep(pk.s[c]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  Step ld, cur, nx;
+  step_at(ld, eb, ee, a.entries);
+  cur = ld;  // step j
+  nx = cur;
+  step_next(nx, ee, a.entries);  // step j + 1
+  issue(ld);
+  step_next(ld, ee, a.entries);
+  commit(0);
+  issue(ld);  // step 1 (zeros if there is none)
+  step_next(ld, ee, a.entries);
+  int bp = NB - 1, bc = 0, bn = 1;
+  __syncthreads();
+  // A of step 0; the first C(-1) runs on zero packs and a cleared buffer
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pk.p[c][e] = to_bf16(0.f);
+      pk.s[c][e] = to_bf16(0.f);
+    }
+  {
+    LDS_PTR(char) b0 = lds + bc * BUF;
+#pragma unroll
+    for (int i = NC; i < NS; ++i) mfma_slot(i, fetch(i, b0, b0));
+  }
+
+  while (true) {
+    const bool more = nx.e < ee;
+    // step j + 1 into its buffer: the waves still in iteration j - 1 use
+    // buffers j - 2 .. j only
+    commit(bn);
+    __syncthreads();
+    issue(ld);  // step j + 2
+    step_next(ld, ee, a.entries);
+    const int delta = cur.r0 - wk0;
+    const bool masked = cur.causal && delta < 32;
+    cur = nx;
+    step_next(nx, ee, a.entries);
+    const int b0 = bp, b1 = bc, b2 = bn;
+    bp = bc;
+    bc = bn;
+    bn = nextb(bn);
+    iteration(b0, b1, b2, masked, delta);
+    if (!more) break;
+  }
+  // C of the last step (its buffer is bp now)
+  {
+    LDS_PTR(char) bl = lds + bp * BUF;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) mfma_slot(i, fetch(i, bl, bl));
+  }
+
+  // dK, dV of this wave's keys: lane holds column d, key rows in registers
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int d = 32 * db + l32;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int kl = 32 * wave + 8 * (v >> 2) + 4 * half + (v & 3);
+      const int kr = k0 + kl;
+      if (kr >= k1) continue;
+      const float dkv = a.scale * dk_acc[db][v];
+      const float dvv = dv_acc[db][v];
+      if (slot < 0) {
+        __bf16* dk = static_cast<__bf16*>(a.dk) + static_cast<int64_t>(kr) * ks +
+                     static_cast<int64_t>(g) * D;
+        __bf16* dv = static_cast<__bf16*>(a.dv) + static_cast<int64_t>(kr) * ks +
+                     static_cast<int64_t>(g) * D;
+        dk[d] = to_bf16(dkv);
+        dv[d] = to_bf16(dvv);
+      } else {
+        const int64_t so = (static_cast<int64_t>(slot) * kBwdKeys + kl) * D + d;
+        a.dk_slots[so] = dkv;
+        a.dv_slots[so] = dvv;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 // 3. dQ: query-tile centric, like the forward pass
 template <typename T, int D>
 struct DqCfg {
@@ -404,7 +790,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
 
   // Q and dO of this lane's row (B operands of S^T = K Q^T and dP^T = V dO^T)
   Frag<SPLIT> qf[KC], df[KC];
-  float lse2, dvq;
+  float nl2, ndq;  // -LSE * log2(e) and -D of this lane's row
   {
     const int64_t r = qrow < last ? qrow : last;
     const T* qp = static_cast<const T*>(a.q) + r * qs + static_cast<int64_t>(h) * D + 8 * half;
@@ -414,8 +800,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
       qf[kc] = load_frag8(qp + 16 * kc);
       df[kc] = load_frag8(dp + 16 * kc);
     }
-    lse2 = a.lse[static_cast<int64_t>(h) * a.n_tokens + r] * kLog2e;
-    dvq = a.dvec[static_cast<int64_t>(h) * a.n_tokens + r];
+    nl2 = a.neg_lse2[static_cast<int64_t>(h) * a.n_tokens + r];
+    ndq = a.neg_d[static_cast<int64_t>(h) * a.n_tokens + r];
   }
 
   constexpr int SPLIT_PER = SPLIT ? kFwdKeys * D / 4 / 256 : 1;
@@ -530,12 +916,12 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], a.scale_log2, -lse2));
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], a.scale_log2, nl2));
           if (need_mask) {
             const int kl = 32 * kb + 16 * (v >> 3) + 8 * half + (v & 7);
             p = kl < klim ? p : 0.f;
           }
-          sacc[kb][v] = p * (pacc[kb][v] - dvq);
+          sacc[kb][v] = p * (pacc[kb][v] + ndq);
         }
       // dQ^T += K^T dS^T over four 16-key chunks (K read transposed)
       Frag<SPLIT> sf[4];
@@ -627,8 +1013,9 @@ static hipError_t pre_t(const BwdArgs& a, hipStream_t s) {
 template <typename T, int D>
 static hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
-  constexpr int bytes = DkdvCfg<T, D>::BYTES;
-  auto kern = tree_attn_dkdv_kernel<T, D>;
+  constexpr bool pipe = !IsSplit<T>::value;
+  constexpr int bytes = pipe ? DkdvPipeCfg<D>::BYTES : DkdvCfg<T, D>::BYTES;
+  auto kern = pipe ? tree_attn_dkdv_pipe_kernel<D> : tree_attn_dkdv_kernel<T, D>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
@@ -666,6 +1053,8 @@ static hipError_t post_t(const BwdArgs& a, hipStream_t s) {
   template __global__ void tree_attn_dkdv_kernel<T, D>(BwdArgs);            \
   template __global__ void tree_attn_dq_kernel<T, D>(BwdArgs);              \
   template __global__ void tree_attn_bwd_reduce_kernel<T, D>(BwdArgs);
+template __global__ void tree_attn_dkdv_pipe_kernel<128>(BwdArgs);
+template __global__ void tree_attn_dkdv_pipe_kernel<64>(BwdArgs);
 TREE_ATTN_INSTANTIATE(__bf16, 128)
 TREE_ATTN_INSTANTIATE(__bf16, 64)
 TREE_ATTN_INSTANTIATE(float, 128)

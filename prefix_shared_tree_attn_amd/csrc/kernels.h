@@ -32,7 +32,8 @@ struct BwdArgs {
   void* dk;
   void* dv;
   void* dq;
-  float* dvec;       // [Hq, N] fp32: sum_d dO * O
+  float* neg_d;      // [Hq, N] fp32: -(sum_d dO * O), written by the preprocess
+  float* neg_lse2;   // [Hq, N] fp32: -LSE * log2(e), written by the preprocess
   float* dk_slots;   // [slots, kBwdKeys, D] fp32
   float* dv_slots;   // [slots, kBwdKeys, D] fp32
   const I8* items;   // dK/dV: (k0, k1, g, entry_begin, entry_end, slot, 0, 0)

@@ -161,7 +161,7 @@ def test_workspace_size():
     al = lambda x: (x + 255) // 256 * 256
     slot = st["bwd_slots"] * 128 * 128 * 4
     assert f == 0
-    assert b == al(n * 32 * 4) + 2 * al(slot)
+    assert b == 2 * al(n * 32 * 4) + 2 * al(slot)
 
 
 def test_empty_tree():
