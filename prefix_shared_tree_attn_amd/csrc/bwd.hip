@@ -366,11 +366,13 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 // and dS = P (dP - D); and C(j), the updates dV += P^T dO and dK += dS^T Q.
 // Iteration j issues C(j-1) and A(j+1) on the matrix cores while the vector
 // ALUs run B(j), so the element-wise work of a wave hides under its own
-// MFMAs.  Q, dO and the row terms of step j + 2 are loaded into registers
-// during iteration j and written to a ring of four LDS buffers before the
-// next barrier (one barrier per step).  Loads go through registers rather
-// than straight to LDS: the compiler cannot tell a direct-to-LDS load from
-// the transposed LDS reads and would drain every prefetch before them.
+// MFMAs.  Q, dO and the row terms stream through registers into a ring of
+// six LDS buffers: iteration j writes step j + 2 (loaded during iteration
+// j - 1) and issues the loads of step j + 3; only even iterations pass a
+// barrier, and the ring is deep enough that no write can reach a buffer a
+// lagging wave still reads.  Loads go through registers rather than
+// straight to LDS: the compiler cannot tell a direct-to-LDS load from the
+// transposed LDS reads and would drain every prefetch before them.
 //
 // No branch masks anything inside the loop:
 //  * rows past a query range read as zeros (each buffer resource ends at the
@@ -382,7 +384,7 @@ template <int D>
 struct DkdvPipeCfg {
   static constexpr int KC = D / 16, DB = D / 32;
   static constexpr int ROWS = 32;                // query rows per step
-  static constexpr int NB = 4;                   // LDS ring buffers
+  static constexpr int NB = 6;                   // LDS ring buffers
   static constexpr int TILE = ROWS * D * 2;      // one bf16 Q or dO tile
   static constexpr int Q_OFF = 0, DO_OFF = TILE;
   static constexpr int NL_OFF = 2 * TILE;        // -LSE log2 e (64 floats, 32 used)
@@ -493,15 +495,18 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
 
   // Loads of one step into registers: C::PER 16-byte chunks of Q and of dO
   // per thread, and for waves 0 / 1 one -LSE log2 e / -D row term per lane.
+  // Thread t fills LDS slots t, t + 256, ... of a tile in address order (no
+  // bank conflicts) and fetches the chunk the tile layout puts there.
   // Resources end at the step's last row, so rows past a query range, and
   // steps past the end (empty resources), load zeros.
   constexpr int PER = C::PER;
-  int voff[PER], loff[PER];
+  int voff[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int c = tid + 256 * i, r = c / (D / 8), cc = c % (D / 8);
-    voff[i] = r * static_cast<int>(qs * 2) + cc * 16;
-    loff[i] = QT::chunk_off(r, cc);
+    const int slot16 = tid + 256 * i;
+    const int sub = slot16 / 128, rem = slot16 % 128, r = rem >> 2;
+    const int c = sub * 4 + ((rem & 3) ^ QT::swz(r));
+    voff[i] = r * static_cast<int>(qs * 2) + c * 16;
   }
   i32x4 qreg[PER], dreg[PER];
   int treg = 0;
@@ -528,8 +533,8 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
     LDS_PTR(char) b = lds + buf * BUF;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      lds_write16(b + C::Q_OFF, loff[i], qreg[i]);
-      lds_write16(b + C::DO_OFF, loff[i], dreg[i]);
+      lds_write16(b + C::Q_OFF, 16 * (tid + 256 * i), qreg[i]);
+      lds_write16(b + C::DO_OFF, 16 * (tid + 256 * i), dreg[i]);
     }
     if (wave < 2) *reinterpret_cast<LDS_PTR(int)>(b + rterm_off + 4 * lane) = treg;
   };
@@ -668,10 +673,13 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   cur = ld;  // step j
   nx = cur;
   step_next(nx, ee, a.entries);  // step j + 1
-  issue(ld);
+  issue(ld);  // steps 0 and 1 straight into their buffers
   step_next(ld, ee, a.entries);
   commit(0);
-  issue(ld);  // step 1 (zeros if there is none)
+  issue(ld);
+  step_next(ld, ee, a.entries);
+  commit(1);
+  issue(ld);  // step 2 (zeros where there is none)
   step_next(ld, ee, a.entries);
   int bp = NB - 1, bc = 0, bn = 1;
   __syncthreads();
@@ -689,22 +697,34 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
     for (int i = NC; i < NS; ++i) mfma_slot(i, fetch(i, b0, b0));
   }
 
-  while (true) {
-    const bool more = nx.e < ee;
-    // step j + 1 into its buffer: the waves still in iteration j - 1 use
-    // buffers j - 2 .. j only
-    commit(bn);
-    __syncthreads();
-    issue(ld);  // step j + 2
-    step_next(ld, ee, a.entries);
-    const int delta = cur.r0 - wk0;
-    const bool masked = cur.causal && delta < 32;
+  auto advance = [&](bool& masked, int& delta, int& b0, int& b1, int& b2) {
+    delta = cur.r0 - wk0;
+    masked = cur.causal && delta < 32;
     cur = nx;
     step_next(nx, ee, a.entries);
-    const int b0 = bp, b1 = bc, b2 = bn;
+    b0 = bp;
+    b1 = bc;
+    b2 = bn;
     bp = bc;
     bc = bn;
     bn = nextb(bn);
+  };
+  int bw = 2;  // buffer of step j + 2
+  bool even = true;
+  while (true) {
+    const bool more = nx.e < ee;
+    // write step j + 2 and load step j + 3; even iterations pass the barrier
+    // after the write, odd ones need none (everything they read was written
+    // before the barrier of the iteration before)
+    commit(bw);
+    bw = nextb(bw);
+    if (even) __syncthreads();
+    even = !even;
+    issue(ld);
+    step_next(ld, ee, a.entries);
+    bool masked;
+    int delta, b0, b1, b2;
+    advance(masked, delta, b0, b1, b2);
     iteration(b0, b1, b2, masked, delta);
     if (!more) break;
   }

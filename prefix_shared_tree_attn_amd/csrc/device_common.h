@@ -212,32 +212,6 @@ __device__ __forceinline__ void load_tile(LDS_PTR(char) hi, LDS_PTR(char) lo, co
   }
 }
 
-// Direct global -> LDS loads (gfx950 global_load_lds_dwordx4): issues the
-// loads of rows [row0, row0 + ROWS) of a bf16 tensor (rows `stride` elements
-// apart, clamped to `last`) into a swizzled LDS tile.  The instruction writes
-// lane l's 16 bytes to LDS base + 16 l, so each lane fetches the logical
-// chunk that the swizzle places at its slot.  Completion is tracked by
-// vmcnt; callers wait (wait_vm) and synchronise before reading the tile.
-template <int D, int ROWS, int NW>
-__device__ __forceinline__ void issue_tile_lds(LDS_PTR(char) tile, const __bf16* base,
-                                               int64_t stride, int64_t row0, int64_t last,
-                                               int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int PER = ROWS * CPR / (64 * NW);
-  static_assert(ROWS * CPR % (64 * NW) == 0, "tile must split into whole wave loads");
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int slot = (wave * PER + j) * 64;
-    const int p = slot + lane;  // 16-byte LDS slot this lane fills
-    const int sub = p / (ROWS * 4), rem = p % (ROWS * 4);
-    const int r = rem >> 2;
-    const int c = sub * 4 + ((rem & 3) ^ Tile<D, ROWS>::swz(r));
-    const int64_t row = row0 + r < last ? row0 + r : last;
-    __builtin_amdgcn_global_load_lds(base + row * stride + c * 8,
-                                     (LDS_PTR(void))(tile + slot * 16), 16, 0, 0);
-  }
-}
-
 // Buffer resources (V#): a 64-bit base in scalar registers, no stride, and a
 // byte range; loads past the range return zero and stores / atomics past it
 // are dropped (the scalar offset counts toward the range).  Row tiles near
@@ -252,11 +226,55 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, const void* end) {
                                            static_cast<int>(r), kRsrcFlags);
 }
 
+// Buffer loads straight to LDS (MUBUF with the lds bit): lane l writes its
+// SIZE bytes to LDS address M0 + SIZE * l.  They are issued from inline
+// assembly on purpose.  The compiler cannot relate a direct-to-LDS load to a
+// later transposed LDS read (ds_read_b64_tr_b16 carries no alias
+// information), so with the intrinsic it drains every outstanding load
+// (vmcnt(0)) before each transposed read -- including the prefetch of the
+// next tile, which then never overlaps the compute.  Issued this way the
+// loads are invisible to that analysis: callers wait for them explicitly
+// (s_waitcnt vmcnt) and synchronise before reading the destination.  The
+// block saves and restores M0, and pads the hazards the assembler does not
+// check inside inline assembly: an SGPR written by a vector instruction
+// needs five wait states before a vector memory instruction reads it, and
+// an M0 write one wait state before an LDS DMA uses it.
+template <int SIZE>
+__device__ __forceinline__ void dma_to_lds(LDS_PTR(char) dst, int voffset, rsrc_t rs) {
+  static_assert(SIZE == 4 || SIZE == 16, "dword or dwordx4 transfers");
+  const unsigned m0v =
+      __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<__SIZE_TYPE__>(dst)));
+  unsigned saved;
+  if constexpr (SIZE == 16) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0v), "v"(voffset), "s"(rs)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0v), "v"(voffset), "s"(rs)
+        : "memory");
+  }
+}
+
 // Loads a ROWS x D bf16 row tile into a swizzled LDS tile (Tile<D, ROWS>)
-// with buffer loads straight to LDS: the wave's lanes fill consecutive
-// 16-byte LDS slots, each lane fetching the logical chunk the swizzle puts at
-// its slot.  Per-lane byte offsets are fixed for a given row stride, so a
-// step only changes the buffer base.
+// with buffer loads straight to LDS (dma_to_lds): the wave's lanes fill
+// consecutive 16-byte LDS slots, each lane fetching the logical chunk the
+// swizzle puts at its slot.  Per-lane byte offsets are fixed for a given row
+// stride, so a step only changes the buffer base.
 template <int D, int ROWS, int NW>
 struct TileLoader {
   static constexpr int PER = ROWS * (D / 8) / (64 * NW);
@@ -276,9 +294,7 @@ struct TileLoader {
   }
   __device__ __forceinline__ void issue(LDS_PTR(char) tile, rsrc_t rs) const {
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_PTR(void))(tile + lds0 + j * 1024), 16,
-                                               voff[j], 0, 0, 0);
+    for (int j = 0; j < PER; ++j) dma_to_lds<16>(tile + lds0 + j * 1024, voff[j], rs);
   }
 };
 
