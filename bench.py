@@ -1,8 +1,8 @@
 """Benchmark: prefix-shared tree attention forward + backward on one MI355X.
 
 One step is one pass of the whole path over one batch: build the plan for
-the tree (host planning + upload of its work arrays), the forward pass and
-the backward pass (preprocess, main, reductions).  Throughput is unique
+the tree (host planning + upload of its work arrays), the per-token position
+pass, the forward pass and the backward pass (preprocess, main, reductions).  Throughput is unique
 tokens per second and TFLOP/s counted on the deduplicated tree work,
 14 * D * Hq * sum_t (d(t) + 1) per step (forward 4, backward 10, in the
 usual attention convention with the backward's recomputation).
@@ -147,8 +147,12 @@ def main() -> int:
 
     plans = []
 
+    node_id = torch.empty((n,), dtype=torch.int32, device=dev)
+    pos_id = torch.empty((n,), dtype=torch.int32, device=dev)
+
     def step():
         p = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype)
+        ta.positions(p, node_id=node_id, pos_id=pos_id)
         ta.fwd(p, q, k, v, scale, o=o, lse=lse)
         ta.bwd(p, q, k, v, o, lse, do, scale, dq=dq, dk=dk, dv=dv, ws=ws)
         plans.append(p)
@@ -218,9 +222,11 @@ def main() -> int:
     dominant = max(("fwd", "bwd_dkdv", "bwd_dq"), key=avg_ms)
     main_roof = roof(dominant)
     main_roof["traffic"] = _traffic_from_profile(dominant, spec["name"])
-    # HBM-bound passes: preprocess reads O and dO and writes D; the reduction
-    # reads the fp32 partial slots and writes the split tiles' dK and dV
-    pre_bytes = n * hq * d * 2 * esize + n * hq * 4
+    # HBM-bound passes: the position pass writes node and position ids; the
+    # preprocess reads O, dO and LSE and writes -D and -LSE log2 e; the
+    # reduction reads the fp32 partial slots and writes the split tiles' dK
+    # and dV
+    pre_bytes = n * hq * d * 2 * esize + 3 * n * hq * 4
     red_bytes = 2 * pstats["bwd_slots"] * 128 * d * 4 + 2 * pstats["bwd_split_tiles"] * 128 * d * esize
     workload = spec["name"]
     result = {
@@ -254,6 +260,7 @@ def main() -> int:
         "roofline": main_roof,
         "roofline_kernels": {k: roof(k) for k in ("fwd", "bwd_dkdv", "bwd_dq")},
         "hbm_passes_GBps": {
+            "positions": 8 * n / (avg_ms("positions") * 1e-3) / 1e9,
             "bwd_pre": pre_bytes / (avg_ms("bwd_pre") * 1e-3) / 1e9,
             "bwd_reduce": (red_bytes / (avg_ms("bwd_reduce") * 1e-3) / 1e9
                            if kt["bwd_reduce"]["launches"] else None),

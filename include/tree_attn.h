@@ -157,6 +157,24 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
                                  const void* dout, float softmax_scale, void* dq, void* dk,
                                  void* dv, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * tree_attn_positions -- per-token node index and position id.
+ * Every root-to-leaf path through a unique token t places it after the
+ * tokens of its ancestor nodes and the earlier tokens of its own node, so t
+ * has one position on all of them (AReaL-DTA, abstract: each shared prefix
+ * is computed once for all trajectories through it).  For every t in
+ * [0, N): node_id[t] = the node whose segment holds t, and
+ * pos_id[t] = d(t) = the number of tokens t attends to besides itself --
+ * the 0-based position a trajectory-wise run gives t (for example the
+ * position id of rotary embeddings).
+ * node_id, pos_id: device int32 [N], overwritten; either may be null (not
+ * written).  Enqueued on `stream`; no host synchronisation.  Errors:
+ * NO_DEVICE_PLAN for host plans, INVALID_ARG for a plan of another device,
+ * HIP for a launch failure.
+ */
+tree_attn_status_t tree_attn_positions(tree_attn_plan_t plan, int32_t* node_id, int32_t* pos_id,
+                                       hipStream_t stream);
+
 /* Plan statistics for reports and tests (host values, no device access). */
 typedef struct {
   int64_t num_tokens, num_nodes, num_q_heads, num_kv_heads, head_dim;
@@ -194,12 +212,12 @@ tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_til
 
 /*
  * Kernel timing for benchmarks and reports.  While enabled, every kernel
- * that fwd/bwd launch is bracketed by HIP events on the call's stream (no
+ * that fwd/bwd/positions launch is bracketed by HIP events on the call's stream (no
  * host synchronisation).  tree_attn_timing_read waits for the recorded
  * events, and returns per kernel kind the number of launches and their summed
  * duration in milliseconds since the last reset (reset != 0 clears them).
  * Kinds: 0 forward, 1 backward preprocess, 2 backward dK/dV, 3 backward
- * partial-slot reduction, 4 backward dQ; 5..7 unused.  Timing is
+ * partial-slot reduction, 4 backward dQ, 5 positions; 6..7 unused.  Timing is
  * process-wide and not meant for concurrent callers.
  */
 typedef struct {

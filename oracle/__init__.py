@@ -11,6 +11,7 @@ Parity status of each function is listed in ``oracle/path_expansion.py``.
 from .path_expansion import (  # noqa: F401
     root_to_leaf_paths,
     path_multiplicity,
+    token_positions,
     causal_attention,
     tree_attention,
     query_rows,

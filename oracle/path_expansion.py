@@ -89,6 +89,32 @@ def path_multiplicity(paths: Sequence[np.ndarray], n_tokens: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # one trajectory: dense causal attention, forward and backward
 
+def token_positions(parent, seg_start, seg_len, n_tokens: int):
+    """Node index and trajectory position of every unique token.
+
+    Walks every root-to-leaf path (``root_to_leaf_paths``): token t at index
+    i of a path gets position i, and the node whose segment holds it.  A
+    shared-prefix token occupies the same index on every path through it (its
+    ancestors' tokens and the earlier tokens of its node precede it); the
+    walk checks that agreement.  Returns (node_id, pos_id), int64 [N].
+    """
+    seg_start = np.asarray(seg_start, np.int64)
+    seg_len = np.asarray(seg_len, np.int64)
+    node_id = np.full(n_tokens, -1, np.int64)
+    for i in range(seg_start.shape[0]):
+        node_id[seg_start[i]:seg_start[i] + seg_len[i]] = i
+    pos_id = np.full(n_tokens, -1, np.int64)
+    for path in root_to_leaf_paths(parent, seg_start, seg_len):
+        idx = np.arange(path.shape[0])
+        seen = pos_id[path]
+        if np.any((seen >= 0) & (seen != idx)):
+            raise AssertionError("a token sits at different positions on two paths")
+        pos_id[path] = idx
+    if np.any(pos_id < 0) or np.any(node_id < 0):
+        raise ValueError("the segments do not cover every token with a path")
+    return node_id, pos_id
+
+
 def causal_attention(q, k, v, do, scale: float, row_block: int = 4096):
     """Scaled dot-product attention with a causal mask on one sequence.
 

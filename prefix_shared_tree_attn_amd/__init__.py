@@ -17,8 +17,8 @@ import numpy as np
 from . import _ffi
 from ._ffi import TreeAttnError, PlanStats  # noqa: F401
 
-__all__ = ["Plan", "plan", "plan_host", "fwd", "bwd", "workspace", "TreeAttnError",
-           "timing_enable", "timing_read"]
+__all__ = ["Plan", "plan", "plan_host", "fwd", "bwd", "positions", "workspace",
+           "TreeAttnError", "timing_enable", "timing_read"]
 
 
 def _i32(a) -> np.ndarray:
@@ -187,6 +187,25 @@ def bwd(p: Plan, q, k, v, o, lse, do, scale: float, dq=None, dk=None, dv=None, w
         ctypes.c_void_p(ws.data_ptr()), ws.numel(),
         ctypes.c_void_p(_stream_handle(stream))), "bwd")
     return dq, dk, dv
+
+
+def positions(p: Plan, node_id=None, pos_id=None, stream=None):
+    """tree_attn_positions: returns (node_id [N] int32, pos_id [N] int32)."""
+    import torch
+    n = p.num_tokens
+    dev = f"cuda:{p.device}"
+    if node_id is None:
+        node_id = torch.empty((n,), dtype=torch.int32, device=dev)
+    if pos_id is None:
+        pos_id = torch.empty((n,), dtype=torch.int32, device=dev)
+    for name, x in (("node_id", node_id), ("pos_id", pos_id)):
+        if (x.dtype != torch.int32 or tuple(x.shape) != (n,) or not x.is_contiguous()
+                or x.device.type != "cuda" or x.device.index != p.device):
+            raise ValueError(f"{name} must be a contiguous int32 [{n}] tensor on {dev}")
+    _ffi.check(_ffi.lib().tree_attn_positions(
+        p.handle, ctypes.c_void_p(node_id.data_ptr()), ctypes.c_void_p(pos_id.data_ptr()),
+        ctypes.c_void_p(_stream_handle(stream))), "positions")
+    return node_id, pos_id
 
 
 def timing_enable(enable: bool = True) -> None:

@@ -19,6 +19,7 @@ EXPORTS = (
     "tree_attn_workspace_size", "tree_attn_fwd", "tree_attn_bwd",
     "tree_attn_plan_stats", "tree_attn_plan_export", "tree_attn_status_string",
     "tree_attn_last_error", "tree_attn_timing_enable", "tree_attn_timing_read",
+    "tree_attn_positions",
 )
 
 
@@ -34,7 +35,7 @@ class Timing(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64 * 8), ("total_ms", ctypes.c_double * 8)]
 
 
-TIMING_KINDS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_reduce", "bwd_dq")
+TIMING_KINDS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_reduce", "bwd_dq", "positions")
 
 
 class TreeAttnError(RuntimeError):
@@ -74,10 +75,12 @@ def lib() -> ctypes.CDLL:
     L.tree_attn_status_string.restype = ctypes.c_char_p
     L.tree_attn_last_error.argtypes = []
     L.tree_attn_last_error.restype = ctypes.c_char_p
+    L.tree_attn_positions.argtypes = [vp, vp, vp, vp]
     L.tree_attn_timing_enable.argtypes = [ctypes.c_int]
     L.tree_attn_timing_read.argtypes = [ctypes.POINTER(Timing), ctypes.c_int]
-    for fn in ("tree_attn_timing_enable", "tree_attn_timing_read", "tree_attn_plan", "tree_attn_plan_host", "tree_attn_workspace_size",
-               "tree_attn_fwd", "tree_attn_bwd", "tree_attn_plan_stats", "tree_attn_plan_export"):
+    for fn in ("tree_attn_timing_enable", "tree_attn_timing_read", "tree_attn_plan",
+               "tree_attn_plan_host", "tree_attn_workspace_size", "tree_attn_fwd", "tree_attn_bwd",
+               "tree_attn_plan_stats", "tree_attn_plan_export", "tree_attn_positions"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L

@@ -29,6 +29,7 @@ struct tree_attn_plan_s {
   const I8* d_bwd_items = nullptr;
   const I4* d_bwd_entries = nullptr;
   const I8* d_bwd_reduce = nullptr;
+  const I4* d_segments = nullptr;
 };
 
 namespace {
@@ -191,7 +192,8 @@ tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_star
   const size_t o_bi = o_fr + align256(bytes_of(hp.fwd_ranges));
   const size_t o_be = o_bi + align256(bytes_of(hp.bwd_items));
   const size_t o_br = o_be + align256(bytes_of(hp.bwd_entries));
-  const size_t total = o_br + align256(bytes_of(hp.bwd_reduce));
+  const size_t o_sg = o_br + align256(bytes_of(hp.bwd_reduce));
+  const size_t total = o_sg + align256(bytes_of(hp.segments));
   if (total > 0) {
     e = hipMalloc(reinterpret_cast<void**>(&p->dev_buf), total);
     if (e != hipSuccess) {
@@ -206,7 +208,8 @@ tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_star
                  {o_fr, hp.fwd_ranges.data(), bytes_of(hp.fwd_ranges)},
                  {o_bi, hp.bwd_items.data(), bytes_of(hp.bwd_items)},
                  {o_be, hp.bwd_entries.data(), bytes_of(hp.bwd_entries)},
-                 {o_br, hp.bwd_reduce.data(), bytes_of(hp.bwd_reduce)}};
+                 {o_br, hp.bwd_reduce.data(), bytes_of(hp.bwd_reduce)},
+                 {o_sg, hp.segments.data(), bytes_of(hp.segments)}};
     for (const Part& part : parts) {
       if (part.n == 0) continue;
       e = hipMemcpyAsync(p->dev_buf + part.off, part.src, part.n, hipMemcpyHostToDevice, stream);
@@ -222,6 +225,7 @@ tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_star
   p->d_bwd_items = reinterpret_cast<const I8*>(p->dev_buf + o_bi);
   p->d_bwd_entries = reinterpret_cast<const I4*>(p->dev_buf + o_be);
   p->d_bwd_reduce = reinterpret_cast<const I8*>(p->dev_buf + o_br);
+  p->d_segments = reinterpret_cast<const I4*>(p->dev_buf + o_sg);
   p->has_device = true;
   p->device = dev;
   *out = p;
@@ -339,6 +343,23 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
   if (e != hipSuccess) return report_hip(e, "backward reduction launch");
   e = timed(4, stream, [&] { return tree_attn::launch_bwd_dq(a, hp.dtype, hd, stream); });
   if (e != hipSuccess) return report_hip(e, "backward dQ launch");
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_positions(tree_attn_plan_t plan, int32_t* node_id,
+                                       int32_t* pos_id, hipStream_t stream) {
+  tree_attn_status_t st = check_device(plan);
+  if (st != TREE_ATTN_OK) return st;
+  const HostPlan& hp = plan->hp;
+  if (hp.num_tokens == 0 || (!node_id && !pos_id)) return TREE_ATTN_OK;
+  tree_attn::PosArgs a{};
+  a.segments = plan->d_segments;
+  a.n_segments = static_cast<int32_t>(hp.segments.size());
+  a.n_tokens = hp.num_tokens;
+  a.node_id = node_id;
+  a.pos_id = pos_id;
+  const hipError_t e = timed(5, stream, [&] { return tree_attn::launch_positions(a, stream); });
+  if (e != hipSuccess) return report_hip(e, "positions launch");
   return TREE_ATTN_OK;
 }
 

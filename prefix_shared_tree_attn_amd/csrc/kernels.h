@@ -51,6 +51,14 @@ struct BwdArgs {
   float scale_log2;  // softmax scale * log2(e)
 };
 
+struct PosArgs {
+  const I4* segments;  // (seg_start, seg_len, depth offset, node) sorted by start
+  int32_t n_segments;
+  int64_t n_tokens;
+  int32_t* node_id;    // [N] or null
+  int32_t* pos_id;     // [N] or null
+};
+
 // dtype: 0 bf16, 1 fp32.  Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, int64_t n_blocks,
                       hipStream_t stream);
@@ -58,5 +66,6 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int head_dim, hipStream_t
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_post(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_positions(const PosArgs& a, hipStream_t stream);
 
 }  // namespace tree_attn

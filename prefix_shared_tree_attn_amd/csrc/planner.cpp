@@ -119,6 +119,9 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
     push_range(anc[i], seg_start[pa], static_cast<int64_t>(seg_start[pa]) + seg_len[pa]);
     depth[i] = depth[pa] + seg_len[pa];
   }
+  p.segments.reserve(m);
+  for (int32_t i : by_start)
+    p.segments.push_back({seg_start[i], seg_len[i], static_cast<int32_t>(depth[i]), i});
   p.pairs = 0;
   for (int64_t i = 0; i < m; ++i) {
     const int64_t L = seg_len[i];

@@ -64,6 +64,10 @@ struct HostPlan {
   std::vector<I8> bwd_reduce;
   int64_t bwd_slots = 0;
   int64_t bwd_split_tiles = 0;
+
+  // segments sorted by start: (seg_start, seg_len, depth offset = ancestor
+  // tokens of the node, node index), for the per-token position pass
+  std::vector<I4> segments;
 };
 
 // Validates the table and fills `out`.  On error returns the status and a

@@ -96,8 +96,10 @@ def test_empty_tree_is_a_no_op():
     zk = torch.empty((0, 1, 128), dtype=torch.bfloat16, device="cuda")
     o, lse = ta.fwd(p, z, zk, zk, 0.1)
     dq, dk, dv = ta.bwd(p, z, zk, zk, o, lse, z, 0.1)
+    node_id, pos_id = ta.positions(p)
     torch.cuda.synchronize()
     assert o.shape == (0, 2, 128) and dk.shape == (0, 1, 128)
+    assert node_id.shape == (0,) and pos_id.shape == (0,)
 
 
 def test_repeat_runs_are_deterministic_where_promised():
@@ -215,3 +217,26 @@ def test_full_size_sampled(cfg):
     assert abs(lhs - rhs) <= 6.0 * noise + 1e-2 * max(abs(lhs), abs(rhs))
     for name in ("o", "dq", "dk", "dv", "lse"):
         assert bool(torch.isfinite(got[name]).all()), name
+
+
+def _position_trees():
+    out = [(name, case[0]) for name, case in CASES.items()]
+    out += [(f"config{i}", config_tree(i)) for i in (1, 2, 3, 4, 5)]
+    out.append(("shuffled", random_tree(np.random.default_rng(11), 13, max_len=90, n_roots=2,
+                                        shuffle=True)))
+    return out
+
+
+def test_positions_bit_exact():
+    """tree_attn_positions against the oracle's path walk, integer-exact."""
+    import torch
+    import prefix_shared_tree_attn_amd as ta
+    for name, t in _position_trees():
+        print(f"positions case {name}: N={t.num_tokens} nodes={t.num_nodes}", flush=True)
+        p = ta.plan(t.parent, t.seg_start, t.seg_len, t.num_tokens, 2, 1, 128)
+        node_id, pos_id = ta.positions(p)
+        torch.cuda.synchronize()
+        ref_node, ref_pos = oracle.token_positions(t.parent, t.seg_start, t.seg_len, t.num_tokens)
+        np.testing.assert_array_equal(node_id.cpu().numpy(), ref_node)
+        np.testing.assert_array_equal(pos_id.cpu().numpy(), ref_pos)
+        p.close()

@@ -40,13 +40,11 @@ def _run(t: NodeTable, q, k, v, do, scale, **kw):
     return oracle.tree_attention(q, k, v, do, t.parent, t.seg_start, t.seg_len, scale, **kw)
 
 
-def brute_force(t: NodeTable, q, k, v, do, scale):
-    """Dense masked attention over all N unique tokens, torch fp64 autograd.
-
-    The mask is built independently of the oracle: node-level ancestry by
-    Warshall's transitive closure of the parent relation, then token t may see
-    token u iff u's node is a proper ancestor of t's node, or both share a
-    node and u is not later in the segment."""
+def visibility_mask(t: NodeTable) -> np.ndarray:
+    """[N, N] bool: token t may see token u.  Built independently of the
+    oracle: node-level ancestry by Warshall's transitive closure of the parent
+    relation, then t sees u iff u's node is a proper ancestor of t's node, or
+    both share a node and u is not later in the segment."""
     m = t.num_nodes
     n = t.num_tokens
     anc = np.eye(m, dtype=bool)
@@ -62,8 +60,15 @@ def brute_force(t: NodeTable, q, k, v, do, scale):
         node_of[s:s + l] = i
         offset[s:s + l] = np.arange(l)
     a, b = node_of[:, None], node_of[None, :]
-    mask = (anc[a, b] & (a != b)) | ((a == b) & (offset[None, :] <= offset[:, None]))
-    mask_t = torch.from_numpy(mask)
+    return (anc[a, b] & (a != b)) | ((a == b) & (offset[None, :] <= offset[:, None]))
+
+
+def brute_force(t: NodeTable, q, k, v, do, scale):
+    """Dense masked attention over all N unique tokens, torch fp64 autograd,
+    with the independent mask of ``visibility_mask``."""
+    m = t.num_nodes
+    n = t.num_tokens
+    mask_t = torch.from_numpy(visibility_mask(t))
     hq, hkv = q.shape[1], k.shape[1]
     gs = hq // hkv
     Q = torch.tensor(q, dtype=torch.float64, requires_grad=True)
@@ -115,6 +120,40 @@ def test_golden_tiny_tree():
                              [0, 1, 2, 3], 0)
     np.testing.assert_allclose(dk, ex["dk"], atol=1e-14)
     np.testing.assert_allclose(dv, ex["dv"], atol=1e-14)
+
+
+# ------------------------------------------------------------- positions
+
+def test_positions_golden():
+    with open(os.path.join(GOLDEN, "tiny_tree_uniform.json")) as f:
+        gd = json.load(f)
+    node_id, pos_id = oracle.token_positions(gd["parent"], gd["seg_start"], gd["seg_len"], 4)
+    assert node_id.tolist() == gd["expected"]["node_id"]
+    assert pos_id.tolist() == gd["expected"]["pos_id"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_positions_equal_visible_count(seed):
+    """The position of a token is the number of tokens it sees besides
+    itself: checked against the independent transitive-closure mask."""
+    rng = np.random.default_rng(100 + seed)
+    t = random_tree(rng, int(rng.integers(1, 12)), max_len=40, n_roots=int(rng.integers(1, 3)),
+                    shuffle=bool(seed % 2))
+    node_id, pos_id = oracle.token_positions(t.parent, t.seg_start, t.seg_len, t.num_tokens)
+    mask = visibility_mask(t)
+    np.testing.assert_array_equal(pos_id, mask.sum(axis=1) - 1)
+    for i in range(t.num_nodes):
+        s, l = int(t.seg_start[i]), int(t.seg_len[i])
+        assert np.all(node_id[s:s + l] == i)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_positions_sum_to_pairs(cfg):
+    """sum_t (pos(t) + 1) is the number of (query, key) pairs, counted by the
+    tree generator independently of the oracle."""
+    t = config_tree(cfg)
+    _, pos_id = oracle.token_positions(t.parent, t.seg_start, t.seg_len, t.num_tokens)
+    assert int((pos_id + 1).sum()) == tree_stats(t)["pairs"]
 
 
 # ------------------------------------------------------------ brute force

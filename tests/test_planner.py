@@ -214,6 +214,8 @@ def test_host_plan_rejected_by_fwd():
     st = lib.tree_attn_fwd(p.handle, None, None, None, ctypes.c_float(1.0), None, None, None, 0,
                            None)
     assert _ffi.STATUS[st] == "NO_DEVICE_PLAN"
+    st = lib.tree_attn_positions(p.handle, None, None, None)
+    assert _ffi.STATUS[st] == "NO_DEVICE_PLAN"
 
 
 def test_config_plans_build_quickly():
