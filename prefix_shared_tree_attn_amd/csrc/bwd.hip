@@ -929,18 +929,27 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
           }
         }
       }
-      // P = 2^(c s - LSE log2 e); dS = P (dP - D); masked entries give 0
+      // P = 2^(c s - LSE log2 e); dS = P (dP - D); masked entries give 0.
+      // Only edge and diagonal steps mask (a wave-uniform branch; the empty
+      // asm keeps the compiler from flattening it into selects on every
+      // step).
       const bool need_mask = (kt + kFwdKeys > k1) || (causal && kt + kFwdKeys - 1 > wave_q0);
-      const int klim = (causal ? (k1 < qrow + 1 ? k1 : qrow + 1) : k1) - kt;
+      if (need_mask) {
+        asm volatile("");
+        const int klim = (causal ? (k1 < qrow + 1 ? k1 : qrow + 1) : k1) - kt;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kl = 32 * kb + 16 * (v >> 3) + 8 * half + (v & 7);
+            sacc[kb][v] = kl < klim ? sacc[kb][v] : -INFINITY;
+          }
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], a.scale_log2, nl2));
-          if (need_mask) {
-            const int kl = 32 * kb + 16 * (v >> 3) + 8 * half + (v & 7);
-            p = kl < klim ? p : 0.f;
-          }
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], a.scale_log2, nl2));
           sacc[kb][v] = p * (pacc[kb][v] + ndq);
         }
       // dQ^T += K^T dS^T over four 16-key chunks (K read transposed)
