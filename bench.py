@@ -98,6 +98,72 @@ def cpu_baseline(t, spec, budget_heads: int | None = None):
     }
 
 
+def _passes_around_attention(ta, torch, t, o, q, k, pos_id, do, hq, hkv, d, reps=5):
+    """The steps either side of the attention call, on the same workload:
+    prefix compression of the tree's root-to-leaf trajectories (host), the
+    gather of O rows to every trajectory position, the fixed-order sum of
+    per-trajectory dO rows onto unique tokens, and rotary embeddings of Q
+    and K at tree depth.  Not part of the timed step; rates are HBM bytes
+    moved (each row read and written once) per second."""
+    n = t.num_tokens
+    # trajectories: root-to-leaf paths, token id = unique row
+    parent, start, length = t.parent, t.seg_start, t.seg_len
+    kids = np.zeros(t.num_nodes, bool)
+    kids[parent[parent >= 0]] = True
+    trajs = []
+    for leaf in np.nonzero(~kids)[0]:
+        chain, node = [], int(leaf)
+        while node >= 0:
+            chain.append(node)
+            node = int(parent[node])
+        trajs.append(np.concatenate([np.arange(start[c], start[c] + length[c]) for c in chain[::-1]]))
+    t0 = time.perf_counter()
+    tree = ta.build_tree(trajs)
+    build_ms = 1e3 * (time.perf_counter() - t0)
+    total = tree.traj_index.shape[0]
+    dev = q.device
+    tidx = torch.from_numpy(tree.traj_index).to(dev)
+    off = torch.from_numpy(tree.inv_offsets).to(dev)
+    pos = torch.from_numpy(tree.inv_positions).to(dev)
+    row = hq * d * o.element_size()
+    o_traj = torch.empty((total, hq, d), dtype=o.dtype, device=dev)
+    do_traj = do[tidx]  # per-trajectory upstream gradients (input of the sum)
+    do_u = torch.empty_like(do)
+    qr, kr = q.clone(), k.clone()
+
+    def passes():
+        ta.gather_rows(o, tidx, out=o_traj)
+        ta.scatter_sum_rows(do_traj, off, pos, n, out=do_u)
+        ta.rope(qr, pos_id)
+        ta.rope(kr, pos_id)
+
+    for _ in range(2):  # warm-up: first touch of the new buffers
+        passes()
+    torch.cuda.synchronize()
+    ta.timing_read(reset=True)
+    ta.timing_enable(True)
+    for _ in range(reps):
+        passes()
+    torch.cuda.synchronize()
+    ta.timing_enable(False)
+    kt = ta.timing_read(reset=True)
+
+    def ms(kind):
+        r = kt[kind]
+        return r["total_ms"] / max(r["launches"], 1)
+
+    rope_bytes = (2 * n * hq * d + 2 * n * hkv * d) * q.element_size() / 2  # per launch, averaged
+    return {
+        "trajectories": len(trajs), "trajectory_tokens": int(total), "unique_tokens": n,
+        "build_tree_ms_host": build_ms,
+        "gather_o_GBps": 2 * total * row / (ms("gather") * 1e-3) / 1e9,
+        "scatter_sum_do_GBps": (total + n) * row / (ms("scatter_sum") * 1e-3) / 1e9,
+        "rope_qk_GBps": rope_bytes / (ms("rope") * 1e-3) / 1e9,
+        "ms": {"gather": ms("gather"), "scatter_sum": ms("scatter_sum"), "rope": ms("rope")},
+        "peak_GBps": PEAK_HBM_GBS,
+    }
+
+
 def main() -> int:
     args = _args()
     if args.gpus != 1:
@@ -268,6 +334,7 @@ def main() -> int:
         },
         "plan": {k: pstats[k] for k in ("fwd_tiles", "bwd_items", "bwd_split_tiles", "bwd_slots")},
     }
+    result["next_rows"] = _passes_around_attention(ta, torch, t, o, q, k, pos_id, do, hq, hkv, d)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu baseline)")
         result["cpu_baseline"] = cpu_baseline(t, spec)

@@ -175,6 +175,91 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
 tree_attn_status_t tree_attn_positions(tree_attn_plan_t plan, int32_t* node_id, int32_t* pos_id,
                                        hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Either side of the attention call.  Rollouts that share prefixes are
+ * stored once (AReaL-DTA, abstract; HARTS, abstract: prefix-shared
+ * trajectories processed in one packed call, per-trajectory objectives keep
+ * their interface).  These entry points build the prefix tree from token
+ * lists, hand per-token results back to trajectory positions, sum
+ * per-trajectory gradients onto unique tokens, and apply rotary embeddings
+ * at tree depth.
+ */
+
+/*
+ * tree_attn_build_tree -- prefix compression on the host (no device work).
+ * tokens[traj_offsets[num_traj]]: the concatenated token ids (>= 0) of
+ * num_traj trajectories; trajectory b is tokens[traj_offsets[b] ..
+ * traj_offsets[b+1]) (traj_offsets[0] = 0, non-decreasing; empty
+ * trajectories are allowed).  Builds the trie of all trajectories and merges
+ * its chains of single-child tokens into segments; nodes are numbered and
+ * packed in depth-first preorder with children in order of first appearance,
+ * so every segment is contiguous and the result is a valid node table for
+ * tree_attn_plan.  A trajectory that is a prefix of another adds no node.
+ * Outputs (host, caller-owned; T = traj_offsets[num_traj]):
+ *   parent, seg_start, seg_len  capacity 2 * num_traj (a node table)
+ *   unique_tokens               capacity T: token id of each unique row
+ *   traj_index [T]              unique row of every trajectory position
+ *   mult (optional)             capacity T: trajectories through each unique row
+ *   inv_offsets (optional)      capacity T + 1, and
+ *   inv_positions (optional)    [T]: positions mapping to unique row u are
+ *       inv_positions[inv_offsets[u] .. inv_offsets[u+1]), ascending
+ *   *num_nodes, *num_tokens     the sizes written
+ * Errors: INVALID_ARG (null pointer, bad offsets, negative token id),
+ * UNSUPPORTED (T >= 2^31 - 1).
+ */
+tree_attn_status_t tree_attn_build_tree(const int32_t* tokens, const int64_t* traj_offsets,
+                                        int32_t num_traj, int32_t* parent, int32_t* seg_start,
+                                        int32_t* seg_len, int32_t* unique_tokens,
+                                        int32_t* traj_index, int32_t* mult, int32_t* inv_offsets,
+                                        int32_t* inv_positions, int32_t* num_nodes,
+                                        int32_t* num_tokens);
+
+/*
+ * tree_attn_gather_rows -- dst[i, :] = src[index[i], :] for i < num_rows.
+ * The inverse of prefix compression: with index = traj_index it unpacks
+ * per-unique-token rows (log-probabilities, hidden states, ...) to every
+ * trajectory position.  src, dst: device rows of row_bytes bytes each,
+ * contiguous; index: device int32 [num_rows], every entry a valid src row
+ * (not checked).  Bit-exact copy; 16-byte transfers when row_bytes and the
+ * pointers allow.  Enqueued on `stream`.
+ */
+tree_attn_status_t tree_attn_gather_rows(const void* src, void* dst, const int32_t* index,
+                                         int64_t num_rows, int64_t row_bytes, hipStream_t stream);
+
+/*
+ * tree_attn_scatter_sum_rows -- the adjoint of the gather:
+ *   dst[u, :] = sum over j in [inv_offsets[u], inv_offsets[u+1]) of
+ *               src[inv_positions[j], :]      for u < num_rows,
+ * accumulated in fp32 in the order of inv_positions (no atomics: bitwise
+ * reproducible).  With the inverse map of tree_attn_build_tree it sums
+ * per-trajectory gradients (e.g. dO of every trajectory position) onto the
+ * unique tokens, which is the dO tree_attn_bwd expects.  src, dst: device
+ * [*, row_elems] in `dtype` (bf16 or fp32; dst is overwritten); inv_offsets
+ * [num_rows + 1] and inv_positions: device int32.  Enqueued on `stream`.
+ */
+tree_attn_status_t tree_attn_scatter_sum_rows(const void* src, void* dst,
+                                              const int32_t* inv_offsets,
+                                              const int32_t* inv_positions, int64_t num_rows,
+                                              int64_t row_elems, tree_attn_dtype_t dtype,
+                                              hipStream_t stream);
+
+/*
+ * tree_attn_rope -- rotary position embedding at tree depth, in place.
+ * x: device [num_tokens, num_heads, head_dim] in `dtype`; pos_id: device
+ * int32 [num_tokens] (e.g. from tree_attn_positions).  For every token t,
+ * head h and i < head_dim/2, the pair (x_i, x_{i + head_dim/2}) is rotated
+ * by the angle pos_id[t] * theta^(-2i/head_dim) (rotate-half pairing); with
+ * inverse != 0 by minus that angle, which is the backward of the forward
+ * rotation.  The angle is reduced in double precision and its sine and
+ * cosine taken in single precision.  Since a unique token has one position on
+ * every path through it, this equals rotating every trajectory copy at its
+ * trajectory position.  Errors: UNSUPPORTED (odd head_dim, unknown dtype),
+ * INVALID_ARG (theta <= 1 or not finite, null pointers).
+ */
+tree_attn_status_t tree_attn_rope(void* x, const int32_t* pos_id, int64_t num_tokens,
+                                  int32_t num_heads, int32_t head_dim, float theta,
+                                  int32_t inverse, tree_attn_dtype_t dtype, hipStream_t stream);
+
 /* Plan statistics for reports and tests (host values, no device access). */
 typedef struct {
   int64_t num_tokens, num_nodes, num_q_heads, num_kv_heads, head_dim;
@@ -212,17 +297,18 @@ tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_til
 
 /*
  * Kernel timing for benchmarks and reports.  While enabled, every kernel
- * that fwd/bwd/positions launch is bracketed by HIP events on the call's stream (no
+ * that the device entry points launch is bracketed by HIP events on the call's stream (no
  * host synchronisation).  tree_attn_timing_read waits for the recorded
  * events, and returns per kernel kind the number of launches and their summed
  * duration in milliseconds since the last reset (reset != 0 clears them).
  * Kinds: 0 forward, 1 backward preprocess, 2 backward dK/dV, 3 backward
- * partial-slot reduction, 4 backward dQ, 5 positions; 6..7 unused.  Timing is
+ * partial-slot reduction, 4 backward dQ, 5 positions, 6 gather, 7 scatter-sum,
+ * 8 rotary embedding; 9..15 unused.  Timing is
  * process-wide and not meant for concurrent callers.
  */
 typedef struct {
-  int64_t launches[8];
-  double total_ms[8];
+  int64_t launches[16];
+  double total_ms[16];
 } tree_attn_timing_t;
 
 tree_attn_status_t tree_attn_timing_enable(int enable);

@@ -17,3 +17,4 @@ from .path_expansion import (  # noqa: F401
     query_rows,
     key_rows,
 )
+from . import prefix_tree  # noqa: F401,E402

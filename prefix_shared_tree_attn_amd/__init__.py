@@ -18,7 +18,8 @@ from . import _ffi
 from ._ffi import TreeAttnError, PlanStats  # noqa: F401
 
 __all__ = ["Plan", "plan", "plan_host", "fwd", "bwd", "positions", "workspace",
-           "TreeAttnError", "timing_enable", "timing_read"]
+           "TreeAttnError", "timing_enable", "timing_read", "PrefixTree", "build_tree",
+           "gather_rows", "scatter_sum_rows", "rope"]
 
 
 def _i32(a) -> np.ndarray:
@@ -206,6 +207,112 @@ def positions(p: Plan, node_id=None, pos_id=None, stream=None):
         p.handle, ctypes.c_void_p(node_id.data_ptr()), ctypes.c_void_p(pos_id.data_ptr()),
         ctypes.c_void_p(_stream_handle(stream))), "positions")
     return node_id, pos_id
+
+
+class PrefixTree:
+    """Result of tree_attn_build_tree (host numpy int32 arrays)."""
+
+    def __init__(self, parent, seg_start, seg_len, unique_tokens, traj_index, mult, inv_offsets,
+                 inv_positions):
+        self.parent, self.seg_start, self.seg_len = parent, seg_start, seg_len
+        self.unique_tokens, self.traj_index, self.mult = unique_tokens, traj_index, mult
+        self.inv_offsets, self.inv_positions = inv_offsets, inv_positions
+
+    @property
+    def num_nodes(self) -> int:
+        return int(self.parent.shape[0])
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.unique_tokens.shape[0])
+
+
+def build_tree(trajectories) -> PrefixTree:
+    """tree_attn_build_tree over a list of token-id sequences."""
+    seqs = [np.asarray(t, dtype=np.int32).ravel() for t in trajectories]
+    b = len(seqs)
+    offsets = np.zeros(b + 1, np.int64)
+    if b:
+        offsets[1:] = np.cumsum([s.shape[0] for s in seqs])
+    total = int(offsets[-1])
+    tokens = np.ascontiguousarray(np.concatenate(seqs) if total else np.zeros(0, np.int32))
+    cap = max(2 * b, 1)
+    parent = np.zeros(cap, np.int32)
+    seg_start = np.zeros(cap, np.int32)
+    seg_len = np.zeros(cap, np.int32)
+    uniq = np.zeros(max(total, 1), np.int32)
+    tidx = np.zeros(max(total, 1), np.int32)
+    mult = np.zeros(max(total, 1), np.int32)
+    inv_off = np.zeros(total + 1, np.int32)
+    inv_pos = np.zeros(max(total, 1), np.int32)
+    m, n = ctypes.c_int32(0), ctypes.c_int32(0)
+    _ffi.check(_ffi.lib().tree_attn_build_tree(
+        _ptr(tokens), offsets.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), b,
+        _ptr(parent), _ptr(seg_start), _ptr(seg_len), _ptr(uniq), _ptr(tidx), _ptr(mult),
+        _ptr(inv_off), _ptr(inv_pos), ctypes.byref(m), ctypes.byref(n)), "build_tree")
+    m, n = m.value, n.value
+    return PrefixTree(parent[:m].copy(), seg_start[:m].copy(), seg_len[:m].copy(),
+                      uniq[:n].copy(), tidx[:total].copy(), mult[:n].copy(),
+                      inv_off[:n + 1].copy(), inv_pos[:total].copy())
+
+
+def _dev_check(x, name, dtype=None):
+    import torch
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if dtype is not None and x.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {x.dtype}")
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def gather_rows(src, index, out=None, stream=None):
+    """tree_attn_gather_rows: out[i] = src[index[i]] (rows = leading dimension)."""
+    import torch
+    rows = int(index.shape[0])
+    if out is None:
+        out = torch.empty((rows,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    if tuple(out.shape[1:]) != tuple(src.shape[1:]) or out.dtype != src.dtype or out.shape[0] != rows:
+        raise ValueError("out must have index.shape[0] rows shaped like src's rows")
+    row_bytes = int(np.prod(src.shape[1:])) * src.element_size()
+    _ffi.check(_ffi.lib().tree_attn_gather_rows(
+        _dev_check(src, "src"), _dev_check(out, "out"), _dev_check(index, "index", torch.int32),
+        rows, row_bytes, ctypes.c_void_p(_stream_handle(stream))), "gather_rows")
+    return out
+
+
+def scatter_sum_rows(src, inv_offsets, inv_positions, num_rows: int, out=None, stream=None):
+    """tree_attn_scatter_sum_rows: out[u] = sum of src rows mapped to u (fp32, fixed order)."""
+    import torch
+    dt = {torch.bfloat16: "bf16", torch.float32: "fp32"}.get(src.dtype)
+    if dt is None:
+        raise TypeError("src must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((num_rows,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    if tuple(out.shape) != (num_rows,) + tuple(src.shape[1:]) or out.dtype != src.dtype:
+        raise ValueError("out must be [num_rows] + src row shape in src's dtype")
+    row_elems = int(np.prod(src.shape[1:])) if src.dim() > 1 else 1
+    _ffi.check(_ffi.lib().tree_attn_scatter_sum_rows(
+        _dev_check(src, "src"), _dev_check(out, "out"),
+        _dev_check(inv_offsets, "inv_offsets", torch.int32),
+        _dev_check(inv_positions, "inv_positions", torch.int32), int(num_rows), row_elems,
+        _ffi.DTYPES[dt], ctypes.c_void_p(_stream_handle(stream))), "scatter_sum_rows")
+    return out
+
+
+def rope(x, pos_id, theta: float = 10000.0, inverse: bool = False, stream=None):
+    """tree_attn_rope: rotates x [N, H, D] in place at positions pos_id [N]."""
+    import torch
+    dt = {torch.bfloat16: "bf16", torch.float32: "fp32"}.get(x.dtype)
+    if dt is None or x.dim() != 3:
+        raise TypeError("x must be a 3-D bfloat16 or float32 tensor [N, H, D]")
+    n, h, d = (int(v) for v in x.shape)
+    if tuple(pos_id.shape) != (n,):
+        raise ValueError(f"pos_id must have shape ({n},)")
+    _ffi.check(_ffi.lib().tree_attn_rope(
+        _dev_check(x, "x"), _dev_check(pos_id, "pos_id", torch.int32), n, h, d,
+        ctypes.c_float(theta), 1 if inverse else 0, _ffi.DTYPES[dt],
+        ctypes.c_void_p(_stream_handle(stream))), "rope")
+    return x
 
 
 def timing_enable(enable: bool = True) -> None:

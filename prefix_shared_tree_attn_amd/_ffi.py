@@ -19,7 +19,8 @@ EXPORTS = (
     "tree_attn_workspace_size", "tree_attn_fwd", "tree_attn_bwd",
     "tree_attn_plan_stats", "tree_attn_plan_export", "tree_attn_status_string",
     "tree_attn_last_error", "tree_attn_timing_enable", "tree_attn_timing_read",
-    "tree_attn_positions",
+    "tree_attn_positions", "tree_attn_build_tree", "tree_attn_gather_rows",
+    "tree_attn_scatter_sum_rows", "tree_attn_rope",
 )
 
 
@@ -32,10 +33,11 @@ class PlanStats(ctypes.Structure):
 
 
 class Timing(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int64 * 8), ("total_ms", ctypes.c_double * 8)]
+    _fields_ = [("launches", ctypes.c_int64 * 16), ("total_ms", ctypes.c_double * 16)]
 
 
-TIMING_KINDS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_reduce", "bwd_dq", "positions")
+TIMING_KINDS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_reduce", "bwd_dq", "positions", "gather",
+                "scatter_sum", "rope")
 
 
 class TreeAttnError(RuntimeError):
@@ -76,11 +78,20 @@ def lib() -> ctypes.CDLL:
     L.tree_attn_last_error.argtypes = []
     L.tree_attn_last_error.restype = ctypes.c_char_p
     L.tree_attn_positions.argtypes = [vp, vp, vp, vp]
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    L.tree_attn_build_tree.argtypes = [i32p, i64p, ctypes.c_int32] + [i32p] * 10
+    L.tree_attn_gather_rows.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
+    L.tree_attn_scatter_sum_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int, vp]
+    L.tree_attn_rope.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_float, ctypes.c_int32, ctypes.c_int, vp]
     L.tree_attn_timing_enable.argtypes = [ctypes.c_int]
     L.tree_attn_timing_read.argtypes = [ctypes.POINTER(Timing), ctypes.c_int]
     for fn in ("tree_attn_timing_enable", "tree_attn_timing_read", "tree_attn_plan",
                "tree_attn_plan_host", "tree_attn_workspace_size", "tree_attn_fwd", "tree_attn_bwd",
-               "tree_attn_plan_stats", "tree_attn_plan_export", "tree_attn_positions"):
+               "tree_attn_plan_stats", "tree_attn_plan_export", "tree_attn_positions",
+               "tree_attn_build_tree", "tree_attn_gather_rows", "tree_attn_scatter_sum_rows",
+               "tree_attn_rope"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L

@@ -21,7 +21,8 @@ LIB = os.path.join(HERE, "libtree_attn.so")
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-SOURCES = ["api.cpp", "planner.cpp", "fwd.hip", "bwd.hip", "positions.hip"]
+SOURCES = ["api.cpp", "planner.cpp", "prefix_tree.cpp", "fwd.hip", "bwd.hip", "positions.hip",
+           "prefix_ops.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Device code: no hand-picked packed fp32 ops (the feature is disabled), fast

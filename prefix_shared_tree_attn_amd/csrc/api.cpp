@@ -13,6 +13,7 @@
 
 #include "kernels.h"
 #include "planner.h"
+#include "prefix_tree.h"
 
 using tree_attn::HostPlan;
 using tree_attn::I4;
@@ -91,7 +92,7 @@ size_t bytes_of(const V& v) {
 }
 
 // Optional per-kernel timing: HIP events around each launch, read later.
-constexpr int kTimingKinds = 8;
+constexpr int kTimingKinds = 16;
 struct Timing {
   std::mutex mu;
   bool enabled = false;
@@ -360,6 +361,77 @@ tree_attn_status_t tree_attn_positions(tree_attn_plan_t plan, int32_t* node_id,
   a.pos_id = pos_id;
   const hipError_t e = timed(5, stream, [&] { return tree_attn::launch_positions(a, stream); });
   if (e != hipSuccess) return report_hip(e, "positions launch");
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_build_tree(const int32_t* tokens, const int64_t* traj_offsets,
+                                        int32_t num_traj, int32_t* parent, int32_t* seg_start,
+                                        int32_t* seg_len, int32_t* unique_tokens,
+                                        int32_t* traj_index, int32_t* mult, int32_t* inv_offsets,
+                                        int32_t* inv_positions, int32_t* num_nodes,
+                                        int32_t* num_tokens) {
+  std::string err;
+  const Status s = tree_attn::build_prefix_tree(tokens, traj_offsets, num_traj, parent, seg_start,
+                                                seg_len, unique_tokens, traj_index, mult,
+                                                inv_offsets, inv_positions, num_nodes, num_tokens,
+                                                &err);
+  if (s != Status::kOk) return report(s, err);
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_gather_rows(const void* src, void* dst, const int32_t* index,
+                                         int64_t num_rows, int64_t row_bytes,
+                                         hipStream_t stream) {
+  if (num_rows < 0 || row_bytes < 0)
+    return report(Status::kInvalidArg, "negative row count or row size");
+  if (num_rows == 0 || row_bytes == 0) return TREE_ATTN_OK;
+  if (!src || !dst || !index) return report(Status::kInvalidArg, "null pointer");
+  const hipError_t e = timed(6, stream, [&] {
+    return tree_attn::launch_gather(src, dst, index, num_rows, row_bytes, stream);
+  });
+  if (e != hipSuccess) return report_hip(e, "gather launch");
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_scatter_sum_rows(const void* src, void* dst,
+                                              const int32_t* inv_offsets,
+                                              const int32_t* inv_positions, int64_t num_rows,
+                                              int64_t row_elems, tree_attn_dtype_t dtype,
+                                              hipStream_t stream) {
+  if (num_rows < 0 || row_elems < 0)
+    return report(Status::kInvalidArg, "negative row count or row size");
+  if (dtype != TREE_ATTN_BF16 && dtype != TREE_ATTN_FP32)
+    return report(Status::kUnsupported, "unknown dtype");
+  if (num_rows == 0 || row_elems == 0) return TREE_ATTN_OK;
+  if (!src || !dst || !inv_offsets || !inv_positions)
+    return report(Status::kInvalidArg, "null pointer");
+  const hipError_t e = timed(7, stream, [&] {
+    return tree_attn::launch_scatter_sum(src, dst, inv_offsets, inv_positions, num_rows, row_elems,
+                                         static_cast<int>(dtype), stream);
+  });
+  if (e != hipSuccess) return report_hip(e, "scatter-sum launch");
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_rope(void* x, const int32_t* pos_id, int64_t num_tokens,
+                                  int32_t num_heads, int32_t head_dim, float theta,
+                                  int32_t inverse, tree_attn_dtype_t dtype, hipStream_t stream) {
+  if (num_tokens < 0 || num_heads < 0)
+    return report(Status::kInvalidArg, "negative token or head count");
+  if (head_dim <= 0 || head_dim % 2 != 0)
+    return report(Status::kUnsupported, "head_dim must be positive and even");
+  if (!(theta > 1.f) || !std::isfinite(theta))
+    return report(Status::kInvalidArg, "theta must be finite and > 1");
+  if (dtype != TREE_ATTN_BF16 && dtype != TREE_ATTN_FP32)
+    return report(Status::kUnsupported, "unknown dtype");
+  if (num_tokens == 0 || num_heads == 0) return TREE_ATTN_OK;
+  if (!x || !pos_id) return report(Status::kInvalidArg, "null pointer");
+  const hipError_t e = timed(8, stream, [&] {
+    return tree_attn::launch_rope(x, pos_id, num_tokens, num_heads, head_dim,
+                                  std::log2(static_cast<double>(theta)), inverse ? 1 : 0,
+                                  static_cast<int>(dtype), stream);
+  });
+  if (e != hipSuccess) return report_hip(e, "rope launch");
   return TREE_ATTN_OK;
 }
 

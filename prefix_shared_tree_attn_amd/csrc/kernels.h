@@ -68,4 +68,13 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int head_dim, hipStream_t 
 hipError_t launch_bwd_post(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_positions(const PosArgs& a, hipStream_t stream);
 
+// Passes either side of the attention call (prefix_ops.hip).
+hipError_t launch_gather(const void* src, void* dst, const int32_t* index, int64_t rows,
+                         int64_t row_bytes, hipStream_t stream);
+hipError_t launch_scatter_sum(const void* src, void* dst, const int32_t* offsets,
+                              const int32_t* positions, int64_t rows, int64_t row_elems, int dtype,
+                              hipStream_t stream);
+hipError_t launch_rope(void* x, const int32_t* pos, int64_t n_tokens, int heads, int head_dim,
+                       double log2_theta, int inverse, int dtype, hipStream_t stream);
+
 }  // namespace tree_attn
