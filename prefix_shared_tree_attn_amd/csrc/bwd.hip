@@ -58,7 +58,7 @@ struct Blk {
 
 __device__ __forceinline__ bool load_entry(Blk& b, int e, int ee, const I4* entries) {
   if (e >= ee) return false;
-  const I4 en = entries[e];
+  const I4 en = load_plan4(entries, e);
   b.h = en.x;
   b.qb = en.y;
   b.qe = en.z;
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem_dyn[];
   LDS_PTR(char) lds = (LDS_PTR(char))(smem_dyn);
 
-  const I8 it = a.items[blockIdx.x];
+  const I8 it = load_plan8(a.items, blockIdx.x);
   const int k0 = it.v[0], k1 = it.v[1], g = it.v[2], eb = it.v[3], ee = it.v[4];
   const int slot = it.v[5];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -402,18 +402,14 @@ struct Step {
   int e, r0, qe, h, causal;
 };
 
-// Plan arrays are read-only while a kernel runs: reading them through the
-// constant address space gives uniform scalar loads.
-#define CONST_PTR(T) __attribute__((address_space(4))) const T*
-
 __device__ __forceinline__ void step_at(Step& s, int e, int ee, const I4* entries) {
   s.e = e;
   if (e < ee) {
-    CONST_PTR(int) en = (CONST_PTR(int))(entries) + 4 * static_cast<int64_t>(e);
-    s.h = en[0];
-    s.r0 = en[1];
-    s.qe = en[2];
-    s.causal = en[3];
+    const I4 en = load_plan4(entries, e);
+    s.h = en.x;
+    s.r0 = en.y;
+    s.qe = en.z;
+    s.causal = en.w;
   } else {
     s.h = 0;
     s.r0 = 0;
@@ -455,7 +451,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   extern __shared__ __attribute__((aligned(16))) char smem_dyn[];
   LDS_PTR(char) lds = (LDS_PTR(char))(smem_dyn);
 
-  const I8 it = a.items[blockIdx.x];
+  const I8 it = load_plan8(a.items, blockIdx.x);
   const int k0 = it.v[0], k1 = it.v[1], g = it.v[2], eb = it.v[3], ee = it.v[4];
   const int slot = it.v[5];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -794,7 +790,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
   const int tile = static_cast<int>(gi / a.hkv);
   const int g = static_cast<int>(gi % a.hkv);
   const int h = g * a.gsize + wslot % a.gsize;
-  const I4 t = a.tiles[tile];
+  const I4 t = load_plan4(a.tiles, tile);
   const int q0 = t.x, q1 = t.y;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -875,7 +871,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
     for (int v = 0; v < 16; ++v) qacc[db][v] = 0.f;
 
   int ri = t.z;
-  I4 rg = a.ranges[ri];
+  I4 rg = load_plan4(a.ranges, ri);
   int kt = rg.x;
   issue(kt, 0);
   commit(0);
@@ -888,7 +884,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
       nri = ri + 1;
       has_next = nri < t.w;
       if (has_next) {
-        nrg = a.ranges[nri];
+        nrg = load_plan4(a.ranges, nri);
         nkt = nrg.x;
       }
     }
@@ -1003,7 +999,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
 // 4. post: partial-slot reduction (fixed order: deterministic dK / dV)
 template <typename T, int D>
 __global__ __launch_bounds__(256) void tree_attn_bwd_reduce_kernel(BwdArgs a) {
-  const I8 r = a.reduce[blockIdx.x];
+  const I8 r = load_plan8(a.reduce, blockIdx.x);
   const int k0 = r.v[0], k1 = r.v[1], g = r.v[2], sb = r.v[3], ns = r.v[4];
   const int64_t ks = static_cast<int64_t>(a.hkv) * D;
   // this block's share of the tile's (k1 - k0) * D elements

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "planner.h"
+
 namespace tree_attn {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -153,6 +155,24 @@ __device__ __forceinline__ int swap23(int r) {
 }
 
 // Global memory helpers -----------------------------------------------------
+
+// Plan arrays are read-only while a kernel runs.  Reading them through the
+// constant address space gives uniform scalar loads; a vector load instead
+// would make the compiler wait for every outstanding vector memory operation
+// (s_waitcnt vmcnt(0)) before using the value -- including tile prefetches.
+#define CONST_PTR(T) __attribute__((address_space(4))) const T*
+
+__device__ __forceinline__ I4 load_plan4(const I4* p, int64_t i) {
+  CONST_PTR(int) q = (CONST_PTR(int))(p) + 4 * i;
+  return {q[0], q[1], q[2], q[3]};
+}
+__device__ __forceinline__ I8 load_plan8(const I8* p, int64_t i) {
+  CONST_PTR(int) q = (CONST_PTR(int))(p) + 8 * i;
+  I8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r.v[j] = q[j];
+  return r;
+}
 __device__ __forceinline__ i32x4 gload16(const void* p) {
   return *reinterpret_cast<const i32x4*>(p);
 }

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   const int tile = static_cast<int>(gi / a.hkv);
   const int g = static_cast<int>(gi % a.hkv);
   const int h = g * a.gsize + slot % a.gsize;
-  const I4 t = a.tiles[tile];
+  const I4 t = load_plan4(a.tiles, tile);
   const int q0 = t.x, q1 = t.y;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   // Key tiles in order: the tile's ranges (ancestors root first, then the
   // causal range of its own node), kFwdKeys keys at a time.
   int ri = t.z;
-  I4 rg = a.ranges[ri];
+  I4 rg = load_plan4(a.ranges, ri);
   int kt = rg.x;
   issue(kt, 0);
   commit(0);
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
       nri = ri + 1;
       has_next = nri < t.w;
       if (has_next) {
-        nrg = a.ranges[nri];
+        nrg = load_plan4(a.ranges, nri);
         nkt = nrg.x;
       }
     }
