@@ -423,23 +423,73 @@ __device__ __forceinline__ void step_next(Step& s, int ee, const I4* entries) {
   if (s.r0 >= s.qe) step_at(s, s.e < ee ? s.e + 1 : ee, ee, entries);
 }
 
+// The step whose rows are being loaded, with the byte addresses of its first
+// Q / dO row and row term, so that moving on within an entry is a few scalar
+// adds rather than a fresh row-times-stride product.
+struct LoadStep {
+  Step s;
+  const char* q;   // &Q[r0, h, 0]
+  const char* d;   // &dO[r0, h, 0]
+  const char* t;   // &rterm[h, r0] (-LSE log2 e or -D)
+};
+
+__device__ __forceinline__ void load_at(LoadStep& l, int e, int ee, const I4* entries,
+                                        const char* q, const char* d, const char* t,
+                                        int64_t row_bytes, int64_t head_bytes, int64_t n_tokens) {
+  step_at(l.s, e, ee, entries);
+  const int64_t r0 = l.s.r0, h = l.s.h;
+  l.q = q + r0 * row_bytes + h * head_bytes;
+  l.d = d + r0 * row_bytes + h * head_bytes;
+  l.t = t + 4 * (h * n_tokens + r0);
+}
+
+__device__ __forceinline__ void load_next(LoadStep& l, int ee, const I4* entries, const char* q,
+                                          const char* d, const char* t, int64_t row_bytes,
+                                          int64_t head_bytes, int64_t n_tokens) {
+  l.s.r0 += 32;
+  l.q += 32 * row_bytes;
+  l.d += 32 * row_bytes;
+  l.t += 4 * 32;
+  if (l.s.r0 >= l.s.qe)
+    load_at(l, l.s.e < ee ? l.s.e + 1 : ee, ee, entries, q, d, t, row_bytes, head_bytes,
+            n_tokens);
+}
+
 // P and dS of one step packed as A operands of the dV / dK products: p[c] /
 // s[c] hold this lane's key against rows 16 c + 8 (lane / 32) + (0..7).
 struct PdsPack {
   bf16x8 p[2], s[2];
 };
 
+// S and dP MFMAs of the pipelined kernel, written as inline asm so that
+// their results land in ordinary VGPRs.  At one wave per SIMD the compiler
+// gives every MFMA result to the accumulation registers, and each element
+// would then need a v_accvgpr_read -- one more instruction for a wave that
+// can issue only one every four cycles.  The compiler does not see these
+// statements as MFMAs and inserts no hazard wait states after them, so the
+// last MFMA of each chain carries its own: sixteen wait states, more than an
+// 8-pass XDL result needs before a VALU op may read or overwrite it (CDNA3 /
+// CDNA4 ISA, dependency rules).  Within a chain the accumulator is read back
+// as source C in the same registers, which needs none.  Their A operands
+// come from LDS loads and their B operands from registers loaded before the
+// loop, never from a VALU op just before; a CPU test checks the compiled
+// code for both conditions.
+__device__ __forceinline__ void mfma_v_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_last(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(d)
+               : "v"(a), "v"(b));
+}
+
 // Empty asm use: the value must be computed before this point, which keeps
 // the compiler from sinking element-wise work out of its MFMA slot.
 __device__ __forceinline__ void keep(float x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void keep(const bf16x8& x) { asm volatile("" ::"v"(x)); }
-
-__device__ __forceinline__ rsrc_t make_rsrc_n(const void* base, int64_t bytes) {
-  const uint32_t r =
-      bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(r), kRsrcFlags);
-}
 
 }  // namespace
 
@@ -506,27 +556,34 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   }
   i32x4 qreg[PER], dreg[PER];
   int treg = 0;
-  const float* rterm = wave == 1 ? a.neg_d : a.neg_lse2;
+  const char* rterm =
+      reinterpret_cast<const char*>(wave == 1 ? a.neg_d : a.neg_lse2);
   const int rterm_off = wave == 1 ? C::ND_OFF : C::NL_OFF;
-  auto issue = [&](const Step& s) {
-    const bool valid = s.e < ee;
-    const int64_t rows = valid ? (s.qe - s.r0 < 32 ? s.qe - s.r0 : 32) : 0;
-    const int64_t base = static_cast<int64_t>(s.r0) * qs + static_cast<int64_t>(s.h) * D;
-    const rsrc_t rq = make_rsrc_n(Qall + base, rows * qs * 2);
-    const rsrc_t rd = make_rsrc_n(dOall + base, rows * qs * 2);
+  // A step covers at most 32 rows, so its byte counts fit 32 bits.
+  const int64_t row_bytes = qs * 2, head_bytes = D * 2;
+  const uint32_t row_bytes32 = static_cast<uint32_t>(row_bytes);
+  const char* Qb = reinterpret_cast<const char*>(Qall);
+  const char* dOb = reinterpret_cast<const char*>(dOall);
+  auto issue = [&](const LoadStep& l) __attribute__((always_inline)) {
+    const int rows = l.s.e < ee ? (l.s.qe - l.s.r0 < 32 ? l.s.qe - l.s.r0 : 32) : 0;
+    const uint32_t nb = static_cast<uint32_t>(rows) * row_bytes32;
+    const rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(l.q), static_cast<short>(0),
+                                                        static_cast<int>(nb), kRsrcFlags);
+    const rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(l.d), static_cast<short>(0),
+                                                        static_cast<int>(nb), kRsrcFlags);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       qreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff[i], 0, 0);
       dreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rd, voff[i], 0, 0);
     }
     if (wave < 2) {
-      const rsrc_t rr =
-          make_rsrc_n(rterm + static_cast<int64_t>(s.h) * a.n_tokens + s.r0, rows * 4);
+      const rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(l.t), static_cast<short>(0), 4 * rows, kRsrcFlags);
       treg = __builtin_amdgcn_raw_buffer_load_b32(rr, 4 * lane, 0, 0);
     }
   };
-  auto commit = [&](int buf) {
-    LDS_PTR(char) b = lds + buf * BUF;
+  auto commit = [&](int boff) __attribute__((always_inline)) {
+    LDS_PTR(char) b = lds + boff;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       lds_write16(b + C::Q_OFF, 16 * (tid + 256 * i), qreg[i]);
@@ -556,7 +613,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
       dv_acc[db][v] = 0.f;
     }
 
-  auto nextb = [](int b) { return b + 1 == NB ? 0 : b + 1; };
+  auto nexto = [&](int o) __attribute__((always_inline)) { return o + BUF == NB * BUF ? 0 : o + BUF; };
 
   // MFMA slots of one iteration: first the dV / dK updates of the previous
   // step (slot i < NC: column block i / 4, row chunk (i / 2) % 2, dV for even
@@ -564,7 +621,8 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   // NC + 2 kc + 1 for dP).
   constexpr int NC = 4 * DB, NS = NC + 2 * KC;
   constexpr int LA = 3;  // operands are read this many slots ahead
-  auto fetch = [&](int i, LDS_PTR(char) bprev, LDS_PTR(char) bnext) -> bf16x8 {
+  auto fetch = [&](int i, LDS_PTR(char) bprev, LDS_PTR(char) bnext)
+                   __attribute__((always_inline)) -> bf16x8 {
     if (i < NC) {
       const int imm = (i >> 2) * QT::SUB + ((i >> 1) & 1) * 1024;
       LDS_PTR(char) t = bprev + ((i & 1) ? C::Q_OFF : C::DO_OFF);
@@ -586,16 +644,18 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   // step whose updates run next
   f32x16 sacc, pacc;
   PdsPack pk;
-  const f32x16 zero16 = {};
-  auto mfma_slot = [&](int i, const bf16x8& op) {
+  auto mfma_slot = [&](int i, const bf16x8& op) __attribute__((always_inline)) {
     if (i < NC) {
       const int db = i >> 2, qc = (i >> 1) & 1;
       if (i & 1) dk_acc[db] = mfma32(pk.s[qc], op, dk_acc[db]);
       else dv_acc[db] = mfma32(pk.p[qc], op, dv_acc[db]);
     } else {
       const int kc = (i - NC) >> 1;
-      if ((i - NC) & 1) pacc = mfma32(op, vf[kc], kc == 0 ? zero16 : pacc);
-      else sacc = mfma32(op, kf[kc], kc == 0 ? zero16 : sacc);
+      f32x16& acc = ((i - NC) & 1) ? pacc : sacc;
+      const bf16x8& b = ((i - NC) & 1) ? vf[kc] : kf[kc];
+      if (kc == 0) mfma_v_first(acc, op, b);
+      else if (kc == KC - 1) mfma_v_last(acc, op, b);
+      else mfma_v_acc(acc, op, b);
     }
   };
 
@@ -606,10 +666,10 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   // bf16 packs are formed, after the last C slot has read the old packs.
   // The fences keep this order.  Under the causal mask (rare steps) x is set
   // to -inf where key > row between the halves.
-  auto iteration = [&](int bp, int bc, int bn, bool masked, int delta) {
-    LDS_PTR(char) bprev = lds + bp * BUF;
-    LDS_PTR(char) bcur = lds + bc * BUF;
-    LDS_PTR(char) bnext = lds + bn * BUF;
+  auto iteration = [&](int bp, int bc, int bn, bool masked, int delta) __attribute__((always_inline)) {
+    LDS_PTR(char) bprev = lds + bp;
+    LDS_PTR(char) bcur = lds + bc;
+    LDS_PTR(char) bnext = lds + bn;
     f32x4 nl[4], nd[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -664,20 +724,24 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  Step ld, cur, nx;
-  step_at(ld, eb, ee, a.entries);
-  cur = ld;  // step j
-  nx = cur;
+  LoadStep ld;
+  auto ld_next = [&]() __attribute__((always_inline)) {
+    load_next(ld, ee, a.entries, Qb, dOb, rterm, row_bytes, head_bytes, a.n_tokens);
+  };
+  load_at(ld, eb, ee, a.entries, Qb, dOb, rterm, row_bytes, head_bytes, a.n_tokens);
+  Step cur = ld.s;  // step j
+  Step nx = cur;
   step_next(nx, ee, a.entries);  // step j + 1
   issue(ld);  // steps 0 and 1 straight into their buffers
-  step_next(ld, ee, a.entries);
+  ld_next();
   commit(0);
   issue(ld);
-  step_next(ld, ee, a.entries);
-  commit(1);
+  ld_next();
+  commit(BUF);
   issue(ld);  // step 2 (zeros where there is none)
-  step_next(ld, ee, a.entries);
-  int bp = NB - 1, bc = 0, bn = 1;
+  ld_next();
+  // ring buffers as byte offsets: previous, current and next step
+  int bp = (NB - 1) * BUF, bc = 0, bn = BUF;
   __syncthreads();
   // A of step 0; the first C(-1) runs on zero packs and a cleared buffer
 #pragma unroll
@@ -688,24 +752,12 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
       pk.s[c][e] = to_bf16(0.f);
     }
   {
-    LDS_PTR(char) b0 = lds + bc * BUF;
+    LDS_PTR(char) b0 = lds + bc;
 #pragma unroll
     for (int i = NC; i < NS; ++i) mfma_slot(i, fetch(i, b0, b0));
   }
 
-  auto advance = [&](bool& masked, int& delta, int& b0, int& b1, int& b2) {
-    delta = cur.r0 - wk0;
-    masked = cur.causal && delta < 32;
-    cur = nx;
-    step_next(nx, ee, a.entries);
-    b0 = bp;
-    b1 = bc;
-    b2 = bn;
-    bp = bc;
-    bc = bn;
-    bn = nextb(bn);
-  };
-  int bw = 2;  // buffer of step j + 2
+  int bw = 2 * BUF;  // buffer of step j + 2
   bool even = true;
   while (true) {
     const bool more = nx.e < ee;
@@ -713,20 +765,24 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
     // after the write, odd ones need none (everything they read was written
     // before the barrier of the iteration before)
     commit(bw);
-    bw = nextb(bw);
+    bw = nexto(bw);
     if (even) __syncthreads();
     even = !even;
     issue(ld);
-    step_next(ld, ee, a.entries);
-    bool masked;
-    int delta, b0, b1, b2;
-    advance(masked, delta, b0, b1, b2);
-    iteration(b0, b1, b2, masked, delta);
+    ld_next();
+    const int delta = cur.r0 - wk0;
+    const bool masked = cur.causal && delta < 32;
+    cur = nx;
+    step_next(nx, ee, a.entries);
+    iteration(bp, bc, bn, masked, delta);
+    bp = bc;
+    bc = bn;
+    bn = nexto(bn);
     if (!more) break;
   }
   // C of the last step (its buffer is bp now)
   {
-    LDS_PTR(char) bl = lds + bp * BUF;
+    LDS_PTR(char) bl = lds + bp;
 #pragma unroll
     for (int i = 0; i < NC; ++i) mfma_slot(i, fetch(i, bl, bl));
   }

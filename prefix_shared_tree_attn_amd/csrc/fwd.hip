@@ -31,6 +31,15 @@ struct FwdCfg {
   static constexpr int BYTES = NBUF * 2 * NP * PLANE;
 };
 
+// Max of x over lanes l and l ^ 32: v_permlane32_swap exchanges the two
+// 32-lane halves between its operands, so with x in both, the pair it returns
+// holds x and its partner lane's x in every lane.
+__device__ __forceinline__ float max_across_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   using C = FwdCfg<T, D>;
@@ -130,8 +139,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-  float m = -INFINITY;  // running max of base-2 scaled scores of row qrow
-  float lsum = 0.f;     // running sum over this lane's keys
+  float m = -INFINITY;                // running max of base-2 scaled scores of row qrow
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // running sum over this lane's keys, four parts
 
   // Key tiles in order: the tile's ranges (ancestors root first, then the
   // causal range of its own node), kFwdKeys keys at a time.
@@ -166,19 +175,34 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
     if (!skip) {
     // S^T for keys kt + 32 kb + (0..31); A row r holds key swap23(r) so
     // that register v of this lane is key 16 (v / 8) + 8 half + v % 8.
+    // K fragments are read KLA products ahead of their MFMA; the fences keep
+    // the scheduler from folding the reads back next to their use, where
+    // each product would wait out a full LDS round trip.
     f32x16 sacc[2];
+    {
+      constexpr int NSL = 2 * KC, KLA = 4;
+      auto kfetch = [&](int i) {
+        const int krow = 32 * (i / KC) + swap23(l32);
+        Frag<SPLIT> f;
+        f.h = row_operand<KT>(k_tile(buf, 0), krow, 2 * (i % KC) + half);
+        if constexpr (SPLIT) f.l = row_operand<KT>(k_tile(buf, 1), krow, 2 * (i % KC) + half);
+        return f;
+      };
+      Frag<SPLIT> kop[NSL];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int i = 0; i < KLA; ++i) kop[i] = kfetch(i);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-      const int krow = 32 * kb + swap23(l32);
+      for (int i = 0; i < NSL; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + KLA < NSL) kop[i + KLA] = kfetch(i + KLA);
+        const int kb = i / KC;
+        if (i % KC == 0) {
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        Frag<SPLIT> af;
-        af.h = row_operand<KT>(k_tile(buf, 0), krow, 2 * kc + half);
-        if constexpr (SPLIT) af.l = row_operand<KT>(k_tile(buf, 1), krow, 2 * kc + half);
-        mma<SPLIT>(sacc[kb], af, qf[kc]);
+          for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+        }
+        mma<SPLIT>(sacc[kb], kop[i], qf[i % KC]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // Mask only on tiles that reach past the range or cross the diagonal of
@@ -199,17 +223,22 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
     // scale is positive) and the running reference m is moved only when the
     // max grows by more than 8: p = 2^(c s - m) then stays below 2^8, and O
     // and l always share the same m, so the result is exact either way.
-    float mx = -INFINITY;
+    // The max and the sum run as four independent chains each (a single
+    // chain would make every step wait out 16 or 32 dependent ALU latencies)
+    // and the two lane halves meet through a lane swap, not through LDS.
+    float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+      for (int v = 0; v < 16; ++v) mx4[v & 3] = fmaxf(mx4[v & 3], sacc[kb][v]);
+    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+    mx = max_across_halves(mx) * a.scale_log2;
     if (__any(mx > m + 8.f)) {
       const float m_new = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       m = m_new;
-      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lsum[i] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -222,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
       for (int v = 0; v < 16; ++v) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], a.scale_log2, neg_m));
         sacc[kb][v] = p;
-        lsum += p;
+        lsum[v & 3] += p;
       }
     }
 
@@ -256,7 +285,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   }
 
   // finalize: O = O^T / l, LSE = ln 2 * (m + log2 l)
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float lpart = (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+  const float ltot = lpart + __shfl_xor(lpart, 32);
   if (qrow < q1) {
     const float inv = 1.f / ltot;
     T* op = static_cast<T*>(a.o) + static_cast<int64_t>(qrow) * qs + static_cast<int64_t>(h) * D;
