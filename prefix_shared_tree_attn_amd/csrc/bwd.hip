@@ -880,12 +880,13 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
   i32x4 kreg[SPLIT_PER], vreg[SPLIT_PER];
   TileLoader<D, kFwdKeys, 4> tl;
   if constexpr (!SPLIT) tl.init(static_cast<int>(ks * sizeof(T)), wave, lane);
-  const T* Kend = static_cast<const T*>(a.k) + a.n_tokens * ks;
-  const T* Vend = static_cast<const T*>(a.v) + a.n_tokens * ks;
   auto issue = [&](int kt, int buf) {
     if constexpr (!SPLIT) {
-      tl.issue(k_tile(buf, 0), make_rsrc(K + static_cast<int64_t>(kt) * ks, Kend));
-      tl.issue(v_tile(buf, 0), make_rsrc(V + static_cast<int64_t>(kt) * ks, Vend));
+      const int64_t left = a.n_tokens - kt;
+      const int rows = left < kFwdKeys ? static_cast<int>(left) : kFwdKeys;
+      const uint32_t rb = static_cast<uint32_t>(ks * sizeof(T));
+      tl.issue(k_tile(buf, 0), tile_rsrc(K + static_cast<int64_t>(kt) * ks, rows, rb));
+      tl.issue(v_tile(buf, 0), tile_rsrc(V + static_cast<int64_t>(kt) * ks, rows, rb));
     } else {
       constexpr int CPR = D / 4;
 #pragma unroll

@@ -246,6 +246,15 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, const void* end) {
                                            static_cast<int>(r), kRsrcFlags);
 }
 
+// Raw buffer resource over `rows` rows of `row_bytes` bytes from `base`: a
+// tile of at most a few hundred rows, whose byte count fits 32 bits, so no
+// 64-bit clamp is needed.  Lanes past the last row read zeros.
+__device__ __forceinline__ rsrc_t tile_rsrc(const void* base, int rows, uint32_t row_bytes) {
+  const uint32_t n = rows > 0 ? static_cast<uint32_t>(rows) * row_bytes : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(n), kRsrcFlags);
+}
+
 // Buffer loads straight to LDS (MUBUF with the lds bit): lane l writes its
 // SIZE bytes to LDS address M0 + SIZE * l.  They are issued from inline
 // assembly on purpose.  The compiler cannot relate a direct-to-LDS load to a
@@ -312,9 +321,52 @@ struct TileLoader {
     }
     lds0 = wave * PER * 1024;
   }
+  // The wave's PER loads go out in one assembly block: the hazard padding
+  // and the M0 save / restore are paid once, and M0 steps 1 KiB (one wave's
+  // 64 x 16 bytes) between loads, with the one wait state an M0 write needs
+  // before an LDS DMA.
   __device__ __forceinline__ void issue(LDS_PTR(char) tile, rsrc_t rs) const {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) dma_to_lds<16>(tile + lds0 + j * 1024, voff[j], rs);
+    static_assert(PER == 1 || PER == 2 || PER == 4, "one, two or four loads per wave");
+    const unsigned m0v = __builtin_amdgcn_readfirstlane(
+        static_cast<unsigned>(reinterpret_cast<__SIZE_TYPE__>(tile + lds0)));
+    unsigned saved;
+    if constexpr (PER == 1) {
+      dma_to_lds<16>(tile + lds0, voff[0], rs);
+    } else if constexpr (PER == 2) {
+      asm volatile(
+          "s_nop 4\n\t"
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
+          "s_add_u32 m0, m0, 0x400\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %3, %4, 0 offen lds\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(m0v), "v"(voff[0]), "v"(voff[1]), "s"(rs)
+          : "memory", "scc");
+    } else {
+      asm volatile(
+          "s_nop 4\n\t"
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
+          "s_add_u32 m0, m0, 0x400\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %3, %6, 0 offen lds\n\t"
+          "s_add_u32 m0, m0, 0x400\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %4, %6, 0 offen lds\n\t"
+          "s_add_u32 m0, m0, 0x400\n\t"
+          "s_nop 0\n\t"
+          "buffer_load_dwordx4 %5, %6, 0 offen lds\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(m0v), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs)
+          : "memory", "scc");
+    }
   }
 };
 
