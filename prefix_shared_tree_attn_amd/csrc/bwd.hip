@@ -390,8 +390,8 @@ struct DkdvPipeCfg {
   static constexpr int NL_OFF = 2 * TILE;        // -LSE log2 e (64 floats, 32 used)
   static constexpr int ND_OFF = 2 * TILE + 256;  // -D (64 floats, 32 used)
   static constexpr int BUF = 2 * TILE + 512;
-  static constexpr int BYTES = NB * BUF;
-  static constexpr int PER = ROWS * (D / 8) / 256;  // 16-byte chunks per thread and tile
+  static constexpr int SPARE_OFF = NB * BUF;     // target of the extra row-term loads
+  static constexpr int BYTES = NB * BUF + 256;
 };
 
 namespace {
@@ -539,58 +539,31 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
     for (int i = tid; i < BUF / 16; i += 256) lds_write16(lds + (NB - 1) * BUF, 16 * i, z);
   }
 
-  // Loads of one step into registers: C::PER 16-byte chunks of Q and of dO
-  // per thread, and for waves 0 / 1 one -LSE log2 e / -D row term per lane.
-  // Thread t fills LDS slots t, t + 256, ... of a tile in address order (no
-  // bank conflicts) and fetches the chunk the tile layout puts there.
+  // Loads of one step go straight from memory into a ring buffer (see
+  // TileLoader): C::PER 16-byte chunks of Q and of dO per thread, and one
+  // row term per lane -- -LSE log2 e for wave 0, -D for wave 1; waves 2 and 3
+  // repeat wave 0's load into a spare slot, so that every wave issues the
+  // same number of loads per step and can count them in its waits.
   // Resources end at the step's last row, so rows past a query range, and
-  // steps past the end (empty resources), load zeros.
-  constexpr int PER = C::PER;
-  int voff[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int slot16 = tid + 256 * i;
-    const int sub = slot16 / 128, rem = slot16 % 128, r = rem >> 2;
-    const int c = sub * 4 + ((rem & 3) ^ QT::swz(r));
-    voff[i] = r * static_cast<int>(qs * 2) + c * 16;
-  }
-  i32x4 qreg[PER], dreg[PER];
-  int treg = 0;
+  // steps past the end (empty resources), read as zeros.
+  TileLoader<D, 32, 4> tl;
   const char* rterm =
       reinterpret_cast<const char*>(wave == 1 ? a.neg_d : a.neg_lse2);
   const int rterm_off = wave == 1 ? C::ND_OFF : C::NL_OFF;
   // A step covers at most 32 rows, so its byte counts fit 32 bits.
   const int64_t row_bytes = qs * 2, head_bytes = D * 2;
   const uint32_t row_bytes32 = static_cast<uint32_t>(row_bytes);
+  tl.init(static_cast<int>(row_bytes32), wave, lane);
   const char* Qb = reinterpret_cast<const char*>(Qall);
   const char* dOb = reinterpret_cast<const char*>(dOall);
-  auto issue = [&](const LoadStep& l) __attribute__((always_inline)) {
+  auto issue = [&](const LoadStep& l, int boff) __attribute__((always_inline)) {
     const int rows = l.s.e < ee ? (l.s.qe - l.s.r0 < 32 ? l.s.qe - l.s.r0 : 32) : 0;
-    const uint32_t nb = static_cast<uint32_t>(rows) * row_bytes32;
-    const rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(l.q), static_cast<short>(0),
-                                                        static_cast<int>(nb), kRsrcFlags);
-    const rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(l.d), static_cast<short>(0),
-                                                        static_cast<int>(nb), kRsrcFlags);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      qreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff[i], 0, 0);
-      dreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rd, voff[i], 0, 0);
-    }
-    if (wave < 2) {
-      const rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<char*>(l.t), static_cast<short>(0), 4 * rows, kRsrcFlags);
-      treg = __builtin_amdgcn_raw_buffer_load_b32(rr, 4 * lane, 0, 0);
-    }
+    tl.issue(lds + boff + C::Q_OFF, tile_rsrc(l.q, rows, row_bytes32));
+    tl.issue(lds + boff + C::DO_OFF, tile_rsrc(l.d, rows, row_bytes32));
+    dma_to_lds<4>(wave < 2 ? lds + boff + rterm_off : lds + C::SPARE_OFF, 4 * lane,
+                  tile_rsrc(l.t, rows, 4));
   };
-  auto commit = [&](int boff) __attribute__((always_inline)) {
-    LDS_PTR(char) b = lds + boff;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      lds_write16(b + C::Q_OFF, 16 * (tid + 256 * i), qreg[i]);
-      lds_write16(b + C::DO_OFF, 16 * (tid + 256 * i), dreg[i]);
-    }
-    if (wave < 2) *reinterpret_cast<LDS_PTR(int)>(b + rterm_off + 4 * lane) = treg;
-  };
+  constexpr int LPS = 2 * TileLoader<D, 32, 4>::PER + 1;  // loads per wave and step
 
   // this wave's K / V operands (B operands of S = Q K^T and dP = dO V^T)
   bf16x8 kf[KC], vf[KC];
@@ -732,14 +705,13 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   Step cur = ld.s;  // step j
   Step nx = cur;
   step_next(nx, ee, a.entries);  // step j + 1
-  issue(ld);  // steps 0 and 1 straight into their buffers
+  issue(ld, 0);  // steps 0, 1 and 2 (zeros where there is none)
   ld_next();
-  commit(0);
-  issue(ld);
+  issue(ld, BUF);
   ld_next();
-  commit(BUF);
-  issue(ld);  // step 2 (zeros where there is none)
+  issue(ld, 2 * BUF);
   ld_next();
+  wait_vmcnt<LPS>();  // steps 0 and 1 are in
   // ring buffers as byte offsets: previous, current and next step
   int bp = (NB - 1) * BUF, bc = 0, bn = BUF;
   __syncthreads();
@@ -757,18 +729,16 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
     for (int i = NC; i < NS; ++i) mfma_slot(i, fetch(i, b0, b0));
   }
 
-  int bw = 2 * BUF;  // buffer of step j + 2
-  bool even = true;
+  int bw = 3 * BUF;  // buffer of step j + 3
   while (true) {
     const bool more = nx.e < ee;
-    // write step j + 2 and load step j + 3; even iterations pass the barrier
-    // after the write, odd ones need none (everything they read was written
-    // before the barrier of the iteration before)
-    commit(bw);
+    // Step j + 1 (loaded during iteration j - 2) must be in for every wave,
+    // and every wave past iteration j - 1, whose previous-step buffer is the
+    // one step j + 3 now goes to.
+    wait_vmcnt<LPS>();
+    __syncthreads();
+    issue(ld, bw);
     bw = nexto(bw);
-    if (even) __syncthreads();
-    even = !even;
-    issue(ld);
     ld_next();
     const int delta = cur.r0 - wk0;
     const bool masked = cur.causal && delta < 32;
@@ -780,6 +750,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
     bn = nexto(bn);
     if (!more) break;
   }
+  wait_vmcnt<0>();  // no load may land in LDS after the workgroup has left
   // C of the last step (its buffer is bp now)
   {
     LDS_PTR(char) bl = lds + bp;

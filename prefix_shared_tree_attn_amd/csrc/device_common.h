@@ -374,6 +374,15 @@ struct TileLoader {
 // loads, stores, atomics) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Waits until at most N vector memory loads of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Stores four consecutive fp32 values as output elements.
 __device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
   bf16x4 x;
