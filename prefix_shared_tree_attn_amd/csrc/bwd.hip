@@ -16,7 +16,7 @@
 //     per 32-row sub-block it recomputes P = exp(S - LSE) from the saved LSE,
 //     forms dP = dO V^T and dS = P (dP - D), and accumulates dV += P^T dO and
 //     dK += dS^T Q with dO and Q read as transposed operands.  Query rows of
-//     the next step stream into a second LDS buffer meanwhile.  Key tiles
+//     the following steps stream into LDS buffers meanwhile.  Key tiles
 //     whose descendant work was split for load balance write fp32 partial
 //     slots instead of the outputs;
 //  3. dQ, one workgroup per query tile and head, walking the tile's ancestor
@@ -366,13 +366,14 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 // and dS = P (dP - D); and C(j), the updates dV += P^T dO and dK += dS^T Q.
 // Iteration j issues C(j-1) and A(j+1) on the matrix cores while the vector
 // ALUs run B(j), so the element-wise work of a wave hides under its own
-// MFMAs.  Q, dO and the row terms stream through registers into a ring of
-// six LDS buffers: iteration j writes step j + 2 (loaded during iteration
-// j - 1) and issues the loads of step j + 3; only even iterations pass a
-// barrier, and the ring is deep enough that no write can reach a buffer a
-// lagging wave still reads.  Loads go through registers rather than
-// straight to LDS: the compiler cannot tell a direct-to-LDS load from the
-// transposed LDS reads and would drain every prefetch before them.
+// MFMAs.  Q, dO and the row terms go from memory straight into a ring of
+// six LDS buffers (inline-asm LDS DMA, which the compiler's wait analysis
+// does not see; the kernel counts its own loads): iteration j waits for
+// step j + 1, passes a barrier and issues the loads of step j + 3, so each
+// step has two iterations to arrive.  Iteration j reads the buffers of steps
+// j - 1, j and j + 1; the barrier makes sure no wave still reads the buffer
+// of step j - 3 that the new loads overwrite.  The S and dP MFMAs are inline
+// asm as well, to keep their results out of the accumulation registers.
 //
 // No branch masks anything inside the loop:
 //  * rows past a query range read as zeros (each buffer resource ends at the
