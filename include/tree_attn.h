@@ -267,7 +267,8 @@ typedef struct {
   int64_t fwd_tiles;        /* query tiles (per head)                       */
   int64_t fwd_ranges;       /* key ranges over all query tiles              */
   int64_t fwd_blocks;       /* workgroups of one forward launch             */
-  int64_t bwd_items;        /* key-tile work items (incl. split chunks)     */
+  int64_t bwd_items;        /* key-tile work items (incl. split chunks and
+                               empty items that pad the launch order)     */
   int64_t bwd_entries;      /* (head, query range) entries over all items   */
   int64_t bwd_split_tiles;  /* key tiles whose work was split               */
   int64_t bwd_slots;        /* fp32 partial dK/dV slots                     */
@@ -286,7 +287,13 @@ tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_st
  *   fwd_tiles  [fwd_tiles, 4]  : q0, q1, range_begin, range_end
  *   fwd_ranges [fwd_ranges, 4] : k0, k1, causal, 0
  *   bwd_items  [bwd_items, 8]  : k0, k1, kv_head, entry_begin, entry_end,
- *                                slot (-1 = writes dK/dV directly), 0, 0
+ *                                slot (-1 = writes dK/dV directly), XCD the
+ *                                item is placed on (-1 for an empty item),
+ *                                0.  Item b is launched as workgroup b, which
+ *                                the hardware sends to XCD b % 8; items that
+ *                                read the same query rows share an XCD, and
+ *                                empty items (entry_begin == entry_end) fill
+ *                                out the per-XCD queues.
  *   bwd_entries[bwd_entries, 4]: q_head, q0, q1, causal
  * A causal range applies the mask key <= query; a query sees a key in a
  * non-causal range unconditionally (range rows are ancestors/descendants).

@@ -123,6 +123,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
   const I8 it = load_plan8(a.items, blockIdx.x);
   const int k0 = it.v[0], k1 = it.v[1], g = it.v[2], eb = it.v[3], ee = it.v[4];
   const int slot = it.v[5];
+  if (eb >= ee) return;  // an empty item that pads the launch order
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
@@ -505,6 +506,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   const I8 it = load_plan8(a.items, blockIdx.x);
   const int k0 = it.v[0], k1 = it.v[1], g = it.v[2], eb = it.v[3], ee = it.v[4];
   const int slot = it.v[5];
+  if (eb >= ee) return;  // an empty item that pads the launch order
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;

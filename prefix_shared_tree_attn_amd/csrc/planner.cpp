@@ -5,8 +5,10 @@
 #include "planner.h"
 
 #include <algorithm>
+#include <map>
 #include <numeric>
 #include <sstream>
+#include <tuple>
 
 namespace tree_attn {
 namespace {
@@ -187,11 +189,12 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
     int64_t k0, k1, g, slot;
     std::vector<I4> entries;
     int64_t cost;
+    int64_t node, chunk;  // tree node of the key tile, chunk of a split tile
   };
   std::vector<BItem> items;
   int64_t total_cost = 0;
   struct KTile {
-    int64_t k0, k1;
+    int64_t k0, k1, node;
     std::vector<Range> causal, full;  // query ranges
     int64_t rows;
   };
@@ -200,6 +203,7 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
     const int64_t s = seg_start[i], e = s + seg_len[i];
     for (int64_t k0 = s; k0 < e; k0 += kBwdKeys) {
       KTile kt;
+      kt.node = i;
       kt.k0 = k0;
       kt.k1 = std::min<int64_t>(e, k0 + kBwdKeys);
       // own node from the tile's first row on (causal), merged with the
@@ -242,12 +246,13 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
       }
       const int64_t cost = kt.rows * gsize * nk;
       if (cost <= cap) {
-        items.push_back({kt.k0, kt.k1, g, -1, std::move(all), cost});
+        items.push_back({kt.k0, kt.k1, g, -1, std::move(all), cost, kt.node, 0});
         continue;
       }
       // chunk the entries (rows cut at kBwdRows boundaries of each entry)
       const int64_t slot_begin = slots;
-      BItem cur{kt.k0, kt.k1, g, slots, {}, 0};
+      int64_t chunk = 0;
+      BItem cur{kt.k0, kt.k1, g, slots, {}, 0, kt.node, chunk};
       for (const I4& en : all) {
         int64_t q0 = en.y;
         while (q0 < en.z) {
@@ -260,7 +265,7 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
           if (cur.cost >= cap) {
             items.push_back(std::move(cur));
             ++slots;
-            cur = BItem{kt.k0, kt.k1, g, slots, {}, 0};
+            cur = BItem{kt.k0, kt.k1, g, slots, {}, 0, kt.node, ++chunk};
           }
         }
       }
@@ -275,15 +280,95 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
     }
   }
   p.bwd_slots = slots;
-  std::stable_sort(items.begin(), items.end(),
-                   [](const BItem& a, const BItem& b) { return a.cost > b.cost; });
-  for (auto& it : items) {
-    const int32_t eb = static_cast<int32_t>(p.bwd_entries.size());
-    p.bwd_entries.insert(p.bwd_entries.end(), it.entries.begin(), it.entries.end());
-    p.bwd_items.push_back({{static_cast<int32_t>(it.k0), static_cast<int32_t>(it.k1),
-                            static_cast<int32_t>(it.g), eb,
-                            static_cast<int32_t>(p.bwd_entries.size()),
-                            static_cast<int32_t>(it.slot), 0, 0}});
+
+  // Placement.  The key tiles of one node (and, for split tiles, the same
+  // chunk of each) read the same query rows of the same heads: a group.
+  // Workgroup b is dispatched to XCD b % 8 and each XCD takes its workgroups
+  // in order, so
+  //  * each group goes whole to one XCD, groups longest first onto the XCD
+  //    with the least work so far, and its re-reads of the rows can hit
+  //    that XCD's L2;
+  //  * an XCD takes its groups eight at a time and interleaves them by rank
+  //    (the largest item of each, then the second largest, ...): a few items
+  //    of a group run side by side, not all at once on the same rows;
+  //  * the last 40% of an XCD's work is ordered longest first, so that it
+  //    ends on short items;
+  // and the queues are interleaved into the launch order, with empty items
+  // (no entries) filling the ends of the shorter queues.
+  std::map<std::tuple<int64_t, int64_t, int64_t>, std::vector<int64_t>> groups;
+  for (int64_t ii = 0; ii < static_cast<int64_t>(items.size()); ++ii) {
+    const BItem& it = items[ii];
+    groups[{it.node, it.g, it.chunk}].push_back(ii);
+  }
+  struct Group {
+    int64_t cost;
+    std::vector<int64_t> members;
+  };
+  std::vector<Group> glist;
+  for (auto& kv : groups) {
+    Group gr{0, std::move(kv.second)};
+    for (int64_t ii : gr.members) gr.cost += items[ii].cost;
+    std::stable_sort(gr.members.begin(), gr.members.end(),
+                     [&](int64_t a, int64_t b) { return items[a].cost > items[b].cost; });
+    glist.push_back(std::move(gr));
+  }
+  std::stable_sort(glist.begin(), glist.end(),
+                   [](const Group& a, const Group& b) { return a.cost > b.cost; });
+  constexpr size_t kBatch = 8;          // groups interleaved together on an XCD
+  constexpr int64_t kTailPercent = 40;  // share of an XCD's work sorted longest first
+  std::vector<int64_t> qg[kXcds];
+  int64_t load[kXcds] = {};
+  for (int64_t gi = 0; gi < static_cast<int64_t>(glist.size()); ++gi) {
+    int x = 0;
+    for (int y = 1; y < kXcds; ++y)
+      if (load[y] < load[x]) x = y;
+    load[x] += glist[gi].cost;
+    qg[x].push_back(gi);
+  }
+  std::vector<int64_t> queue[kXcds];
+  for (int x = 0; x < kXcds; ++x) {
+    for (size_t b0 = 0; b0 < qg[x].size(); b0 += kBatch) {
+      const size_t b1 = std::min(qg[x].size(), b0 + kBatch);
+      for (size_t r = 0;; ++r) {
+        bool any = false;
+        for (size_t b = b0; b < b1; ++b) {
+          const auto& mem = glist[qg[x][b]].members;
+          if (r < mem.size()) {
+            queue[x].push_back(mem[r]);
+            any = true;
+          }
+        }
+        if (!any) break;
+      }
+    }
+    int64_t acc = 0;
+    size_t cut = queue[x].size();
+    for (size_t q = 0; q < queue[x].size(); ++q) {
+      acc += items[queue[x][q]].cost;
+      if (acc * 100 >= load[x] * (100 - kTailPercent)) {
+        cut = q + 1;
+        break;
+      }
+    }
+    std::stable_sort(queue[x].begin() + cut, queue[x].end(),
+                     [&](int64_t a, int64_t b) { return items[a].cost > items[b].cost; });
+  }
+  size_t qlen = 0;
+  for (int x = 0; x < kXcds; ++x) qlen = std::max(qlen, queue[x].size());
+  for (size_t q = 0; q < qlen; ++q) {
+    for (int x = 0; x < kXcds; ++x) {
+      const int32_t eb = static_cast<int32_t>(p.bwd_entries.size());
+      if (q >= queue[x].size()) {
+        p.bwd_items.push_back({{0, 0, 0, eb, eb, -1, -1, 0}});
+        continue;
+      }
+      const BItem& it = items[queue[x][q]];
+      p.bwd_entries.insert(p.bwd_entries.end(), it.entries.begin(), it.entries.end());
+      p.bwd_items.push_back({{static_cast<int32_t>(it.k0), static_cast<int32_t>(it.k1),
+                              static_cast<int32_t>(it.g), eb,
+                              static_cast<int32_t>(p.bwd_entries.size()),
+                              static_cast<int32_t>(it.slot), x, 0}});
+    }
   }
   return Status::kOk;
 }

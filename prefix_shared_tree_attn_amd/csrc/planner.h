@@ -56,9 +56,10 @@ struct HostPlan {
   int64_t fwd_groups = 0;  // tiles * hkv
   int64_t fwd_blocks = 0;  // launch size (padded to whole XCD rounds) * group size
 
-  // backward: items (k0, k1, kv_head, entry_begin, entry_end, slot, 0, 0)
-  // longest first; entries (q_head, q0, q1, causal); reductions of split key
-  // tiles (k0, k1, kv_head, slot_begin, num_slots, 0, 0, 0)
+  // backward: items (k0, k1, kv_head, entry_begin, entry_end, slot, xcd, 0)
+  // in launch order (item b runs on XCD b % 8; empty items pad the per-XCD
+  // queues); entries (q_head, q0, q1, causal); reductions of split key tiles
+  // (k0, k1, kv_head, slot_begin, num_slots, 0, 0, 0)
   std::vector<I8> bwd_items;
   std::vector<I4> bwd_entries;
   std::vector<I8> bwd_reduce;

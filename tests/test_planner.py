@@ -131,17 +131,33 @@ def test_forward_block_mapping_covers_tiles_and_heads_once():
         assert set(seen.values()) == {1}
 
 
-def test_items_longest_first_and_split_heavy_tiles():
+def test_item_placement_and_split_heavy_tiles():
     t = config_tree(2)  # star: the prompt's key tiles are seen by every response
     p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, 32, 8, 128)
     ex = p.export()
     st = p.stats()
     assert st["bwd_split_tiles"] > 0 and st["bwd_slots"] > 0
-    costs = []
-    for it in ex["bwd_items"]:
-        rows = (ex["bwd_entries"][it[3]:it[4], 2] - ex["bwd_entries"][it[3]:it[4], 1]).sum()
-        costs.append(int(rows) * int(it[1] - it[0]))
-    assert all(a >= b for a, b in zip(costs, costs[1:]))
+    items, ent = ex["bwd_items"], ex["bwd_entries"]
+    load = np.zeros(8)
+    queues = [[] for _ in range(8)]
+    for b, it in enumerate(items):
+        if it[3] == it[4]:  # padding: no work, no slot
+            assert it[5] == -1 and it[6] == -1
+            continue
+        assert it[6] == b % 8  # workgroup b runs on XCD b % 8
+        rows = int((ent[it[3]:it[4], 2] - ent[it[3]:it[4], 1]).sum())
+        load[b % 8] += rows * int(it[1] - it[0])
+        queues[b % 8].append(it)
+    assert load.max() <= 1.05 * load.mean()
+    # the key tiles of one response node and kv head read the same rows: they
+    # all sit on one XCD
+    prompt = int(t.seg_len[0])
+    where = {}
+    for x, q in enumerate(queues):
+        for it in q:
+            if it[0] >= prompt:
+                where.setdefault((int((it[0] - prompt) // 2048), int(it[2])), set()).add(x)
+    assert len(where) == 16 * 8 and all(len(xs) == 1 for xs in where.values())
     fcost = []
     for q0, q1, rb, re_ in ex["fwd_tiles"]:
         keys = sum(int(k1 - k0) for k0, k1, _, _ in ex["fwd_ranges"][rb:re_])
