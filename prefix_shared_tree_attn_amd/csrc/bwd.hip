@@ -488,6 +488,29 @@ __device__ __forceinline__ void mfma_v_last(f32x16& d, const bf16x8& a, const bf
                : "v"(a), "v"(b));
 }
 
+// Waits until at most n LDS (and scalar memory) operations of this wave are
+// outstanding.  n must fold to a constant once the caller is unrolled; the
+// switch turns it into the immediate the instruction needs (gfx9 s_waitcnt:
+// lgkmcnt in bits 11:8, vmcnt and expcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_lgkm_c() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+}
+__device__ __forceinline__ void wait_lgkm(int n) {
+  switch (n) {
+    case 0: wait_lgkm_c<0>(); break;
+    case 1: wait_lgkm_c<1>(); break;
+    case 2: wait_lgkm_c<2>(); break;
+    case 3: wait_lgkm_c<3>(); break;
+    case 4: wait_lgkm_c<4>(); break;
+    case 5: wait_lgkm_c<5>(); break;
+    case 6: wait_lgkm_c<6>(); break;
+    case 7: wait_lgkm_c<7>(); break;
+    default: wait_lgkm_c<8>(); break;
+  }
+}
+
 // Empty asm use: the value must be computed before this point, which keeps
 // the compiler from sinking element-wise work out of its MFMA slot.
 __device__ __forceinline__ void keep(float x) { asm volatile("" ::"v"(x)); }
@@ -596,7 +619,16 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   // i and dK for odd i), then S and dP of the next step (slot NC + 2 kc for S,
   // NC + 2 kc + 1 for dP).
   constexpr int NC = 4 * DB, NS = NC + 2 * KC;
-  constexpr int LA = 3;  // operands are read this many slots ahead
+  constexpr int LA = 4;  // operands are read this many slots ahead
+  // LDS reads issued after operand i + 1 once slot i has issued its own read
+  // ahead (a transposed operand takes two reads).  Even slots wait for their
+  // operand and the next one together: one s_waitcnt per two MFMAs, each an
+  // issue slot of the only wave on the SIMD.
+  auto younger = [&](int i) constexpr {
+    int n = 0;
+    for (int j = i + 2; j <= i + LA && j < NS; ++j) n += j < NC ? 2 : 1;
+    return n;
+  };
   auto fetch = [&](int i, LDS_PTR(char) bprev, LDS_PTR(char) bnext)
                    __attribute__((always_inline)) -> bf16x8 {
     if (i < NC) {
@@ -663,6 +695,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
     for (int i = 0; i < NC; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       op[i + LA] = fetch(i + LA, bprev, bnext);
+      if ((i & 1) == 0) wait_lgkm(younger(i));
       mfma_slot(i, op[i]);
 #pragma unroll
       for (int e = EC * i; e < EC * (i + 1); ++e) {
@@ -684,6 +717,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
     for (int i = NC; i < NS; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       if (i + LA < NS) op[i + LA] = fetch(i + LA, bprev, bnext);
+      if (((i - NC) & 1) == 0) wait_lgkm(younger(i));
       mfma_slot(i, op[i]);
 #pragma unroll
       for (int e = EA * (i - NC); e < EA * (i - NC + 1); ++e) {
