@@ -488,6 +488,62 @@ __device__ __forceinline__ void mfma_v_last(f32x16& d, const bf16x8& a, const bf
                : "v"(a), "v"(b));
 }
 
+// The LDS-DMA loads of one query step of the pipelined kernel in one
+// assembly block (see TileLoader for the lane layout): PER loads of the Q
+// tile from M0 = mq on, in 1 KiB steps, the same for dO at DSTEP bytes past
+// the last Q load, and one row-term dword per lane to M0 = mt.  One hazard
+// pad (an SGPR written by a VALU op needs five wait states before a vector
+// memory op reads it), one M0 save / restore, and the one wait state an
+// LDS DMA needs after each M0 write.
+template <int PER, int DSTEP>
+__device__ __forceinline__ void step_loads(unsigned mq, unsigned mt, const int (&voff)[PER],
+                                           int vt, rsrc_t rq, rsrc_t rd, rsrc_t rt) {
+  static_assert(PER == 1 || PER == 2, "one or two loads per wave and tile");
+  unsigned saved;
+  if constexpr (PER == 2) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %3, %6, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %4, %6, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, %9\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %3, %7, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %4, %7, 0 offen lds\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %5, %8, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(mq), "s"(mt), "v"(voff[0]), "v"(voff[1]), "v"(vt), "s"(rq), "s"(rd), "s"(rt),
+          "i"(DSTEP)
+        : "memory", "scc");
+  } else {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, %8\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %3, %6, 0 offen lds\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %4, %7, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(mq), "s"(mt), "v"(voff[0]), "v"(vt), "s"(rq), "s"(rd), "s"(rt), "i"(DSTEP)
+        : "memory", "scc");
+  }
+}
+
 // Waits until at most n LDS (and scalar memory) operations of this wave are
 // outstanding.  n must fold to a constant once the caller is unrolled; the
 // switch turns it into the immediate the instruction needs (gfx9 s_waitcnt:
@@ -582,14 +638,20 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   tl.init(static_cast<int>(row_bytes32), wave, lane);
   const char* Qb = reinterpret_cast<const char*>(Qall);
   const char* dOb = reinterpret_cast<const char*>(dOall);
+  constexpr int TPER = TileLoader<D, 32, 4>::PER;
+  constexpr int LPS = 2 * TPER + 1;  // loads per wave and step
+  auto lds_addr = [&](LDS_PTR(char) p) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(
+        static_cast<unsigned>(reinterpret_cast<__SIZE_TYPE__>(p)));
+  };
   auto issue = [&](const LoadStep& l, int boff) __attribute__((always_inline)) {
     const int rows = l.s.e < ee ? (l.s.qe - l.s.r0 < 32 ? l.s.qe - l.s.r0 : 32) : 0;
-    tl.issue(lds + boff + C::Q_OFF, tile_rsrc(l.q, rows, row_bytes32));
-    tl.issue(lds + boff + C::DO_OFF, tile_rsrc(l.d, rows, row_bytes32));
-    dma_to_lds<4>(wave < 2 ? lds + boff + rterm_off : lds + C::SPARE_OFF, 4 * lane,
-                  tile_rsrc(l.t, rows, 4));
+    step_loads<TPER, C::TILE - (TPER - 1) * 1024>(
+        lds_addr(lds + boff + C::Q_OFF + tl.lds0),
+        lds_addr(wave < 2 ? lds + boff + rterm_off : lds + C::SPARE_OFF), tl.voff, 4 * lane,
+        tile_rsrc(l.q, rows, row_bytes32), tile_rsrc(l.d, rows, row_bytes32),
+        tile_rsrc(l.t, rows, 4));
   };
-  constexpr int LPS = 2 * TileLoader<D, 32, 4>::PER + 1;  // loads per wave and step
 
   // this wave's K / V operands (B operands of S = Q K^T and dP = dO V^T)
   bf16x8 kf[KC], vf[KC];
@@ -748,7 +810,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   ld_next();
   issue(ld, 2 * BUF);
   ld_next();
-  wait_vmcnt<LPS>();  // steps 0 and 1 are in
+  wait_vmcnt<2 * LPS>();  // step 0 is in
   // ring buffers as byte offsets: previous, current and next step
   int bp = (NB - 1) * BUF, bc = 0, bn = BUF;
   __syncthreads();
@@ -767,16 +829,24 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   }
 
   int bw = 3 * BUF;  // buffer of step j + 3
+  bool even = true;
   while (true) {
     const bool more = nx.e < ee;
-    // Step j + 1 (loaded during iteration j - 2) must be in for every wave,
-    // and every wave past iteration j - 1, whose previous-step buffer is the
-    // one step j + 3 now goes to.
-    wait_vmcnt<LPS>();
-    __syncthreads();
-    issue(ld, bw);
-    bw = nexto(bw);
-    ld_next();
+    // Even iterations: steps j + 1 and j + 2 (loaded during iteration j - 2)
+    // must be in for every wave, and every wave past iteration j - 1; then
+    // steps j + 3 and j + 4 go to the buffers of steps j - 3 and j - 2.
+    // Iterations j and j + 1 read only the buffers of steps j - 1 .. j + 2.
+    if (even) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      issue(ld, bw);
+      bw = nexto(bw);
+      ld_next();
+      issue(ld, bw);
+      bw = nexto(bw);
+      ld_next();
+    }
+    even = !even;
     const int delta = cur.r0 - wk0;
     const bool masked = cur.causal && delta < 32;
     cur = nx;
