@@ -369,11 +369,12 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 // ALUs run B(j), so the element-wise work of a wave hides under its own
 // MFMAs.  Q, dO and the row terms go from memory straight into a ring of
 // six LDS buffers (inline-asm LDS DMA, which the compiler's wait analysis
-// does not see; the kernel counts its own loads): iteration j waits for
-// step j + 1, passes a barrier and issues the loads of step j + 3, so each
-// step has two iterations to arrive.  Iteration j reads the buffers of steps
-// j - 1, j and j + 1; the barrier makes sure no wave still reads the buffer
-// of step j - 3 that the new loads overwrite.  The S and dP MFMAs are inline
+// does not see; the kernel counts its own loads): every other iteration j
+// waits for steps j + 1 and j + 2, passes a barrier and issues the loads of
+// steps j + 3 and j + 4, so each step has two iterations to arrive.
+// Iterations j and j + 1 read the buffers of steps j - 1 .. j + 2; the
+// barrier makes sure no wave still reads the buffers of steps j - 3 and
+// j - 2 that the new loads overwrite.  The S and dP MFMAs are inline
 // asm as well, to keep their results out of the accumulation registers.
 //
 // No branch masks anything inside the loop:
