@@ -1043,21 +1043,27 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
           pacc[kb][v] = 0.f;
         }
         const int krow = 32 * kb + swap23(l32);
-        // two half-batches of row operands (K, then V) to bound registers
+        // row operands (K, then V) in four batches of KC / 2 fragments: the
+        // smallest batches that keep the kernel within 256 VGPRs without
+        // spilling
+        constexpr int HB = KC / 2;
 #pragma unroll
-        for (int kv = 0; kv < 2; ++kv) {
-          Frag<SPLIT> fr[KC];
+        for (int part = 0; part < 4; ++part) {
+          const int kv = part >> 1, kc0 = (part & 1) * HB;
+          Frag<SPLIT> fr[HB];
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            fr[kc].h = row_operand<KT>(kv ? v_tile(buf, 0) : k_tile(buf, 0), krow, 2 * kc + half);
+          for (int kc = 0; kc < HB; ++kc) {
+            fr[kc].h =
+                row_operand<KT>(kv ? v_tile(buf, 0) : k_tile(buf, 0), krow, 2 * (kc0 + kc) + half);
             if constexpr (SPLIT)
-              fr[kc].l = row_operand<KT>(kv ? v_tile(buf, 1) : k_tile(buf, 1), krow, 2 * kc + half);
+              fr[kc].l = row_operand<KT>(kv ? v_tile(buf, 1) : k_tile(buf, 1), krow,
+                                         2 * (kc0 + kc) + half);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            if (kv) mma<SPLIT>(pacc[kb], fr[kc], df[kc]);
-            else mma<SPLIT>(sacc[kb], fr[kc], qf[kc]);
+          for (int kc = 0; kc < HB; ++kc) {
+            if (kv) mma<SPLIT>(pacc[kb], fr[kc], df[kc0 + kc]);
+            else mma<SPLIT>(sacc[kb], fr[kc], qf[kc0 + kc]);
           }
         }
       }
