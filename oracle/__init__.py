@@ -5,7 +5,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 shares no code with the HIP library: both consume the seeded inputs of
 ``tree_inputs`` and nothing else.
 
-Parity status of each function is listed in ``oracle/path_expansion.py``.
+Parity status of each function is listed in ``oracle/path_expansion.py``
+(softmax tree attention), ``oracle/linear_attention.py`` (linear attention
+over the tree) and ``oracle/prefix_tree.py``.
 """
 
 from .path_expansion import (  # noqa: F401
@@ -16,5 +18,9 @@ from .path_expansion import (  # noqa: F401
     tree_attention,
     query_rows,
     key_rows,
+)
+from .linear_attention import (  # noqa: F401,E402
+    causal_linear_attention,
+    tree_linear_attention,
 )
 from . import prefix_tree  # noqa: F401,E402
