@@ -276,6 +276,9 @@ typedef struct {
   int64_t fwd_tile_keys;    /* keys per forward key step                    */
   int64_t bwd_tile_keys;    /* keys per backward key tile                   */
   int64_t bwd_block_rows;   /* query rows per backward step                 */
+  int64_t lin_pieces;       /* linear attention: pieces                     */
+  int64_t lin_succ;         /* linear attention: successor entries          */
+  int64_t lin_chunk;        /* linear attention: chunk (trajectory depth)   */
 } tree_attn_plan_stats_t;
 
 tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_stats_t* out);
@@ -303,6 +306,57 @@ tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_til
                                          int32_t* bwd_entries);
 
 /*
+ * Chunkwise causal linear attention over the same tree (HARTS, abstract:
+ * the chunkwise linear-attention layers of hybrid models run over arbitrary
+ * rollout trees in one packed call, with state handed from each prefix to its
+ * branches and gradients propagated back through those handoffs).  The pages
+ * name no gate or normaliser; the library computes the plain recurrence
+ *
+ *   O_t = scale * S_t^T q_t,   S_t = sum over s <= t on t's root-to-leaf
+ *                              path of k_s v_s^T     (D x D per kv head),
+ *
+ * i.e. O_t = scale * sum_s (q_t . k_s) v_s, query head h reading kv head
+ * h / G, with the results of running each trajectory separately and each
+ * shared prefix computed once.  The loss is sum_t <dO_t, O_t> over unique
+ * tokens: dQ, dK, dV are its gradients, dK / dV of a shared token summed over
+ * every branch that sees it.
+ *
+ * Chunking: each node is cut where the trajectory depth (ancestor tokens +
+ * offset) is a multiple of 64, so every state the kernels materialise is a
+ * trajectory chunk-boundary state or a branch-point state; a chunk that
+ * straddles a branch point is computed as its parent part once and its child
+ * parts once each (no replay).  The states live in the caller's workspace as
+ * fp32 [pieces, Hkv, D, D]; products run in bf16 on the matrix cores.
+ *
+ * Tensors: Q, O, dO, dQ [N, Hq, D] and K, V, dK, dV [N, Hkv, D], bf16 only
+ * (a plan built for fp32 gives TREE_ATTN_ERR_UNSUPPORTED); D 64 or 128.
+ * Workspace: device memory, 256-byte aligned, at least the size
+ * tree_attn_lin_workspace_size reports (2 state arrays forward, 3 backward);
+ * it holds no result between calls.  The backward pass recomputes the
+ * forward states itself, so it does not need the forward's workspace or O.
+ * Errors as for tree_attn_fwd: invalid arguments are rejected before any
+ * launch; TREE_ATTN_ERR_WORKSPACE for a missing or short workspace.
+ */
+tree_attn_status_t tree_attn_lin_workspace_size(tree_attn_plan_t plan, size_t* fwd_bytes,
+                                                size_t* bwd_bytes);
+tree_attn_status_t tree_attn_lin_fwd(tree_attn_plan_t plan, const void* q, const void* k,
+                                     const void* v, float scale, void* o, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+tree_attn_status_t tree_attn_lin_bwd(tree_attn_plan_t plan, const void* q, const void* k,
+                                     const void* v, const void* dout, float scale, void* dq,
+                                     void* dk, void* dv, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
+/*
+ * Copies the linear-attention piece table to host arrays: pieces [lin_pieces
+ * x 8] = (first token, length, predecessor piece or -1, successor begin,
+ * successor end, node, 0, 0) in root-first order, and successors [lin_succ].
+ * Either pointer may be null.
+ */
+tree_attn_status_t tree_attn_lin_plan_export(tree_attn_plan_t plan, int32_t* pieces,
+                                             int32_t* successors);
+
+/*
  * Kernel timing for benchmarks and reports.  While enabled, every kernel
  * that the device entry points launch is bracketed by HIP events on the call's stream (no
  * host synchronisation).  tree_attn_timing_read waits for the recorded
@@ -310,7 +364,10 @@ tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_til
  * duration in milliseconds since the last reset (reset != 0 clears them).
  * Kinds: 0 forward, 1 backward preprocess, 2 backward dK/dV, 3 backward
  * partial-slot reduction, 4 backward dQ, 5 positions, 6 gather, 7 scatter-sum,
- * 8 rotary embedding; 9..15 unused.  Timing is
+ * 8 rotary embedding, 9 linear-attention piece sums K^T V (forward and
+ * the backward's recomputation), 10 its state scan, 11 linear-attention
+ * output, 12 piece sums Q^T dO, 13 state-gradient scan, 14 linear-attention
+ * dQ, 15 linear-attention dK and dV (two launches).  Timing is
  * process-wide and not meant for concurrent callers.
  */
 typedef struct {

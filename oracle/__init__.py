@@ -22,5 +22,7 @@ from .path_expansion import (  # noqa: F401
 from .linear_attention import (  # noqa: F401,E402
     causal_linear_attention,
     tree_linear_attention,
+    linear_query_rows,
+    linear_key_rows,
 )
 from . import prefix_tree  # noqa: F401,E402

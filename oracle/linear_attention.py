@@ -114,3 +114,83 @@ def tree_linear_attention(q, k, v, do, parent, seg_start, seg_len,
             dk[p, g] += dkp
             dv[p, g] += dvp
     return {"o": o, "dq": dq, "dk": dk, "dv": dv, "mult": mult, "path_spread": spread}
+
+
+# --------------------------------------------------------------------------
+# sampled outputs for workloads too large for the full expansion
+
+def _ancestor_context(parent, seg_start, seg_len, row: int) -> np.ndarray:
+    """Rows that token ``row`` attends to, root first: the segments of its
+    node's proper ancestors, then its own node up to and including it."""
+    seg_start = np.asarray(seg_start, np.int64)
+    seg_len = np.asarray(seg_len, np.int64)
+    node = int(np.nonzero((seg_start <= row) & (row < seg_start + seg_len))[0][0])
+    chain = []
+    a = int(parent[node])
+    while a >= 0:
+        chain.append(a)
+        a = int(parent[a])
+    parts = [np.arange(seg_start[c], seg_start[c] + seg_len[c]) for c in reversed(chain)]
+    parts.append(np.arange(seg_start[node], row + 1))
+    return np.concatenate(parts)
+
+
+def linear_query_rows(q, k, v, do, parent, seg_start, seg_len, scale: float, rows, heads):
+    """O and dQ of selected (row, head) pairs, fp64.
+
+    A token's context (its path prefix) is the same on every path through
+    it, so one row of ``causal_linear_attention`` gives O; its dQ row sums
+    the ``mult`` path copies, each carrying dO / mult, which is the row for
+    the full dO.  Returns ``o, dq`` of shape [R, H, D].
+    """
+    hq, hkv = q.shape[1], k.shape[1]
+    gs = hq // hkv
+    o = np.empty((len(rows), len(heads), q.shape[2]))
+    dq = np.empty_like(o)
+    for ri, t in enumerate(rows):
+        ctx = _ancestor_context(parent, seg_start, seg_len, int(t))
+        for hi, h in enumerate(heads):
+            kc = np.asarray(k[ctx, h // gs], np.float64)
+            vc = np.asarray(v[ctx, h // gs], np.float64)
+            o[ri, hi] = scale * ((kc @ np.asarray(q[t, h], np.float64)) @ vc)
+            dq[ri, hi] = scale * ((vc @ np.asarray(do[t, h], np.float64)) @ kc)
+    return o, dq
+
+
+def linear_key_rows(q, k, v, do, parent, seg_start, seg_len, scale: float, keys,
+                    kv_head: int):
+    """dK and dV of selected packed key rows of one kv head, fp64.
+
+    Sums, over every path containing a selected key and every query head of
+    the kv head's group, that key's column of the per-path gradients of
+    ``causal_linear_attention`` (rows at or after the key, dO / mult per path
+    copy).  Returns ``dk, dv`` of shape [K, D].
+    """
+    n, hq = q.shape[0], q.shape[1]
+    gs = hq // k.shape[1]
+    keys = np.asarray(keys, np.int64)
+    paths = root_to_leaf_paths(parent, seg_start, seg_len)
+    inv_mult = 1.0 / path_multiplicity(paths, n).astype(np.float64)
+    d = q.shape[2]
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), d))
+    g = kv_head
+    for p in paths:
+        where = {int(t): i for i, t in enumerate(p)}
+        sel = [(ki, where[int(t)]) for ki, t in enumerate(keys) if int(t) in where]
+        if not sel:
+            continue
+        kidx = np.array([s[0] for s in sel])
+        kpos = np.array([s[1] for s in sel])
+        r0 = int(kpos.min())
+        later = np.arange(r0, len(p))[:, None] >= kpos[None, :]  # row sees key
+        ks_ = np.asarray(k[p[kpos], g], np.float64)
+        vs_ = np.asarray(v[p[kpos], g], np.float64)
+        for h in range(g * gs, (g + 1) * gs):
+            qr = np.asarray(q[p[r0:], h], np.float64)
+            dor = np.asarray(do[p[r0:], h], np.float64) * inv_mult[p[r0:]][:, None]
+            gcol = scale * (dor @ vs_.T) * later  # dL / d(q_t . k_s)
+            acol = scale * (qr @ ks_.T) * later   # A[t, s]
+            np.add.at(dk, kidx, gcol.T @ qr)
+            np.add.at(dv, kidx, acol.T @ dor)
+    return dk, dv

@@ -19,7 +19,7 @@ from ._ffi import TreeAttnError, PlanStats  # noqa: F401
 
 __all__ = ["Plan", "plan", "plan_host", "fwd", "bwd", "positions", "workspace",
            "TreeAttnError", "timing_enable", "timing_read", "PrefixTree", "build_tree",
-           "gather_rows", "scatter_sum_rows", "rope"]
+           "gather_rows", "scatter_sum_rows", "rope", "lin_fwd", "lin_bwd", "lin_workspace"]
 
 
 def _i32(a) -> np.ndarray:
@@ -68,6 +68,21 @@ class Plan:
         _ffi.check(_ffi.lib().tree_attn_workspace_size(self.handle, ctypes.byref(f),
                                                        ctypes.byref(b)), "workspace_size")
         return int(f.value), int(b.value)
+
+    def lin_workspace_size(self) -> Tuple[int, int]:
+        f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        _ffi.check(_ffi.lib().tree_attn_lin_workspace_size(self.handle, ctypes.byref(f),
+                                                           ctypes.byref(b)), "lin_workspace_size")
+        return int(f.value), int(b.value)
+
+    def lin_export(self) -> dict:
+        """Linear-attention piece table: ``pieces [P, 8]`` and ``succ``."""
+        st = self.stats()
+        out = {"pieces": np.zeros((st["lin_pieces"], 8), np.int32),
+               "succ": np.zeros((st["lin_succ"],), np.int32)}
+        _ffi.check(_ffi.lib().tree_attn_lin_plan_export(
+            self.handle, _ptr(out["pieces"]), _ptr(out["succ"])), "lin_plan_export")
+        return out
 
     def stats(self) -> dict:
         s = PlanStats()
@@ -187,6 +202,54 @@ def bwd(p: Plan, q, k, v, o, lse, do, scale: float, dq=None, dk=None, dv=None, w
         p.handle, *args[:5], args[5], ctypes.c_float(scale), *outs,
         ctypes.c_void_p(ws.data_ptr()), ws.numel(),
         ctypes.c_void_p(_stream_handle(stream))), "bwd")
+    return dq, dk, dv
+
+
+def lin_workspace(p: Plan, which: str = "bwd"):
+    """Allocates the device workspace of the linear-attention pass."""
+    import torch
+    f, b = p.lin_workspace_size()
+    n = b if which == "bwd" else f
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=f"cuda:{p.device}")
+
+
+def lin_fwd(p: Plan, q, k, v, scale: float, o=None, ws=None, stream=None):
+    """tree_attn_lin_fwd: chunkwise linear attention over the tree; returns o."""
+    import torch
+    n, hq, hkv, d = p.num_tokens, p.hq, p.hkv, p.head_dim
+    if o is None:
+        o = torch.empty((n, hq, d), dtype=q.dtype, device=q.device)
+    if ws is None:
+        ws = lin_workspace(p, "fwd")
+    args = [_check_tensor(q, "q", (n, hq, d), p), _check_tensor(k, "k", (n, hkv, d), p),
+            _check_tensor(v, "v", (n, hkv, d), p)]
+    po = _check_tensor(o, "o", (n, hq, d), p)
+    _ffi.check(_ffi.lib().tree_attn_lin_fwd(
+        p.handle, *args, ctypes.c_float(scale), po, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+        ctypes.c_void_p(_stream_handle(stream))), "lin_fwd")
+    return o
+
+
+def lin_bwd(p: Plan, q, k, v, do, scale: float, dq=None, dk=None, dv=None, ws=None,
+            stream=None):
+    """tree_attn_lin_bwd: returns (dq, dk, dv)."""
+    import torch
+    n, hq, hkv, d = p.num_tokens, p.hq, p.hkv, p.head_dim
+    if dq is None:
+        dq = torch.empty((n, hq, d), dtype=q.dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty((n, hkv, d), dtype=q.dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((n, hkv, d), dtype=q.dtype, device=q.device)
+    if ws is None:
+        ws = lin_workspace(p, "bwd")
+    args = [_check_tensor(q, "q", (n, hq, d), p), _check_tensor(k, "k", (n, hkv, d), p),
+            _check_tensor(v, "v", (n, hkv, d), p), _check_tensor(do, "do", (n, hq, d), p)]
+    outs = [_check_tensor(dq, "dq", (n, hq, d), p), _check_tensor(dk, "dk", (n, hkv, d), p),
+            _check_tensor(dv, "dv", (n, hkv, d), p)]
+    _ffi.check(_ffi.lib().tree_attn_lin_bwd(
+        p.handle, *args, ctypes.c_float(scale), *outs, ctypes.c_void_p(ws.data_ptr()),
+        ws.numel(), ctypes.c_void_p(_stream_handle(stream))), "lin_bwd")
     return dq, dk, dv
 
 

@@ -20,7 +20,8 @@ EXPORTS = (
     "tree_attn_plan_stats", "tree_attn_plan_export", "tree_attn_status_string",
     "tree_attn_last_error", "tree_attn_timing_enable", "tree_attn_timing_read",
     "tree_attn_positions", "tree_attn_build_tree", "tree_attn_gather_rows",
-    "tree_attn_scatter_sum_rows", "tree_attn_rope",
+    "tree_attn_scatter_sum_rows", "tree_attn_rope", "tree_attn_lin_workspace_size",
+    "tree_attn_lin_fwd", "tree_attn_lin_bwd", "tree_attn_lin_plan_export",
 )
 
 
@@ -29,7 +30,7 @@ class PlanStats(ctypes.Structure):
         "num_tokens", "num_nodes", "num_q_heads", "num_kv_heads", "head_dim", "pairs",
         "fwd_tiles", "fwd_ranges", "fwd_blocks", "bwd_items", "bwd_entries",
         "bwd_split_tiles", "bwd_slots", "fwd_tile_rows", "fwd_tile_keys", "bwd_tile_keys",
-        "bwd_block_rows")]
+        "bwd_block_rows", "lin_pieces", "lin_succ", "lin_chunk")]
 
 
 class Timing(ctypes.Structure):
@@ -37,7 +38,8 @@ class Timing(ctypes.Structure):
 
 
 TIMING_KINDS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_reduce", "bwd_dq", "positions", "gather",
-                "scatter_sum", "rope")
+                "scatter_sum", "rope", "lin_kv", "lin_scan", "lin_out", "lin_qdo", "lin_rscan",
+                "lin_dq", "lin_dkdv")
 
 
 class TreeAttnError(RuntimeError):
@@ -85,13 +87,20 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_int, vp]
     L.tree_attn_rope.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_float, ctypes.c_int32, ctypes.c_int, vp]
+    L.tree_attn_lin_workspace_size.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t),
+                                               ctypes.POINTER(ctypes.c_size_t)]
+    L.tree_attn_lin_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    L.tree_attn_lin_bwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
+                                    ctypes.c_size_t, vp]
+    L.tree_attn_lin_plan_export.argtypes = [vp, i32p, i32p]
     L.tree_attn_timing_enable.argtypes = [ctypes.c_int]
     L.tree_attn_timing_read.argtypes = [ctypes.POINTER(Timing), ctypes.c_int]
     for fn in ("tree_attn_timing_enable", "tree_attn_timing_read", "tree_attn_plan",
                "tree_attn_plan_host", "tree_attn_workspace_size", "tree_attn_fwd", "tree_attn_bwd",
                "tree_attn_plan_stats", "tree_attn_plan_export", "tree_attn_positions",
                "tree_attn_build_tree", "tree_attn_gather_rows", "tree_attn_scatter_sum_rows",
-               "tree_attn_rope"):
+               "tree_attn_rope", "tree_attn_lin_workspace_size", "tree_attn_lin_fwd",
+               "tree_attn_lin_bwd", "tree_attn_lin_plan_export"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L

@@ -31,6 +31,8 @@ struct tree_attn_plan_s {
   const I4* d_bwd_entries = nullptr;
   const I8* d_bwd_reduce = nullptr;
   const I4* d_segments = nullptr;
+  const I8* d_lin_pieces = nullptr;
+  const int32_t* d_lin_succ = nullptr;
 };
 
 namespace {
@@ -65,6 +67,12 @@ BwdLayout bwd_layout(const HostPlan& p) {
   l.total = l.dv_slots + align256(slot);
   if (p.num_tokens == 0) l.total = 0;
   return l;
+}
+
+// Linear attention workspace: piece states and per-piece deltas, each
+// [pieces, Hkv, D, D] fp32; the backward pass adds the state gradients.
+size_t lin_block(const HostPlan& p) {
+  return align256(p.lin_pieces.size() * static_cast<size_t>(p.hkv) * p.head_dim * p.head_dim * 4);
 }
 
 tree_attn_status_t make_host_plan(const int32_t* parent, const int32_t* seg_start,
@@ -194,7 +202,9 @@ tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_star
   const size_t o_be = o_bi + align256(bytes_of(hp.bwd_items));
   const size_t o_br = o_be + align256(bytes_of(hp.bwd_entries));
   const size_t o_sg = o_br + align256(bytes_of(hp.bwd_reduce));
-  const size_t total = o_sg + align256(bytes_of(hp.segments));
+  const size_t o_lp = o_sg + align256(bytes_of(hp.segments));
+  const size_t o_ls = o_lp + align256(bytes_of(hp.lin_pieces));
+  const size_t total = o_ls + align256(bytes_of(hp.lin_succ));
   if (total > 0) {
     e = hipMalloc(reinterpret_cast<void**>(&p->dev_buf), total);
     if (e != hipSuccess) {
@@ -210,7 +220,9 @@ tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_star
                  {o_bi, hp.bwd_items.data(), bytes_of(hp.bwd_items)},
                  {o_be, hp.bwd_entries.data(), bytes_of(hp.bwd_entries)},
                  {o_br, hp.bwd_reduce.data(), bytes_of(hp.bwd_reduce)},
-                 {o_sg, hp.segments.data(), bytes_of(hp.segments)}};
+                 {o_sg, hp.segments.data(), bytes_of(hp.segments)},
+                 {o_lp, hp.lin_pieces.data(), bytes_of(hp.lin_pieces)},
+                 {o_ls, hp.lin_succ.data(), bytes_of(hp.lin_succ)}};
     for (const Part& part : parts) {
       if (part.n == 0) continue;
       e = hipMemcpyAsync(p->dev_buf + part.off, part.src, part.n, hipMemcpyHostToDevice, stream);
@@ -227,6 +239,8 @@ tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_star
   p->d_bwd_entries = reinterpret_cast<const I4*>(p->dev_buf + o_be);
   p->d_bwd_reduce = reinterpret_cast<const I8*>(p->dev_buf + o_br);
   p->d_segments = reinterpret_cast<const I4*>(p->dev_buf + o_sg);
+  p->d_lin_pieces = reinterpret_cast<const I8*>(p->dev_buf + o_lp);
+  p->d_lin_succ = reinterpret_cast<const int32_t*>(p->dev_buf + o_ls);
   p->has_device = true;
   p->device = dev;
   *out = p;
@@ -347,6 +361,121 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
   return TREE_ATTN_OK;
 }
 
+tree_attn_status_t tree_attn_lin_workspace_size(tree_attn_plan_t plan, size_t* fwd_bytes,
+                                                size_t* bwd_bytes) {
+  if (!plan) return report(Status::kInvalidArg, "null plan");
+  const size_t b = plan->hp.num_tokens ? lin_block(plan->hp) : 0;
+  if (fwd_bytes) *fwd_bytes = 2 * b;
+  if (bwd_bytes) *bwd_bytes = 3 * b;
+  return TREE_ATTN_OK;
+}
+
+namespace {
+
+tree_attn_status_t lin_common(tree_attn_plan_t plan, float scale, void* ws, size_t ws_bytes,
+                              size_t need) {
+  tree_attn_status_t st = check_device(plan);
+  if (st != TREE_ATTN_OK) return st;
+  const HostPlan& hp = plan->hp;
+  if (hp.dtype != 0) return report(Status::kUnsupported, "linear attention takes bf16 tensors");
+  if (!std::isfinite(scale)) return report(Status::kInvalidArg, "scale must be finite");
+  if (hp.num_tokens == 0) return TREE_ATTN_OK;
+  if (!ws || ws_bytes < need)
+    return report(Status::kWorkspace, "linear attention workspace needs " +
+                                          std::to_string(need) + " bytes, got " +
+                                          std::to_string(ws_bytes));
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return report(Status::kWorkspace, "workspace must be 256-byte aligned");
+  return TREE_ATTN_OK;
+}
+
+tree_attn::LinArgs lin_args(tree_attn_plan_t plan, float scale) {
+  const HostPlan& hp = plan->hp;
+  tree_attn::LinArgs a{};
+  a.pieces = plan->d_lin_pieces;
+  a.succ = plan->d_lin_succ;
+  a.n_pieces = static_cast<int64_t>(hp.lin_pieces.size());
+  a.hq = static_cast<int>(hp.hq);
+  a.hkv = static_cast<int>(hp.hkv);
+  a.gsize = static_cast<int>(hp.hq / hp.hkv);
+  a.scale = scale;
+  return a;
+}
+
+}  // namespace
+
+tree_attn_status_t tree_attn_lin_fwd(tree_attn_plan_t plan, const void* q, const void* k,
+                                     const void* v, float scale, void* o, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  if (!plan) return report(Status::kInvalidArg, "null plan");
+  const size_t blk = lin_block(plan->hp);
+  tree_attn_status_t st = lin_common(plan, scale, ws, ws_bytes, 2 * blk);
+  if (st != TREE_ATTN_OK || plan->hp.num_tokens == 0) return st;
+  if (!q || !k || !v || !o) return report(Status::kInvalidArg, "null tensor pointer");
+  tree_attn::LinArgs a = lin_args(plan, scale);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = o;
+  a.state = reinterpret_cast<float*>(ws);
+  a.delta = reinterpret_cast<float*>(static_cast<char*>(ws) + blk);
+  const int hd = static_cast<int>(plan->hp.head_dim);
+  hipError_t e = timed(9, stream, [&] { return tree_attn::launch_lin_outer(a, 0, hd, stream); });
+  if (e == hipSuccess)
+    e = timed(10, stream, [&] { return tree_attn::launch_lin_scan(a, 0, hd, stream); });
+  if (e == hipSuccess)
+    e = timed(11, stream, [&] { return tree_attn::launch_lin_chunk(a, 0, hd, stream); });
+  if (e != hipSuccess) return report_hip(e, "linear attention forward launch");
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_lin_bwd(tree_attn_plan_t plan, const void* q, const void* k,
+                                     const void* v, const void* dout, float scale, void* dq,
+                                     void* dk, void* dv, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  if (!plan) return report(Status::kInvalidArg, "null plan");
+  const size_t blk = lin_block(plan->hp);
+  tree_attn_status_t st = lin_common(plan, scale, ws, ws_bytes, 3 * blk);
+  if (st != TREE_ATTN_OK || plan->hp.num_tokens == 0) return st;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv)
+    return report(Status::kInvalidArg, "null tensor pointer");
+  char* w = static_cast<char*>(ws);
+  tree_attn::LinArgs a = lin_args(plan, scale);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  const int hd = static_cast<int>(plan->hp.head_dim);
+  // states S recomputed (block 0, deltas in block 1), then the state
+  // gradients R (block 2, deltas again in block 1)
+  float* s_state = reinterpret_cast<float*>(w);
+  float* r_state = reinterpret_cast<float*>(w + 2 * blk);
+  a.delta = reinterpret_cast<float*>(w + blk);
+  a.state = s_state;
+  hipError_t e = timed(9, stream, [&] { return tree_attn::launch_lin_outer(a, 0, hd, stream); });
+  if (e == hipSuccess)
+    e = timed(10, stream, [&] { return tree_attn::launch_lin_scan(a, 0, hd, stream); });
+  if (e == hipSuccess) {
+    a.out = dq;
+    e = timed(14, stream, [&] { return tree_attn::launch_lin_chunk(a, 1, hd, stream); });
+  }
+  a.state = r_state;
+  if (e == hipSuccess)
+    e = timed(12, stream, [&] { return tree_attn::launch_lin_outer(a, 1, hd, stream); });
+  if (e == hipSuccess)
+    e = timed(13, stream, [&] { return tree_attn::launch_lin_scan(a, 1, hd, stream); });
+  if (e == hipSuccess) {
+    a.out = dk;
+    e = timed(15, stream, [&] { return tree_attn::launch_lin_chunk(a, 2, hd, stream); });
+  }
+  if (e == hipSuccess) {
+    a.out = dv;
+    e = timed(15, stream, [&] { return tree_attn::launch_lin_chunk(a, 3, hd, stream); });
+  }
+  if (e != hipSuccess) return report_hip(e, "linear attention backward launch");
+  return TREE_ATTN_OK;
+}
+
 tree_attn_status_t tree_attn_positions(tree_attn_plan_t plan, int32_t* node_id,
                                        int32_t* pos_id, hipStream_t stream) {
   tree_attn_status_t st = check_device(plan);
@@ -456,6 +585,20 @@ tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_st
   out->fwd_tile_keys = tree_attn::kFwdKeys;
   out->bwd_tile_keys = tree_attn::kBwdKeys;
   out->bwd_block_rows = tree_attn::kBwdRows;
+  out->lin_pieces = static_cast<int64_t>(hp.lin_pieces.size());
+  out->lin_succ = static_cast<int64_t>(hp.lin_succ.size());
+  out->lin_chunk = tree_attn::kLinChunk;
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_lin_plan_export(tree_attn_plan_t plan, int32_t* pieces,
+                                             int32_t* successors) {
+  if (!plan) return report(Status::kInvalidArg, "null plan");
+  const HostPlan& hp = plan->hp;
+  if (pieces && !hp.lin_pieces.empty())
+    std::memcpy(pieces, hp.lin_pieces.data(), bytes_of(hp.lin_pieces));
+  if (successors && !hp.lin_succ.empty())
+    std::memcpy(successors, hp.lin_succ.data(), bytes_of(hp.lin_succ));
   return TREE_ATTN_OK;
 }
 

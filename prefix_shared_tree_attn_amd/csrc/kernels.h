@@ -59,6 +59,22 @@ struct PosArgs {
   int32_t* pos_id;     // [N] or null
 };
 
+// Chunkwise linear attention over the tree (linear.hip), bf16 tensors.
+struct LinArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  void* out;             // chunk products: O, dQ, dK or dV
+  float* state;          // [pieces, Hkv, D, D] S (forward) or R (backward)
+  float* delta;          // [pieces, Hkv, D, D] K^T V or sum_h Q_h^T dO_h per piece
+  const I8* pieces;      // (token0, len, pred, succ_begin, succ_end, node, 0, 0)
+  const int32_t* succ;   // successor piece indices
+  int64_t n_pieces;
+  int hq, hkv, gsize;
+  float scale;
+};
+
 // dtype: 0 bf16, 1 fp32.  Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, int64_t n_blocks,
                       hipStream_t stream);
@@ -67,6 +83,11 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int dtype, int head_dim, hipStream_
 hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_post(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_positions(const PosArgs& a, hipStream_t stream);
+// backward = 0: delta = K^T V, state scan root first; backward = 1: delta =
+// sum_h Q_h^T dO_h, state scan leaves first.  mode: 0 O, 1 dQ, 2 dK, 3 dV.
+hipError_t launch_lin_outer(const LinArgs& a, int backward, int head_dim, hipStream_t stream);
+hipError_t launch_lin_scan(const LinArgs& a, int backward, int head_dim, hipStream_t stream);
+hipError_t launch_lin_chunk(const LinArgs& a, int mode, int head_dim, hipStream_t stream);
 
 // Passes either side of the attention call (prefix_ops.hip).
 hipError_t launch_gather(const void* src, void* dst, const int32_t* index, int64_t rows,

@@ -32,6 +32,47 @@ Status fail(std::string* err, Status s, const std::string& msg) {
   return s;
 }
 
+// Pieces of chunkwise linear attention.  A node's tokens are cut where
+// their trajectory depth is a multiple of kLinChunk, so every state a piece
+// starts from is either a trajectory chunk boundary or a branch point.
+// Pieces are listed in the root-first node order, so a piece's predecessor
+// (the previous piece of its node, else its parent's last piece) comes
+// before it and its successors (the next piece of its node, else the first
+// pieces of the child nodes) after it.
+void build_lin_pieces(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
+                      const std::vector<int32_t>& order,
+                      const std::vector<std::vector<int32_t>>& children,
+                      const std::vector<int64_t>& depth, HostPlan* out) {
+  const size_t m = order.size();
+  std::vector<int32_t> first(m, -1), last(m, -1);
+  std::vector<I8>& pc = out->lin_pieces;
+  for (int32_t i : order) {
+    const int64_t s = seg_start[i], e = s + seg_len[i];
+    int64_t t = s, d = depth[i];
+    int32_t pred = parent[i] >= 0 ? last[parent[i]] : -1;
+    while (t < e) {
+      const int64_t len = std::min<int64_t>(e - t, kLinChunk - d % kLinChunk);
+      const int32_t id = static_cast<int32_t>(pc.size());
+      pc.push_back({{static_cast<int32_t>(t), static_cast<int32_t>(len), pred, 0, 0, i, 0, 0}});
+      if (first[i] < 0) first[i] = id;
+      pred = id;
+      t += len;
+      d += len;
+    }
+    last[i] = pred;
+  }
+  std::vector<int32_t>& sc = out->lin_succ;
+  for (size_t j = 0; j < pc.size(); ++j) {
+    const int32_t node = pc[j].v[5];
+    pc[j].v[3] = static_cast<int32_t>(sc.size());
+    if (static_cast<int32_t>(j) != last[node])
+      sc.push_back(static_cast<int32_t>(j + 1));
+    else
+      for (int32_t c : children[node]) sc.push_back(first[c]);
+    pc[j].v[4] = static_cast<int32_t>(sc.size());
+  }
+}
+
 }  // namespace
 
 Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
@@ -124,6 +165,7 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
   p.segments.reserve(m);
   for (int32_t i : by_start)
     p.segments.push_back({seg_start[i], seg_len[i], static_cast<int32_t>(depth[i]), i});
+  build_lin_pieces(parent, seg_start, seg_len, order, children, depth, &p);
   p.pairs = 0;
   for (int64_t i = 0; i < m; ++i) {
     const int64_t L = seg_len[i];

@@ -35,6 +35,7 @@ constexpr int kFwdKeys = 64;   // keys per forward step
 constexpr int kBwdKeys = 128;  // keys per backward workgroup (4 waves x 32)
 constexpr int kBwdRows = 32;   // query rows per backward step
 constexpr int kXcds = 8;       // MI355X: 8 accelerator complex dies, 8 L2s
+constexpr int kLinChunk = 64;  // chunk of chunkwise linear attention (trajectory depth)
 
 struct I4 {
   int32_t x, y, z, w;
@@ -69,6 +70,11 @@ struct HostPlan {
   // segments sorted by start: (seg_start, seg_len, depth offset = ancestor
   // tokens of the node, node index), for the per-token position pass
   std::vector<I4> segments;
+
+  // linear attention: pieces (token0, len, pred, succ_begin, succ_end, node,
+  // 0, 0) in root-first order, pred = -1 at a root; successor piece indices
+  std::vector<I8> lin_pieces;
+  std::vector<int32_t> lin_succ;
 };
 
 // Validates the table and fills `out`.  On error returns the status and a

@@ -168,3 +168,21 @@ def test_scale_and_path_consistency():
     # the prompt's outputs equal those of the prompt alone
     p = _lin(chain_tree([7]), q[:7], k[:7], v[:7], do[:7], 1.0)
     _close(r1["o"][:7], p["o"])
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_sampled_rows_match_full_expansion(seed):
+    rng = np.random.default_rng(40 + seed)
+    t = random_tree(rng, n_nodes=10, max_len=9, n_roots=1 + seed)
+    q, k, v, do = _rand(rng, t.num_tokens, 4, 2, 6)
+    r = _lin(t, q, k, v, do, 0.3)
+    rows = rng.choice(t.num_tokens, size=7, replace=False)
+    o, dq = oracle.linear_query_rows(q, k, v, do, t.parent, t.seg_start, t.seg_len, 0.3,
+                                     rows, [0, 3])
+    _close(o, r["o"][rows][:, [0, 3]])
+    _close(dq, r["dq"][rows][:, [0, 3]])
+    for g in range(2):
+        dk, dv = oracle.linear_key_rows(q, k, v, do, t.parent, t.seg_start, t.seg_len, 0.3,
+                                        rows, g)
+        _close(dk, r["dk"][rows, g])
+        _close(dv, r["dv"][rows, g])
