@@ -325,13 +325,16 @@ tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_til
  * offset) is a multiple of 64, so every state the kernels materialise is a
  * trajectory chunk-boundary state or a branch-point state; a chunk that
  * straddles a branch point is computed as its parent part once and its child
- * parts once each (no replay).  The states live in the caller's workspace as
- * fp32 [pieces, Hkv, D, D]; products run in bf16 on the matrix cores.
+ * parts once each (no replay).  The states live in the caller's workspace:
+ * the scans accumulate in fp32 and store each piece's entering state as bf16
+ * [pieces, Hkv, D, D] (the matrix cores' operand type), with fp32 copies at
+ * branch points [nodes, Hkv, D, D]; products run in bf16 on the matrix cores.
  *
  * Tensors: Q, O, dO, dQ [N, Hq, D] and K, V, dK, dV [N, Hkv, D], bf16 only
  * (a plan built for fp32 gives TREE_ATTN_ERR_UNSUPPORTED); D 64 or 128.
  * Workspace: device memory, 256-byte aligned, at least the size
- * tree_attn_lin_workspace_size reports (2 state arrays forward, 3 backward);
+ * tree_attn_lin_workspace_size reports (2 piece arrays and the node array
+ * forward, 3 piece arrays and the node array backward);
  * it holds no result between calls.  The backward pass recomputes the
  * forward states itself, so it does not need the forward's workspace or O.
  * Errors as for tree_attn_fwd: invalid arguments are rejected before any

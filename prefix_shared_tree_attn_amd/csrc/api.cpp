@@ -69,10 +69,14 @@ BwdLayout bwd_layout(const HostPlan& p) {
   return l;
 }
 
-// Linear attention workspace: piece states and per-piece deltas, each
-// [pieces, Hkv, D, D] fp32; the backward pass adds the state gradients.
+// Linear attention workspace: bf16 piece states and per-piece deltas, each
+// [pieces, Hkv, D, D], and fp32 node-end states [nodes, Hkv, D, D]; the
+// backward pass adds the bf16 state gradients.
 size_t lin_block(const HostPlan& p) {
-  return align256(p.lin_pieces.size() * static_cast<size_t>(p.hkv) * p.head_dim * p.head_dim * 4);
+  return align256(p.lin_pieces.size() * static_cast<size_t>(p.hkv) * p.head_dim * p.head_dim * 2);
+}
+size_t lin_ends(const HostPlan& p) {
+  return align256(static_cast<size_t>(p.num_nodes) * p.hkv * p.head_dim * p.head_dim * 4);
 }
 
 tree_attn_status_t make_host_plan(const int32_t* parent, const int32_t* seg_start,
@@ -364,9 +368,10 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
 tree_attn_status_t tree_attn_lin_workspace_size(tree_attn_plan_t plan, size_t* fwd_bytes,
                                                 size_t* bwd_bytes) {
   if (!plan) return report(Status::kInvalidArg, "null plan");
-  const size_t b = plan->hp.num_tokens ? lin_block(plan->hp) : 0;
-  if (fwd_bytes) *fwd_bytes = 2 * b;
-  if (bwd_bytes) *bwd_bytes = 3 * b;
+  const bool any = plan->hp.num_tokens > 0;
+  const size_t b = any ? lin_block(plan->hp) : 0, e = any ? lin_ends(plan->hp) : 0;
+  if (fwd_bytes) *fwd_bytes = 2 * b + e;
+  if (bwd_bytes) *bwd_bytes = 3 * b + e;
   return TREE_ATTN_OK;
 }
 
@@ -409,7 +414,7 @@ tree_attn_status_t tree_attn_lin_fwd(tree_attn_plan_t plan, const void* q, const
                                      size_t ws_bytes, hipStream_t stream) {
   if (!plan) return report(Status::kInvalidArg, "null plan");
   const size_t blk = lin_block(plan->hp);
-  tree_attn_status_t st = lin_common(plan, scale, ws, ws_bytes, 2 * blk);
+  tree_attn_status_t st = lin_common(plan, scale, ws, ws_bytes, 2 * blk + lin_ends(plan->hp));
   if (st != TREE_ATTN_OK || plan->hp.num_tokens == 0) return st;
   if (!q || !k || !v || !o) return report(Status::kInvalidArg, "null tensor pointer");
   tree_attn::LinArgs a = lin_args(plan, scale);
@@ -417,8 +422,9 @@ tree_attn_status_t tree_attn_lin_fwd(tree_attn_plan_t plan, const void* q, const
   a.k = k;
   a.v = v;
   a.out = o;
-  a.state = reinterpret_cast<float*>(ws);
-  a.delta = reinterpret_cast<float*>(static_cast<char*>(ws) + blk);
+  a.state = ws;
+  a.delta = static_cast<char*>(ws) + blk;
+  a.ends = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * blk);
   const int hd = static_cast<int>(plan->hp.head_dim);
   hipError_t e = timed(9, stream, [&] { return tree_attn::launch_lin_outer(a, 0, hd, stream); });
   if (e == hipSuccess)
@@ -435,7 +441,7 @@ tree_attn_status_t tree_attn_lin_bwd(tree_attn_plan_t plan, const void* q, const
                                      hipStream_t stream) {
   if (!plan) return report(Status::kInvalidArg, "null plan");
   const size_t blk = lin_block(plan->hp);
-  tree_attn_status_t st = lin_common(plan, scale, ws, ws_bytes, 3 * blk);
+  tree_attn_status_t st = lin_common(plan, scale, ws, ws_bytes, 3 * blk + lin_ends(plan->hp));
   if (st != TREE_ATTN_OK || plan->hp.num_tokens == 0) return st;
   if (!q || !k || !v || !dout || !dq || !dk || !dv)
     return report(Status::kInvalidArg, "null tensor pointer");
@@ -447,10 +453,11 @@ tree_attn_status_t tree_attn_lin_bwd(tree_attn_plan_t plan, const void* q, const
   a.dout = dout;
   const int hd = static_cast<int>(plan->hp.head_dim);
   // states S recomputed (block 0, deltas in block 1), then the state
-  // gradients R (block 2, deltas again in block 1)
-  float* s_state = reinterpret_cast<float*>(w);
-  float* r_state = reinterpret_cast<float*>(w + 2 * blk);
-  a.delta = reinterpret_cast<float*>(w + blk);
+  // gradients R (block 2, deltas again in block 1); node ends after them
+  void* s_state = w;
+  void* r_state = w + 2 * blk;
+  a.delta = w + blk;
+  a.ends = reinterpret_cast<float*>(w + 3 * blk);
   a.state = s_state;
   hipError_t e = timed(9, stream, [&] { return tree_attn::launch_lin_outer(a, 0, hd, stream); });
   if (e == hipSuccess)

@@ -66,9 +66,11 @@ struct LinArgs {
   const void* v;
   const void* dout;
   void* out;             // chunk products: O, dQ, dK or dV
-  float* state;          // [pieces, Hkv, D, D] S (forward) or R (backward)
-  float* delta;          // [pieces, Hkv, D, D] K^T V or sum_h Q_h^T dO_h per piece
-  const I8* pieces;      // (token0, len, pred, succ_begin, succ_end, node, 0, 0)
+  void* state;           // bf16 [pieces, Hkv, D, D] S (forward) or R (backward)
+  void* delta;           // bf16 [pieces, Hkv, D, D] K^T V or sum_h Q_h^T dO_h per piece
+  float* ends;           // [nodes, Hkv, D, D] fp32 state at a node's end (forward)
+                         // or with its first piece's delta added (backward)
+  const I8* pieces;      // (token0, len, pred, succ_begin, succ_end, node, flags, 0)
   const int32_t* succ;   // successor piece indices
   int64_t n_pieces;
   int hq, hkv, gsize;

@@ -24,8 +24,9 @@
 // branch to its prefix;  (3) dQ = scale (dO S_p^T + tril(dO V^T) K),
 // dK = scale (V R_p^T + sum_h triu(V dO_h^T) Q_h),
 // dV = scale (K R_p + sum_h triu(K Q_h^T) dO_h).
-// All products run on the matrix cores in bf16 with fp32 accumulation; the
-// states stay fp32 in HBM and are rounded to bf16 as MFMA operands.
+// All products run on the matrix cores in bf16 with fp32 accumulation.  The
+// scans accumulate in fp32 and hand the per-piece states to the chunk kernels
+// in bf16 (their MFMA operand type); per-piece deltas are stored in bf16 too.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,74 +35,44 @@ namespace {
 
 constexpr int CH = kLinChunk;
 
-// LDS operand with R rows of K contiguous bf16 (padded by 8 elements so that
-// 16-byte fragment reads of consecutive rows spread over the banks).
-template <int R, int K>
-struct LOp {
-  static constexpr int P = K + 8;
-  static constexpr int BYTES = R * P * 2;
-};
-
-// acc += A[m0 + 0..31, 0..K) . B[n0 + 0..31, 0..K)^T, with A and B in LDS,
-// rows PA / PB elements apart: lane l reads row l % 32, elements
-// 8 (l / 32) .. + 7 of each 16-wide chunk (the 32x32x16 operand layout).
-template <int PA, int PB, int K>
-__device__ __forceinline__ void mma_rows(f32x16& acc, const LDS_PTR(__bf16) a, int m0,
-                                         const LDS_PTR(__bf16) b, int n0, int lane) {
-  const LDS_PTR(__bf16) pa = a + (m0 + (lane & 31)) * PA + 8 * (lane >> 5);
-  const LDS_PTR(__bf16) pb = b + (n0 + (lane & 31)) * PB + 8 * (lane >> 5);
-#pragma unroll
-  for (int kk = 0; kk < K / 16; ++kk) {
-    const bf16x8 fa = *reinterpret_cast<const LDS_PTR(bf16x8)>(pa + 16 * kk);
-    const bf16x8 fb = *reinterpret_cast<const LDS_PTR(bf16x8)>(pb + 16 * kk);
-    acc = mfma32(fa, fb, acc);
-  }
-}
-
 // Rows 0 .. CH-1 of a token-major tensor (rows `stride` elements apart, D
-// columns from `src`) into x[r][c]; rows at or past n are zero.
-template <int D, int P>
-__device__ __forceinline__ void stage_rows(LDS_PTR(__bf16) x, const __bf16* src, int64_t stride,
+// columns from `src`) into a swizzled LDS tile (see Tile); rows at or past n
+// are zero.  16-byte copies: D / 8 per row.
+template <int D>
+__device__ __forceinline__ void stage_tile(LDS_PTR(char) t, const __bf16* src, int64_t stride,
                                            int n, int tid) {
-  constexpr int CPR = D / 8;
-  for (int c = tid; c < CH * CPR; c += 256) {
-    const int r = c / CPR, cc = c % CPR;
-    i32x4 v = {0, 0, 0, 0};
-    if (r < n) v = gload16(src + r * stride + 8 * cc);
-    *reinterpret_cast<LDS_PTR(i32x4)>(x + r * P + 8 * cc) = v;
+  constexpr int CPR = D / 8, PER = CH * CPR / 256;
+  i32x4 v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
+    v[i] = i32x4{0, 0, 0, 0};
+    if (r < n) v[i] = gload16(src + r * stride + 8 * cc);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
+    lds_write16(t, Tile<D, CH>::chunk_off(r, cc), v[i]);
   }
 }
 
-// The same rows transposed: x[c][r] (D rows of CH tokens).
-template <int D, int P>
-__device__ __forceinline__ void stage_cols(LDS_PTR(__bf16) x, const __bf16* src, int64_t stride,
-                                           int n, int tid) {
-  constexpr int CPR = D / 8;
-  for (int c = tid; c < CH * CPR; c += 256) {
-    const int r = c / CPR, cc = c % CPR;
-    bf16x8 v;
-    if (r < n) {
-      v = *reinterpret_cast<const bf16x8*>(src + r * stride + 8 * cc);
+// B operand fragments of a D x D bf16 state W read straight from global
+// memory (L2): f[kk] holds W[n][16 kk + 8 (lane / 32) + s] for
+// n = n0 + lane % 32.  W is the state s itself (TR = false: one 16-byte load
+// per fragment) or its transpose (TR = true: eight 2-byte loads, each reading
+// 32 consecutive values across the lane half).
+template <int D, bool TR>
+__device__ __forceinline__ void state_frags(bf16x8 (&f)[D / 16], const __bf16* s, int n0,
+                                            int lane) {
+  const int n = n0 + (lane & 31), h = 8 * (lane >> 5);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const int k0 = 16 * kk + h;
+    if constexpr (!TR) {
+      f[kk] = *reinterpret_cast<const bf16x8*>(s + n * D + k0);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = to_bf16(0.f);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[(8 * cc + e) * P + r] = v[e];
-  }
-}
-
-// A D x D fp32 state (row-major) as bf16: x[i][j] = s[i][j], or x[j][i] when
-// transposed.
-template <int D, int P, bool TR>
-__device__ __forceinline__ void stage_state(LDS_PTR(__bf16) x, const float* s, int tid) {
-  for (int c = tid; c < D * D / 4; c += 256) {
-    const int i = c / (D / 4), j = 4 * (c % (D / 4));
-    const f32x4 v = *reinterpret_cast<const f32x4*>(s + i * D + j);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if constexpr (TR) x[(j + e) * P + i] = to_bf16(v[e]);
-      else x[i * P + j + e] = to_bf16(v[e]);
+      for (int e = 0; e < 8; ++e) f[kk][e] = s[(k0 + e) * D + n];
     }
   }
 }
@@ -113,15 +84,16 @@ __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 
 
 // (1) Per-piece outer-product sums, one workgroup per (piece, kv head g):
 // out[p, g] = sum over heads j < nh of A_j^T B_j over the piece's tokens, a
-// D x D fp32 matrix.  Forward: A = K, B = V of head g (nh = 1).  Backward:
-// A = Q, B = dO of the group's query heads.
+// D x D matrix accumulated in fp32 and stored as bf16.  Forward: A = K, B = V of head g (nh = 1).  Backward:
+// A = Q, B = dO of the group's query heads.  Both are staged row-major and
+// read as transposed operands (the reduction runs over the tokens).
 template <int D>
 __global__ __launch_bounds__(256) void lin_outer_kernel(LinArgs a, int backward) {
-  using OP = LOp<D, CH>;
+  using T = Tile<D, CH>;
   constexpr int NBD = D / 32, NB = NBD * NBD, PER = (NB + 3) / 4;
   extern __shared__ __attribute__((aligned(16))) char smem_dyn[];
-  LDS_PTR(__bf16) xa = (LDS_PTR(__bf16))(smem_dyn);
-  LDS_PTR(__bf16) xb = (LDS_PTR(__bf16))(smem_dyn + OP::BYTES);
+  LDS_PTR(char) ta = (LDS_PTR(char))(smem_dyn);
+  LDS_PTR(char) tb = (LDS_PTR(char))(smem_dyn + T::BYTES);
   const int p = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
   const I8 pc = load_plan8(a.pieces, p);
   const int tok0 = pc.v[0], len = pc.v[1];
@@ -138,55 +110,68 @@ __global__ __launch_bounds__(256) void lin_outer_kernel(LinArgs a, int backward)
     if (backward) {
       const int h = g * a.gsize + j;
       const int64_t off = static_cast<int64_t>(tok0) * qs + static_cast<int64_t>(h) * D;
-      stage_cols<D, OP::P>(xa, static_cast<const __bf16*>(a.q) + off, qs, len, tid);
-      stage_cols<D, OP::P>(xb, static_cast<const __bf16*>(a.dout) + off, qs, len, tid);
+      stage_tile<D>(ta, static_cast<const __bf16*>(a.q) + off, qs, len, tid);
+      stage_tile<D>(tb, static_cast<const __bf16*>(a.dout) + off, qs, len, tid);
     } else {
       const int64_t off = static_cast<int64_t>(tok0) * ks + static_cast<int64_t>(g) * D;
-      stage_cols<D, OP::P>(xa, static_cast<const __bf16*>(a.k) + off, ks, len, tid);
-      stage_cols<D, OP::P>(xb, static_cast<const __bf16*>(a.v) + off, ks, len, tid);
+      stage_tile<D>(ta, static_cast<const __bf16*>(a.k) + off, ks, len, tid);
+      stage_tile<D>(tb, static_cast<const __bf16*>(a.v) + off, ks, len, tid);
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int blk = wave + 4 * i;
-      if (blk < NB) mma_rows<OP::P, OP::P, CH>(acc[i], xa, 32 * (blk / NBD), xb, 32 * (blk % NBD), lane);
+      if (blk >= NB) continue;
+      const int bi = blk / NBD, bj = blk % NBD;
+#pragma unroll
+      for (int kk = 0; kk < CH / 16; ++kk)
+        acc[i] = mfma32(tr_operand<T>(ta, 16 * kk, 32 * bi, lane),
+                        tr_operand<T>(tb, 16 * kk, 32 * bj, lane), acc[i]);
     }
     __syncthreads();
   }
-  float* out = a.delta + (static_cast<int64_t>(p) * a.hkv + g) * D * D;
+  __bf16* out = static_cast<__bf16*>(a.delta) + (static_cast<int64_t>(p) * a.hkv + g) * D * D;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int blk = wave + 4 * i;
     if (blk >= NB) continue;
     const int r0 = 32 * (blk / NBD), c = 32 * (blk % NBD) + (lane & 31);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) out[(r0 + acc_row(v, lane)) * D + c] = acc[i][v];
+    for (int v = 0; v < 16; ++v) out[(r0 + acc_row(v, lane)) * D + c] = to_bf16(acc[i][v]);
   }
 }
 
-// (2) State scan over the pieces, one thread per (kv head, state element):
-// forward, in root-first order, state[p] = state[pred] + delta[pred] (zero at
-// a root); backward, in reverse, state[p] = sum over successors c of
-// (state[c] + delta[c]) (zero at a leaf).  The running value of the piece
-// just done stays in a register, which covers the usual case of a piece
-// followed by the next piece of its node; the deltas of eight pieces are
-// loaded ahead of their turn.
+// (2) State scan over the pieces, one thread per two neighbouring (kv head,
+// state element) pairs, accumulating in fp32.  Forward, in root-first order: the state entering
+// piece p is that of its predecessor plus the predecessor's delta (zero at a
+// root).  Backward, in reverse: the state gradient leaving piece p is the sum
+// over its successors c of (state leaving c + delta of c) (zero at a leaf).
+// The running value of the piece just done stays in a register; it is the
+// predecessor (forward) or the one in-node successor (backward) of the next
+// piece except at branch points, whose values go through `ends` in fp32: the
+// state at the end of each node (forward), or the state entering each node's
+// first piece (backward).  The consumers read the states as bf16.
 template <int D>
 __global__ __launch_bounds__(256) void lin_scan_kernel(LinArgs a, int backward) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
   const int64_t per = static_cast<int64_t>(a.hkv) * D * D;  // one piece's states
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  // two neighbouring elements per thread: 4-byte bf16 accesses
+  const int64_t e = 2 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
   if (e >= per) return;
   const int64_t np = a.n_pieces;
-  constexpr int LA = 8;
+  const __bf16* delta = static_cast<const __bf16*>(a.delta);
+  __bf16* state = static_cast<__bf16*>(a.state);
+  constexpr int LA = 8;  // deltas loaded ahead
   int cached = -1;
-  float run = 0.f;  // state + delta of piece `cached`
+  float r0 = 0.f, r1 = 0.f;  // state + delta of piece `cached`
   for (int64_t b = 0; b < np; b += LA) {
-    float dl[LA];
+    bf16x2 dl[LA];
 #pragma unroll
     for (int u = 0; u < LA; ++u) {
       const int64_t i = b + u;
       const int64_t p = backward ? np - 1 - i : i;
-      dl[u] = i < np ? a.delta[p * per + e] : 0.f;
+      dl[u] = i < np ? *reinterpret_cast<const bf16x2*>(delta + p * per + e) : bf16x2{};
     }
 #pragma unroll
     for (int u = 0; u < LA; ++u) {
@@ -194,96 +179,128 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(LinArgs a, int backward) 
       if (i >= np) break;
       const int p = static_cast<int>(backward ? np - 1 - i : i);
       const I8 pc = load_plan8(a.pieces, p);
-      float s = 0.f;
+      float s0 = 0.f, s1 = 0.f;
       if (!backward) {
         const int pr = pc.v[2];
-        if (pr >= 0) s = pr == cached ? run : a.state[pr * per + e] + a.delta[pr * per + e];
+        if (pr >= 0) {
+          if (pr == cached) {
+            s0 = r0;
+            s1 = r1;
+          } else {
+            const f32x2 x = *reinterpret_cast<const f32x2*>(
+                a.ends + load_plan8(a.pieces, pr).v[5] * per + e);
+            s0 = x[0];
+            s1 = x[1];
+          }
+        }
       } else {
         for (int j = pc.v[3]; j < pc.v[4]; ++j) {
           const int c = a.succ[j];
-          s += c == cached ? run : a.state[c * per + e] + a.delta[c * per + e];
+          if (c == cached) {
+            s0 += r0;
+            s1 += r1;
+          } else {
+            const f32x2 x = *reinterpret_cast<const f32x2*>(
+                a.ends + load_plan8(a.pieces, c).v[5] * per + e);
+            s0 += x[0];
+            s1 += x[1];
+          }
         }
       }
-      a.state[p * per + e] = s;
+      bf16x2 out;
+      out[0] = to_bf16(s0);
+      out[1] = to_bf16(s1);
+      *reinterpret_cast<bf16x2*>(state + p * per + e) = out;
       cached = p;
-      run = s + dl[u];
+      r0 = s0 + static_cast<float>(dl[u][0]);
+      r1 = s1 + static_cast<float>(dl[u][1]);
+      if (pc.v[6] & (backward ? 1 : 2)) {
+        f32x2 w;
+        w[0] = r0;
+        w[1] = r1;
+        *reinterpret_cast<f32x2*>(a.ends + pc.v[5] * per + e) = w;
+      }
     }
   }
 }
 
 // (3) Chunk products, one workgroup per (piece, kv head g), a loop over the
-// query heads of the group.  With X the piece's rows of one operand, W a D x D
-// state, Z and U the piece's rows of two more, and M the causal mask,
-//   out = scale (X W^T + (M o X Z^T) U)
-// with W^T, U read as "B^T" operands (row n holds column n):
-//   OUT: X = Q_h, W = S^T, Z = K, U = V^T, M: key <= query, out = O_h
-//   DQ : X = dO_h, W = S,  Z = V, U = K^T, M: key <= query, out = dQ_h
-//   DK : X = V,  W = R,    Z = dO_h, U = Q_h^T, M: query >= key, out = dK
-//   DV : X = K,  W = R^T,  Z = Q_h, U = dO_h^T, M: query >= key, out = dV
-// (summed over the group's heads for DK and DV).
+// query heads of the group.  With X, Z, Y the piece's rows of three operands,
+// W a D x D state and M the causal mask,
+//   out = scale (X W^T + (M o X Z^T) Y)          (W^T: W read as B^T)
+//   OUT: X = Q_h,  W = S^T, Z = K,    Y = V,    M: key <= query, out = O_h
+//   DQ : X = dO_h, W = S,   Z = V,    Y = K,    M: key <= query, out = dQ_h
+//   DK : X = V,    W = R,   Z = dO_h, Y = Q_h,  M: query >= key, out = dK
+//   DV : X = K,    W = R^T, Z = Q_h,  Y = dO_h, M: query >= key, out = dV
+// (DK and DV summed over the group's heads).  X, Z, Y sit row-major in
+// swizzled LDS tiles: X and Z feed X Z^T as row operands, Y feeds the second
+// product as transposed operands.  The state fragments (bf16) come from
+// global memory once per workgroup and stay in registers.  Wave w owns output
+// blocks w and w + 4 (rows 0 and 32 of column block w) at D = 128, block w
+// at D = 64, and one 32 x 32 block of M o X Z^T, which goes to LDS as bf16.
 template <int D, int MODE>
-__global__ __launch_bounds__(256) void lin_chunk_kernel(LinArgs a) {
+__global__ __launch_bounds__(256, 2) void lin_chunk_kernel(LinArgs a) {
   constexpr bool PER_HEAD_X = MODE < 2;  // OUT, DQ: X changes with the head
-  using OX = LOp<CH, D>;   // X, Z: CH rows of D
-  using OW = LOp<D, D>;    // W: D rows of D
-  using OU = LOp<D, CH>;   // U: D rows of CH
-  using OA = LOp<CH, CH>;  // masked X Z^T
-  constexpr int NBN = D / 32, NB = 2 * NBN, PER = NB / 4;
+  constexpr bool W_TR = MODE == 0 || MODE == 3;
+  using T = Tile<D, CH>;    // CH tokens x D
+  using TA = Tile<CH, CH>;  // masked X Z^T
+  constexpr int NBN = D / 32, NB = 2 * NBN, PER = NB / 4, KD = D / 16;
   extern __shared__ __attribute__((aligned(16))) char smem_dyn[];
-  LDS_PTR(__bf16) xs = (LDS_PTR(__bf16))(smem_dyn);
-  LDS_PTR(__bf16) ws = (LDS_PTR(__bf16))(smem_dyn + OX::BYTES);
-  LDS_PTR(__bf16) zs = (LDS_PTR(__bf16))(smem_dyn + OX::BYTES + OW::BYTES);
-  LDS_PTR(__bf16) us = (LDS_PTR(__bf16))(smem_dyn + 2 * OX::BYTES + OW::BYTES);
-  LDS_PTR(__bf16) as = (LDS_PTR(__bf16))(smem_dyn + 2 * OX::BYTES + OW::BYTES + OU::BYTES);
+  LDS_PTR(char) xs = (LDS_PTR(char))(smem_dyn);
+  LDS_PTR(char) zs = (LDS_PTR(char))(smem_dyn + T::BYTES);
+  LDS_PTR(char) ys = (LDS_PTR(char))(smem_dyn + 2 * T::BYTES);
+  LDS_PTR(char) as = (LDS_PTR(char))(smem_dyn + 3 * T::BYTES);
 
   const int p = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
   const I8 pc = load_plan8(a.pieces, p);
   const int tok0 = pc.v[0], len = pc.v[1];
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t qs = static_cast<int64_t>(a.hq) * D, ks = static_cast<int64_t>(a.hkv) * D;
   const __bf16* Q = static_cast<const __bf16*>(a.q) + static_cast<int64_t>(tok0) * qs;
   const __bf16* dO = static_cast<const __bf16*>(a.dout) + static_cast<int64_t>(tok0) * qs;
   const __bf16* K = static_cast<const __bf16*>(a.k) + static_cast<int64_t>(tok0) * ks + g * D;
   const __bf16* V = static_cast<const __bf16*>(a.v) + static_cast<int64_t>(tok0) * ks + g * D;
-  const float* st = a.state + (static_cast<int64_t>(p) * a.hkv + g) * D * D;
+  const __bf16* st =
+      static_cast<const __bf16*>(a.state) + (static_cast<int64_t>(p) * a.hkv + g) * D * D;
 
   // head-independent operands
   if constexpr (MODE == 0) {
-    stage_state<D, OW::P, true>(ws, st, tid);
-    stage_rows<D, OX::P>(zs, K, ks, len, tid);
-    stage_cols<D, OU::P>(us, V, ks, len, tid);
+    stage_tile<D>(zs, K, ks, len, tid);
+    stage_tile<D>(ys, V, ks, len, tid);
   } else if constexpr (MODE == 1) {
-    stage_state<D, OW::P, false>(ws, st, tid);
-    stage_rows<D, OX::P>(zs, V, ks, len, tid);
-    stage_cols<D, OU::P>(us, K, ks, len, tid);
+    stage_tile<D>(zs, V, ks, len, tid);
+    stage_tile<D>(ys, K, ks, len, tid);
   } else if constexpr (MODE == 2) {
-    stage_state<D, OW::P, false>(ws, st, tid);
-    stage_rows<D, OX::P>(xs, V, ks, len, tid);
+    stage_tile<D>(xs, V, ks, len, tid);
   } else {
-    stage_state<D, OW::P, true>(ws, st, tid);
-    stage_rows<D, OX::P>(xs, K, ks, len, tid);
+    stage_tile<D>(xs, K, ks, len, tid);
   }
+  // this wave's output column block and its state fragments
+  const int n0 = 32 * (wave % NBN);
+  bf16x8 wf[KD];
+  state_frags<D, W_TR>(wf, st, n0, lane);
 
   f32x16 acc[PER];
-  auto inter = [&]() {
+  auto inter = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
+      const int m0 = 32 * ((wave + 4 * i) / NBN);
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
-      const int blk = wave + 4 * i;
-      mma_rows<OX::P, OW::P, D>(acc[i], xs, 32 * (blk / NBN), ws, 32 * (blk % NBN), lane);
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk)
+        acc[i] = mfma32(row_operand<T>(xs, m0 + l32, 2 * kk + half), wf[kk], acc[i]);
     }
   };
-  auto store = [&](__bf16* out, int64_t stride) {
+  auto store = [&](__bf16* out, int64_t stride) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int blk = wave + 4 * i;
-      const int r0 = 32 * (blk / NBN), c = 32 * (blk % NBN) + (lane & 31);
+      const int m0 = 32 * ((wave + 4 * i) / NBN);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = r0 + acc_row(v, lane);
-        if (r < len) out[r * stride + c] = to_bf16(a.scale * acc[i][v]);
+        const int r = m0 + acc_row(v, lane);
+        if (r < len) out[r * stride + n0 + l32] = to_bf16(a.scale * acc[i][v]);
       }
     }
   };
@@ -294,38 +311,44 @@ __global__ __launch_bounds__(256) void lin_chunk_kernel(LinArgs a) {
   }
   for (int j = 0; j < a.gsize; ++j) {
     const int h = g * a.gsize + j;
-    if constexpr (MODE == 0) stage_rows<D, OX::P>(xs, Q + h * D, qs, len, tid);
-    if constexpr (MODE == 1) stage_rows<D, OX::P>(xs, dO + h * D, qs, len, tid);
+    if constexpr (MODE == 0) stage_tile<D>(xs, Q + h * D, qs, len, tid);
+    if constexpr (MODE == 1) stage_tile<D>(xs, dO + h * D, qs, len, tid);
     if constexpr (MODE == 2) {
-      stage_rows<D, OX::P>(zs, dO + h * D, qs, len, tid);
-      stage_cols<D, OU::P>(us, Q + h * D, qs, len, tid);
+      stage_tile<D>(zs, dO + h * D, qs, len, tid);
+      stage_tile<D>(ys, Q + h * D, qs, len, tid);
     }
     if constexpr (MODE == 3) {
-      stage_rows<D, OX::P>(zs, Q + h * D, qs, len, tid);
-      stage_cols<D, OU::P>(us, dO + h * D, qs, len, tid);
+      stage_tile<D>(zs, Q + h * D, qs, len, tid);
+      stage_tile<D>(ys, dO + h * D, qs, len, tid);
     }
     __syncthreads();
     if constexpr (PER_HEAD_X) inter();
     {
-      // one 32x32 block of X Z^T per wave, masked, to LDS as bf16
+      // one 32x32 block of M o X Z^T per wave, to LDS as bf16
       const int bi = wave >> 1, bj = wave & 1;
       f32x16 t;
 #pragma unroll
       for (int v = 0; v < 16; ++v) t[v] = 0.f;
-      mma_rows<OX::P, OX::P, D>(t, xs, 32 * bi, zs, 32 * bj, lane);
-      const int c = 32 * bj + (lane & 31);
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk)
+        t = mfma32(row_operand<T>(xs, 32 * bi + l32, 2 * kk + half),
+                   row_operand<T>(zs, 32 * bj + l32, 2 * kk + half), t);
+      const int c = 32 * bj + l32;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = 32 * bi + acc_row(v, lane);
         const bool keep = PER_HEAD_X ? c <= r : c >= r;
-        as[r * OA::P + c] = to_bf16(keep ? t[v] : 0.f);
+        *reinterpret_cast<LDS_PTR(__bf16)>(as + TA::elem_off(r, c)) = to_bf16(keep ? t[v] : 0.f);
       }
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int blk = wave + 4 * i;
-      mma_rows<OA::P, OU::P, CH>(acc[i], as, 32 * (blk / NBN), us, 32 * (blk % NBN), lane);
+      const int m0 = 32 * ((wave + 4 * i) / NBN);
+#pragma unroll
+      for (int kk = 0; kk < CH / 16; ++kk)
+        acc[i] = mfma32(row_operand<TA>(as, m0 + l32, 2 * kk + half),
+                        tr_operand<T>(ys, 16 * kk, n0, lane), acc[i]);
     }
     if constexpr (PER_HEAD_X) {
       __bf16* out = static_cast<__bf16*>(a.out) + static_cast<int64_t>(tok0) * qs + h * D;
@@ -367,7 +390,7 @@ hipError_t launch_dyn(Kern kern, int64_t blocks, int bytes, hipStream_t s, const
 
 template <int D>
 hipError_t lin_outer_t(const LinArgs& a, int backward, hipStream_t s) {
-  const int bytes = 2 * LOp<D, CH>::BYTES;
+  const int bytes = 2 * Tile<D, CH>::BYTES;
   auto kern = lin_outer_kernel<D>;
   if (bytes > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -382,15 +405,14 @@ hipError_t lin_outer_t(const LinArgs& a, int backward, hipStream_t s) {
 template <int D>
 hipError_t lin_scan_t(const LinArgs& a, int backward, hipStream_t s) {
   const int64_t per = static_cast<int64_t>(a.hkv) * D * D;
-  hipLaunchKernelGGL(lin_scan_kernel<D>, dim3(static_cast<unsigned>((per + 255) / 256)), dim3(256),
-                     0, s, a, backward);
+  hipLaunchKernelGGL(lin_scan_kernel<D>, dim3(static_cast<unsigned>((per / 2 + 255) / 256)),
+                     dim3(256), 0, s, a, backward);
   return hipGetLastError();
 }
 
 template <int D, int MODE>
 hipError_t lin_chunk_t(const LinArgs& a, hipStream_t s) {
-  const int bytes = 2 * LOp<CH, D>::BYTES + LOp<D, D>::BYTES + LOp<D, CH>::BYTES +
-                    LOp<CH, CH>::BYTES;
+  const int bytes = 3 * Tile<D, CH>::BYTES + Tile<CH, CH>::BYTES;
   return launch_dyn(lin_chunk_kernel<D, MODE>, a.n_pieces * a.hkv, bytes, s, a);
 }
 

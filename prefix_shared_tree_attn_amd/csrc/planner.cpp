@@ -70,6 +70,8 @@ void build_lin_pieces(const int32_t* parent, const int32_t* seg_start, const int
     else
       for (int32_t c : children[node]) sc.push_back(first[c]);
     pc[j].v[4] = static_cast<int32_t>(sc.size());
+    pc[j].v[6] = (static_cast<int32_t>(j) == first[node] ? 1 : 0) |
+                 (static_cast<int32_t>(j) == last[node] ? 2 : 0);
   }
 }
 

@@ -72,7 +72,8 @@ struct HostPlan {
   std::vector<I4> segments;
 
   // linear attention: pieces (token0, len, pred, succ_begin, succ_end, node,
-  // 0, 0) in root-first order, pred = -1 at a root; successor piece indices
+  // flags: 1 first / 2 last piece of its node, 0) in root-first order,
+  // pred = -1 at a root; successor piece indices
   std::vector<I8> lin_pieces;
   std::vector<int32_t> lin_succ;
 };

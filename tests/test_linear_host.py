@@ -47,6 +47,9 @@ def _check(t):
         assert pred < j
         first.setdefault(int(node), j)
         last[int(node)] = j
+    for j, pc in enumerate(pcs):
+        node = int(pc[5])
+        assert pc[6] == (1 if first[node] == j else 0) | (2 if last[node] == j else 0)
     assert np.all(covered == 1)
     for j, (t0, ln, pred, sb, se, node, _, _) in enumerate(pcs):
         node = int(node)
@@ -75,5 +78,6 @@ def test_workspace_sizes():
     t = star_tree(100, 3, 70)
     p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, 4, 2, 128, "bf16")
     f, b = p.lin_workspace_size()
-    blk = p.stats()["lin_pieces"] * 2 * 128 * 128 * 4
-    assert f >= 2 * blk and b >= 3 * blk and f % 256 == 0 and b % 256 == 0
+    blk = p.stats()["lin_pieces"] * 2 * 128 * 128 * 2  # bf16 piece states
+    ends = t.num_nodes * 2 * 128 * 128 * 4              # fp32 node states
+    assert f >= 2 * blk + ends and b >= 3 * blk + ends and f % 256 == 0 and b % 256 == 0
