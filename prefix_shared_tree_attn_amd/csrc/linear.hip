@@ -36,24 +36,37 @@ namespace {
 constexpr int CH = kLinChunk;
 
 // Rows 0 .. CH-1 of a token-major tensor (rows `stride` elements apart, D
-// columns from `src`) into a swizzled LDS tile (see Tile); rows at or past n
-// are zero.  16-byte copies: D / 8 per row.
+// columns from `src`), 16 bytes per thread and step, into registers (rows at
+// or past n read as zero) and from there into a swizzled LDS tile (see
+// Tile).  The two halves are separate so that a tile can be fetched while
+// the previous one is in use.
+template <int D>
+struct TileRegs {
+  static constexpr int CPR = D / 8, PER = CH * CPR / 256;
+  i32x4 v[PER];
+  __device__ __forceinline__ void load(const __bf16* src, int64_t stride, int n, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
+      v[i] = i32x4{0, 0, 0, 0};
+      if (r < n) v[i] = gload16(src + r * stride + 8 * cc);
+    }
+  }
+  __device__ __forceinline__ void store(LDS_PTR(char) t, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
+      lds_write16(t, Tile<D, CH>::chunk_off(r, cc), v[i]);
+    }
+  }
+};
+
 template <int D>
 __device__ __forceinline__ void stage_tile(LDS_PTR(char) t, const __bf16* src, int64_t stride,
                                            int n, int tid) {
-  constexpr int CPR = D / 8, PER = CH * CPR / 256;
-  i32x4 v[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
-    v[i] = i32x4{0, 0, 0, 0};
-    if (r < n) v[i] = gload16(src + r * stride + 8 * cc);
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
-    lds_write16(t, Tile<D, CH>::chunk_off(r, cc), v[i]);
-  }
+  TileRegs<D> r;
+  r.load(src, stride, n, tid);
+  r.store(t, tid);
 }
 
 // B operand fragments of a D x D bf16 state W read straight from global
@@ -309,18 +322,31 @@ __global__ __launch_bounds__(256, 2) void lin_chunk_kernel(LinArgs a) {
     __syncthreads();
     inter();
   }
-  for (int j = 0; j < a.gsize; ++j) {
-    const int h = g * a.gsize + j;
-    if constexpr (MODE == 0) stage_tile<D>(xs, Q + h * D, qs, len, tid);
-    if constexpr (MODE == 1) stage_tile<D>(xs, dO + h * D, qs, len, tid);
+  // per-head operands: head j + 1's rows are fetched into registers while
+  // head j is computed
+  TileRegs<D> r1, r2;
+  auto fetch = [&](int h) __attribute__((always_inline)) {
+    if constexpr (MODE == 0) r1.load(Q + h * D, qs, len, tid);
+    if constexpr (MODE == 1) r1.load(dO + h * D, qs, len, tid);
     if constexpr (MODE == 2) {
-      stage_tile<D>(zs, dO + h * D, qs, len, tid);
-      stage_tile<D>(ys, Q + h * D, qs, len, tid);
+      r1.load(dO + h * D, qs, len, tid);
+      r2.load(Q + h * D, qs, len, tid);
     }
     if constexpr (MODE == 3) {
-      stage_tile<D>(zs, Q + h * D, qs, len, tid);
-      stage_tile<D>(ys, dO + h * D, qs, len, tid);
+      r1.load(Q + h * D, qs, len, tid);
+      r2.load(dO + h * D, qs, len, tid);
     }
+  };
+  fetch(g * a.gsize);
+  for (int j = 0; j < a.gsize; ++j) {
+    const int h = g * a.gsize + j;
+    if constexpr (PER_HEAD_X) {
+      r1.store(xs, tid);
+    } else {
+      r1.store(zs, tid);
+      r2.store(ys, tid);
+    }
+    if (j + 1 < a.gsize) fetch(h + 1);
     __syncthreads();
     if constexpr (PER_HEAD_X) inter();
     {
