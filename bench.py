@@ -10,7 +10,10 @@ usual attention convention with the backward's recomputation).
 Prints one JSON line.  Default workload: the GRPO-style star tree (one
 1024-token prompt, 16 responses of 2048 tokens; 32 query / 8 kv heads,
 head dim 128, bf16).  ``--config`` selects another of the five workload
-trees.  Only one GPU is used; ``--gpus`` above 1 is refused.
+trees.  ``--workload linear`` times the chunkwise linear-attention pass over
+the same tree instead (plan + linear forward + linear backward per step),
+with its own metric line.  Only one GPU is used; ``--gpus`` above 1 is
+refused.
 """
 
 from __future__ import annotations
@@ -32,6 +35,8 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_FP32_TFLOPS = 157.3    # dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0
 METRIC = "tree-attn fwd+bwd unique tokens/s and TFLOP/s (% of bf16 MFMA peak), 1 GPU"
+LIN_METRIC = "tree linear-attn fwd+bwd unique tokens/s (chunkwise, state handoffs), 1 GPU"
+LIN_CHUNK = 64
 
 
 def log(msg: str) -> None:
@@ -48,6 +53,8 @@ def _args():
                     help="skip timing the oracle on the host")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--workload", choices=["softmax", "linear"], default="softmax",
+                    help="softmax tree attention (default) or chunkwise linear attention")
     return ap.parse_args()
 
 
@@ -96,6 +103,183 @@ def cpu_baseline(t, spec, budget_heads: int | None = None):
         "sample": (f"kv-head group 0 of {hkv} ({hq // hkv} query heads), full tree, "
                    f"fwd+bwd in fp64: {dt:.2f} s, scaled by {hkv} groups"),
     }
+
+
+def cpu_baseline_linear(t, spec):
+    """Times the fp64 linear-attention oracle on the host over one kv-head
+    group of the same workload and scales it to unique tokens/s."""
+    import oracle
+    from tree_inputs import make_inputs
+    from threadpoolctl import threadpool_info
+    hq, hkv, d = spec["heads_q"], spec["heads_kv"], spec["head_dim"]
+    x = make_inputs(t.num_tokens, hq, hkv, d, dtype=spec["dtype"], do_std=spec["do_std"])
+    t0 = time.perf_counter()
+    oracle.tree_linear_attention(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len,
+                                 spec["scale"], kv_heads=[0])
+    dt = time.perf_counter() - t0
+    threads = sum(int(p.get("num_threads", 0)) for p in threadpool_info()
+                  if p.get("user_api") == "blas") or 1
+    return {
+        "value": t.num_tokens / (dt * hkv),
+        "unit": "unique tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"kv-head group 0 of {hkv} ({hq // hkv} query heads), full tree, linear "
+                   f"attention fwd+bwd in fp64 by path expansion: {dt:.2f} s, scaled by "
+                   f"{hkv} groups"),
+    }
+
+
+def main_linear(args) -> int:
+    """Chunkwise linear attention over the tree: plan + forward + backward."""
+    import torch
+    import prefix_shared_tree_attn_amd as ta
+    from tree_inputs import config_spec, config_tree, make_inputs, tree_stats
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = args.config
+    t = config_tree(cfg)
+    spec = config_spec(cfg)
+    if spec["dtype"] != "bf16":
+        print("the linear-attention pass takes bf16 tensors; choose a bf16 workload",
+              file=sys.stderr)
+        return 2
+    st = tree_stats(t)
+    hq, hkv, d = spec["heads_q"], spec["heads_kv"], spec["head_dim"]
+    scale = spec["scale"]
+    n = t.num_tokens
+    log(f"linear workload {spec['name']}: N={n} nodes={t.num_nodes} hq={hq} hkv={hkv} d={d}")
+    x = make_inputs(n, hq, hkv, d, dtype="bf16", do_std=spec["do_std"])
+
+    def up(name):
+        return torch.from_numpy(x.bits[name].view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = up("q"), up("k"), up("v"), up("do")
+    o = torch.empty_like(q)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    probe = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, "bf16")
+    ws = ta.lin_workspace(probe, "bwd")
+    pstats = probe.stats()
+    probe.close()
+    del x
+    plans = []
+
+    def step():
+        p = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, "bf16")
+        ta.lin_fwd(p, q, k, v, scale, o=o, ws=ws)
+        ta.lin_bwd(p, q, k, v, do, scale, dq=dq, dk=dk, dv=dv, ws=ws)
+        plans.append(p)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for p in plans:
+        p.close()
+    plans.clear()
+    log(f"warmup done ({args.warmup} steps)")
+    ta.timing_read(reset=True)
+    ta.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ta.timing_enable(False)
+    kt = ta.timing_read(reset=True)
+    for p in plans:
+        p.close()
+    plans.clear()
+    log(f"timed {args.steps} steps: {wall:.3f} s")
+    if args.copy_probe_mib > 0:
+        nb = args.copy_probe_mib << 20
+        a = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        log(f"copy probe: {nb} bytes read + {nb} bytes written")
+
+    ms_step = 1e3 * wall / args.steps
+    P, M, C, E = pstats["lin_pieces"], t.num_nodes, LIN_CHUNK, 2
+    sb = P * hkv * d * d * E            # bf16 piece states (or deltas)
+    eb = M * hkv * d * d * 4            # fp32 node-boundary states
+    tq = n * hq * d * E                 # one [N, Hq, D] bf16 tensor
+    tk = n * hkv * d * E                # one [N, Hkv, D] bf16 tensor
+    # algorithmic HBM bytes per launch (each operand read once, each result
+    # written once)
+    kern_bytes = {
+        "lin_kv": 2 * tk + sb,          # K, V -> per-piece K^T V
+        "lin_scan": 2 * sb + eb,        # deltas -> states (+ node ends)
+        "lin_out": sb + tq + 2 * tk + tq,
+        "lin_qdo": 2 * tq + sb,
+        "lin_rscan": 2 * sb + eb,
+        "lin_dq": sb + tq + 2 * tk + tq,
+        "lin_dkdv": sb + 2 * tq + 2 * tk,  # one of dK / dV per launch
+    }
+    # matrix-core work as executed (chunks padded to 64 tokens)
+    f_in = 2.0 * C * d * d               # one chunk x state product
+    f_att = 4.0 * C * C * d               # masked chunk products
+    kern_flop = {
+        "lin_kv": P * hkv * f_in, "lin_scan": 0.0, "lin_out": P * hq * (f_in + f_att),
+        "lin_qdo": P * hq * f_in, "lin_rscan": 0.0, "lin_dq": P * hq * (f_in + f_att),
+        "lin_dkdv": P * hkv * f_in + P * hq * f_att,
+    }
+    step_flop = (2 * kern_flop["lin_kv"] + kern_flop["lin_out"] + kern_flop["lin_qdo"]
+                 + kern_flop["lin_dq"] + 2 * kern_flop["lin_dkdv"])
+
+    def avg_ms(kind):
+        r = kt[kind]
+        return r["total_ms"] / max(r["launches"], 1)
+
+    kinds = [kk for kk in kern_bytes if kt[kk]["launches"]]
+    kname = {"lin_kv": "lin_outer_kernel", "lin_scan": "lin_scan_kernel",
+             "lin_out": "lin_chunk_kernel<128, 0>", "lin_qdo": "lin_outer_kernel",
+             "lin_rscan": "lin_scan_kernel", "lin_dq": "lin_chunk_kernel<128, 1>",
+             "lin_dkdv": "lin_chunk_kernel<128, 2 / 3>"}
+
+    def roof(kind):
+        ach = kern_bytes[kind] / (avg_ms(kind) * 1e-3) / 1e9
+        return {"bound": "hbm", "kernel": kname[kind], "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "bytes_per_launch": kern_bytes[kind],
+                "avg_ms": avg_ms(kind)}
+
+    dominant = max(kinds, key=avg_ms)
+    main_roof = roof(dominant)
+    main_roof["traffic"] = _traffic_from_profile(dominant, spec["name"] + "-linear")
+    result = {
+        "metric": LIN_METRIC,
+        "value": n / (ms_step * 1e-3),
+        "unit": "unique tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{spec['name']} tree, chunkwise linear attention (chunk {C})",
+            "unique_tokens": n, "nodes": t.num_nodes, "pieces": P, "heads_q": hq,
+            "heads_kv": hkv, "head_dim": d, "scale": scale, "global_batch": 1,
+            "seq_len": st["max_path"], "parallelism": "none (1 GPU)",
+        },
+        "tflops": step_flop / (ms_step * 1e-3) / 1e12,
+        "kernels_ms": {kk: avg_ms(kk) for kk in kinds},
+        "roofline": main_roof,
+        "roofline_kernels": {kk: roof(kk) for kk in kinds},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the linear-attention oracle on the host (cpu baseline)")
+        result["cpu_baseline"] = cpu_baseline_linear(t, spec)
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def _passes_around_attention(ta, torch, t, o, q, k, pos_id, do, hq, hkv, d, reps=5):
@@ -170,6 +354,8 @@ def main() -> int:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the path is single-GPU; multi-GPU sharding is design-only)", file=sys.stderr)
         return 2
+    if args.workload == "linear":
+        return main_linear(args)
     import torch
     import prefix_shared_tree_attn_amd as ta
     from tree_inputs import config_spec, config_tree, make_inputs, tree_stats
@@ -276,8 +462,11 @@ def main() -> int:
     # dS through an atomic reduction.
     kern_flop = {"fwd": 4.0 * d * hq * pairs, "bwd_dkdv": 8.0 * d * hq * pairs,
                  "bwd_dq": 6.0 * d * hq * pairs}
-    kern_name = {"fwd": "tree_attn_fwd_kernel", "bwd_dkdv": "tree_attn_dkdv_kernel",
-                 "bwd_dq": "tree_attn_dq_kernel"}
+    pipe = dtype == "bf16"
+    kern_name = {"fwd": f"tree_attn_fwd_kernel<{'bf16' if pipe else 'float'}, {d}>",
+                 "bwd_dkdv": (f"tree_attn_dkdv_pipe_kernel<{d}>" if pipe
+                              else f"tree_attn_dkdv_kernel<float, {d}>"),
+                 "bwd_dq": f"tree_attn_dq_kernel<{'bf16' if pipe else 'float'}, {d}>"}
 
     def roof(kind):
         ach = kern_flop[kind] / (avg_ms(kind) * 1e-3) / 1e12

@@ -68,14 +68,16 @@ def causal_linear_attention(q, k, v, do, scale: float):
     return o, g @ k, g.T @ q, a.T @ do
 
 
-def tree_linear_attention(q, k, v, do, parent, seg_start, seg_len,
-                          scale: float) -> Dict[str, np.ndarray]:
+def tree_linear_attention(q, k, v, do, parent, seg_start, seg_len, scale: float,
+                          kv_heads=None) -> Dict[str, np.ndarray]:
     """Forward and backward of tree linear attention by path expansion, fp64.
 
     ``q, do``: [N, Hq, D]; ``k, v``: [N, Hkv, D]; node table as in the
-    library.  Returns ``o, dq [N,Hq,D]``, ``dk, dv [N,Hkv,D]``, ``mult [N]``
-    and ``path_spread``, the largest difference between two paths' outputs
-    for the same token.
+    library.  ``kv_heads`` restricts the work to those kv-head groups (all
+    query heads of each group); entries of other heads are NaN.  Returns
+    ``o, dq [N,Hq,D]``, ``dk, dv [N,Hkv,D]``, ``mult [N]`` and
+    ``path_spread``, the largest difference between two paths' outputs for
+    the same token.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -93,14 +95,22 @@ def tree_linear_attention(q, k, v, do, parent, seg_start, seg_len,
     if n and mult.min() < 1:
         raise ValueError("some token lies on no root-to-leaf path")
     inv_mult = 1.0 / mult.astype(np.float64)
-    o = np.zeros((n, hq, d))
-    dq = np.zeros((n, hq, d))
-    dk = np.zeros((n, hkv, d))
-    dv = np.zeros((n, hkv, d))
+    groups = set(range(hkv) if kv_heads is None else kv_heads)
+    o = np.full((n, hq, d), np.nan)
+    dq = np.full((n, hq, d), np.nan)
+    dk = np.full((n, hkv, d), np.nan)
+    dv = np.full((n, hkv, d), np.nan)
+    for g in groups:
+        o[:, g * gs:(g + 1) * gs] = 0.0
+        dq[:, g * gs:(g + 1) * gs] = 0.0
+        dk[:, g] = 0.0
+        dv[:, g] = 0.0
     seen = np.zeros((n, hq), bool)
     spread = 0.0
     for h in range(hq):
         g = h // gs
+        if g not in groups:
+            continue
         for p in paths:
             op, dqp, dkp, dvp = causal_linear_attention(
                 q[p, h], k[p, g], v[p, g], do[p, h] * inv_mult[p][:, None], scale)

@@ -166,6 +166,9 @@ __device__ __forceinline__ I4 load_plan4(const I4* p, int64_t i) {
   CONST_PTR(int) q = (CONST_PTR(int))(p) + 4 * i;
   return {q[0], q[1], q[2], q[3]};
 }
+__device__ __forceinline__ int load_plan1(const int32_t* p, int64_t i) {
+  return *((CONST_PTR(int))(p) + i);
+}
 __device__ __forceinline__ I8 load_plan8(const I8* p, int64_t i) {
   CONST_PTR(int) q = (CONST_PTR(int))(p) + 8 * i;
   I8 r;

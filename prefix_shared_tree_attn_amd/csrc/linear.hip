@@ -175,46 +175,48 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(LinArgs a, int backward) 
   const int64_t np = a.n_pieces;
   const __bf16* delta = static_cast<const __bf16*>(a.delta);
   __bf16* state = static_cast<__bf16*>(a.state);
-  constexpr int LA = 8;  // deltas loaded ahead
-  int cached = -1;
-  float r0 = 0.f, r1 = 0.f;  // state + delta of piece `cached`
+  const int in_node = backward ? 2 : 1;   // flag: the neighbour lies outside the node
+  const int end_flag = backward ? 1 : 2;  // flag: write this piece's value to `ends`
+  // Pieces go in batches of LA: the batch's plan entries are loaded together,
+  // and its deltas one batch ahead.
+  constexpr int LA = 8;
+  auto piece_of = [&](int64_t i) { return backward ? np - 1 - i : i; };
+  auto load_deltas = [&](int64_t b, bf16x2 (&dl)[LA]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < LA; ++u)
+      dl[u] = b + u < np ? *reinterpret_cast<const bf16x2*>(delta + piece_of(b + u) * per + e)
+                         : bf16x2{};
+  };
+  auto ends_at = [&](int piece) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f32x2*>(a.ends + load_plan8(a.pieces, piece).v[5] * per + e);
+  };
+  float r0 = 0.f, r1 = 0.f;  // running value: state + delta of the piece just done
+  bf16x2 dl[LA], dn[LA];
+  load_deltas(0, dl);
   for (int64_t b = 0; b < np; b += LA) {
-    bf16x2 dl[LA];
+    load_deltas(b + LA, dn);
+    I8 pcs[LA];
+#pragma unroll
+    for (int u = 0; u < LA; ++u)
+      if (b + u < np) pcs[u] = load_plan8(a.pieces, piece_of(b + u));
 #pragma unroll
     for (int u = 0; u < LA; ++u) {
-      const int64_t i = b + u;
-      const int64_t p = backward ? np - 1 - i : i;
-      dl[u] = i < np ? *reinterpret_cast<const bf16x2*>(delta + p * per + e) : bf16x2{};
-    }
-#pragma unroll
-    for (int u = 0; u < LA; ++u) {
-      const int64_t i = b + u;
-      if (i >= np) break;
-      const int p = static_cast<int>(backward ? np - 1 - i : i);
-      const I8 pc = load_plan8(a.pieces, p);
-      float s0 = 0.f, s1 = 0.f;
-      if (!backward) {
-        const int pr = pc.v[2];
-        if (pr >= 0) {
-          if (pr == cached) {
-            s0 = r0;
-            s1 = r1;
-          } else {
-            const f32x2 x = *reinterpret_cast<const f32x2*>(
-                a.ends + load_plan8(a.pieces, pr).v[5] * per + e);
+      if (b + u >= np) break;
+      const int p = static_cast<int>(piece_of(b + u));
+      const I8& pc = pcs[u];
+      float s0 = r0, s1 = r1;  // the in-node neighbour is the piece just done
+      if (pc.v[6] & in_node) {
+        s0 = s1 = 0.f;
+        if (!backward) {
+          const int pr = pc.v[2];  // the parent's last piece, or none at a root
+          if (pr >= 0) {
+            const f32x2 x = ends_at(pr);
             s0 = x[0];
             s1 = x[1];
           }
-        }
-      } else {
-        for (int j = pc.v[3]; j < pc.v[4]; ++j) {
-          const int c = a.succ[j];
-          if (c == cached) {
-            s0 += r0;
-            s1 += r1;
-          } else {
-            const f32x2 x = *reinterpret_cast<const f32x2*>(
-                a.ends + load_plan8(a.pieces, c).v[5] * per + e);
+        } else {
+          for (int j = pc.v[3]; j < pc.v[4]; ++j) {  // the children's first pieces
+            const f32x2 x = ends_at(load_plan1(a.succ, j));
             s0 += x[0];
             s1 += x[1];
           }
@@ -224,16 +226,17 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(LinArgs a, int backward) 
       out[0] = to_bf16(s0);
       out[1] = to_bf16(s1);
       *reinterpret_cast<bf16x2*>(state + p * per + e) = out;
-      cached = p;
       r0 = s0 + static_cast<float>(dl[u][0]);
       r1 = s1 + static_cast<float>(dl[u][1]);
-      if (pc.v[6] & (backward ? 1 : 2)) {
+      if (pc.v[6] & end_flag) {
         f32x2 w;
         w[0] = r0;
         w[1] = r1;
         *reinterpret_cast<f32x2*>(a.ends + pc.v[5] * per + e) = w;
       }
     }
+#pragma unroll
+    for (int u = 0; u < LA; ++u) dl[u] = dn[u];
   }
 }
 

@@ -186,3 +186,15 @@ def test_sampled_rows_match_full_expansion(seed):
                                         rows, g)
         _close(dk, r["dk"][rows, g])
         _close(dv, r["dv"][rows, g])
+
+
+def test_kv_head_restriction():
+    rng = np.random.default_rng(21)
+    t = star_tree(5, 3, 4)
+    q, k, v, do = _rand(rng, t.num_tokens, 4, 2, 3)
+    full = _lin(t, q, k, v, do, 0.5)
+    part = oracle.tree_linear_attention(q, k, v, do, t.parent, t.seg_start, t.seg_len, 0.5,
+                                        kv_heads=[1])
+    _close(part["o"][:, 2:], full["o"][:, 2:])
+    _close(part["dk"][:, 1], full["dk"][:, 1])
+    assert np.isnan(part["o"][:, :2]).all() and np.isnan(part["dv"][:, 0]).all()
