@@ -33,6 +33,7 @@ struct tree_attn_plan_s {
   const I4* d_segments = nullptr;
   const I8* d_lin_pieces = nullptr;
   const int32_t* d_lin_succ = nullptr;
+  const I4* d_lin_nodes = nullptr;
 };
 
 namespace {
@@ -208,7 +209,8 @@ tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_star
   const size_t o_sg = o_br + align256(bytes_of(hp.bwd_reduce));
   const size_t o_lp = o_sg + align256(bytes_of(hp.segments));
   const size_t o_ls = o_lp + align256(bytes_of(hp.lin_pieces));
-  const size_t total = o_ls + align256(bytes_of(hp.lin_succ));
+  const size_t o_ln = o_ls + align256(bytes_of(hp.lin_succ));
+  const size_t total = o_ln + align256(bytes_of(hp.lin_nodes));
   if (total > 0) {
     e = hipMalloc(reinterpret_cast<void**>(&p->dev_buf), total);
     if (e != hipSuccess) {
@@ -226,7 +228,8 @@ tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_star
                  {o_br, hp.bwd_reduce.data(), bytes_of(hp.bwd_reduce)},
                  {o_sg, hp.segments.data(), bytes_of(hp.segments)},
                  {o_lp, hp.lin_pieces.data(), bytes_of(hp.lin_pieces)},
-                 {o_ls, hp.lin_succ.data(), bytes_of(hp.lin_succ)}};
+                 {o_ls, hp.lin_succ.data(), bytes_of(hp.lin_succ)},
+                 {o_ln, hp.lin_nodes.data(), bytes_of(hp.lin_nodes)}};
     for (const Part& part : parts) {
       if (part.n == 0) continue;
       e = hipMemcpyAsync(p->dev_buf + part.off, part.src, part.n, hipMemcpyHostToDevice, stream);
@@ -245,6 +248,7 @@ tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_star
   p->d_segments = reinterpret_cast<const I4*>(p->dev_buf + o_sg);
   p->d_lin_pieces = reinterpret_cast<const I8*>(p->dev_buf + o_lp);
   p->d_lin_succ = reinterpret_cast<const int32_t*>(p->dev_buf + o_ls);
+  p->d_lin_nodes = reinterpret_cast<const I4*>(p->dev_buf + o_ln);
   p->has_device = true;
   p->device = dev;
   *out = p;
@@ -399,7 +403,9 @@ tree_attn::LinArgs lin_args(tree_attn_plan_t plan, float scale) {
   tree_attn::LinArgs a{};
   a.pieces = plan->d_lin_pieces;
   a.succ = plan->d_lin_succ;
+  a.lnodes = plan->d_lin_nodes;
   a.n_pieces = static_cast<int64_t>(hp.lin_pieces.size());
+  a.n_nodes = static_cast<int64_t>(hp.lin_nodes.size());
   a.hq = static_cast<int>(hp.hq);
   a.hkv = static_cast<int>(hp.hkv);
   a.gsize = static_cast<int>(hp.hq / hp.hkv);

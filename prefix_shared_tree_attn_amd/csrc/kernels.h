@@ -72,7 +72,9 @@ struct LinArgs {
                          // or with its first piece's delta added (backward)
   const I8* pieces;      // (token0, len, pred, succ_begin, succ_end, node, flags, 0)
   const int32_t* succ;   // successor piece indices
+  const I4* lnodes;      // (first piece, pieces, parent node, node) root first
   int64_t n_pieces;
+  int64_t n_nodes;
   int hq, hkv, gsize;
   float scale;
 };

@@ -154,16 +154,18 @@ __global__ __launch_bounds__(256) void lin_outer_kernel(LinArgs a, int backward)
   }
 }
 
-// (2) State scan over the pieces, one thread per two neighbouring (kv head,
-// state element) pairs, accumulating in fp32.  Forward, in root-first order: the state entering
-// piece p is that of its predecessor plus the predecessor's delta (zero at a
-// root).  Backward, in reverse: the state gradient leaving piece p is the sum
-// over its successors c of (state leaving c + delta of c) (zero at a leaf).
-// The running value of the piece just done stays in a register; it is the
-// predecessor (forward) or the one in-node successor (backward) of the next
-// piece except at branch points, whose values go through `ends` in fp32: the
-// state at the end of each node (forward), or the state entering each node's
-// first piece (backward).  The consumers read the states as bf16.
+// (2) State scan, one thread per two neighbouring (kv head, state element)
+// pairs, accumulating in fp32.  Nodes go in root-first order (forward) or
+// its reverse (backward); inside a node the pieces form a chain, streamed
+// with their sums fetched LA pieces ahead.
+//   Forward: the state entering a node's first piece is the state at its
+//   parent's end (zero at a root); each piece's entering state is stored,
+//   then its sum added; the node's end state goes to `ends`.
+//   Backward: the gradient leaving a node's last piece is the sum of what
+//   its children hand up (zero at a leaf); walking the chain backwards, each
+//   piece's leaving gradient is stored, then its sum added; what is left is
+//   handed to the parent through `ends`.
+// The chunk kernels read the stored states as bf16.
 template <int D>
 __global__ __launch_bounds__(256) void lin_scan_kernel(LinArgs a, int backward) {
   typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
@@ -172,71 +174,60 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(LinArgs a, int backward) 
   // two neighbouring elements per thread: 4-byte bf16 accesses
   const int64_t e = 2 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
   if (e >= per) return;
-  const int64_t np = a.n_pieces;
   const __bf16* delta = static_cast<const __bf16*>(a.delta);
   __bf16* state = static_cast<__bf16*>(a.state);
-  const int in_node = backward ? 2 : 1;   // flag: the neighbour lies outside the node
-  const int end_flag = backward ? 1 : 2;  // flag: write this piece's value to `ends`
-  // Pieces go in batches of LA: the batch's plan entries are loaded together,
-  // and its deltas one batch ahead.
-  constexpr int LA = 8;
-  auto piece_of = [&](int64_t i) { return backward ? np - 1 - i : i; };
-  auto load_deltas = [&](int64_t b, bf16x2 (&dl)[LA]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < LA; ++u)
-      dl[u] = b + u < np ? *reinterpret_cast<const bf16x2*>(delta + piece_of(b + u) * per + e)
-                         : bf16x2{};
-  };
-  auto ends_at = [&](int piece) __attribute__((always_inline)) {
-    return *reinterpret_cast<const f32x2*>(a.ends + load_plan8(a.pieces, piece).v[5] * per + e);
-  };
-  float r0 = 0.f, r1 = 0.f;  // running value: state + delta of the piece just done
-  bf16x2 dl[LA], dn[LA];
-  load_deltas(0, dl);
-  for (int64_t b = 0; b < np; b += LA) {
-    load_deltas(b + LA, dn);
-    I8 pcs[LA];
-#pragma unroll
-    for (int u = 0; u < LA; ++u)
-      if (b + u < np) pcs[u] = load_plan8(a.pieces, piece_of(b + u));
-#pragma unroll
-    for (int u = 0; u < LA; ++u) {
-      if (b + u >= np) break;
-      const int p = static_cast<int>(piece_of(b + u));
-      const I8& pc = pcs[u];
-      float s0 = r0, s1 = r1;  // the in-node neighbour is the piece just done
-      if (pc.v[6] & in_node) {
-        s0 = s1 = 0.f;
-        if (!backward) {
-          const int pr = pc.v[2];  // the parent's last piece, or none at a root
-          if (pr >= 0) {
-            const f32x2 x = ends_at(pr);
-            s0 = x[0];
-            s1 = x[1];
-          }
-        } else {
-          for (int j = pc.v[3]; j < pc.v[4]; ++j) {  // the children's first pieces
-            const f32x2 x = ends_at(load_plan1(a.succ, j));
-            s0 += x[0];
-            s1 += x[1];
-          }
-        }
+  constexpr int LA = 16;
+  const int nn = static_cast<int>(a.n_nodes);
+  for (int k = 0; k < nn; ++k) {
+    const I4 nd = load_plan4(a.lnodes, backward ? nn - 1 - k : k);
+    const int first = nd.x, count = nd.y;
+    float s0 = 0.f, s1 = 0.f;
+    if (!backward) {
+      if (nd.z >= 0) {
+        const f32x2 x = *reinterpret_cast<const f32x2*>(a.ends + nd.z * per + e);
+        s0 = x[0];
+        s1 = x[1];
       }
-      bf16x2 out;
-      out[0] = to_bf16(s0);
-      out[1] = to_bf16(s1);
-      *reinterpret_cast<bf16x2*>(state + p * per + e) = out;
-      r0 = s0 + static_cast<float>(dl[u][0]);
-      r1 = s1 + static_cast<float>(dl[u][1]);
-      if (pc.v[6] & end_flag) {
-        f32x2 w;
-        w[0] = r0;
-        w[1] = r1;
-        *reinterpret_cast<f32x2*>(a.ends + pc.v[5] * per + e) = w;
+    } else {
+      const I8 lp = load_plan8(a.pieces, first + count - 1);
+      for (int j = lp.v[3]; j < lp.v[4]; ++j) {  // the children's first pieces
+        const int child = load_plan8(a.pieces, load_plan1(a.succ, j)).v[5];
+        const f32x2 x = *reinterpret_cast<const f32x2*>(a.ends + child * per + e);
+        s0 += x[0];
+        s1 += x[1];
       }
     }
+    // the chain: i-th piece visited is first + i (forward) or last - i
+    auto piece = [&](int i) { return backward ? first + count - 1 - i : first + i; };
+    bf16x2 dl[LA], dn[LA];
 #pragma unroll
-    for (int u = 0; u < LA; ++u) dl[u] = dn[u];
+    for (int u = 0; u < LA; ++u)
+      dl[u] = u < count ? *reinterpret_cast<const bf16x2*>(delta + piece(u) * per + e)
+                        : bf16x2{};
+    for (int i0 = 0; i0 < count; i0 += LA) {
+#pragma unroll
+      for (int u = 0; u < LA; ++u) {
+        const int i = i0 + LA + u;
+        dn[u] = i < count ? *reinterpret_cast<const bf16x2*>(delta + piece(i) * per + e)
+                          : bf16x2{};
+      }
+#pragma unroll
+      for (int u = 0; u < LA; ++u) {
+        if (i0 + u >= count) break;
+        bf16x2 out;
+        out[0] = to_bf16(s0);
+        out[1] = to_bf16(s1);
+        *reinterpret_cast<bf16x2*>(state + piece(i0 + u) * per + e) = out;
+        s0 += static_cast<float>(dl[u][0]);
+        s1 += static_cast<float>(dl[u][1]);
+      }
+#pragma unroll
+      for (int u = 0; u < LA; ++u) dl[u] = dn[u];
+    }
+    f32x2 w;
+    w[0] = s0;
+    w[1] = s1;
+    *reinterpret_cast<f32x2*>(a.ends + nd.w * per + e) = w;
   }
 }
 

@@ -60,6 +60,8 @@ void build_lin_pieces(const int32_t* parent, const int32_t* seg_start, const int
       d += len;
     }
     last[i] = pred;
+    out->lin_nodes.push_back({first[i], pred - first[i] + 1,
+                              parent[i] >= 0 ? parent[i] : -1, i});
   }
   std::vector<int32_t>& sc = out->lin_succ;
   for (size_t j = 0; j < pc.size(); ++j) {

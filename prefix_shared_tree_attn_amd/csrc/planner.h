@@ -76,6 +76,9 @@ struct HostPlan {
   // pred = -1 at a root; successor piece indices
   std::vector<I8> lin_pieces;
   std::vector<int32_t> lin_succ;
+  // nodes in the same root-first order: (first piece, pieces, parent node or
+  // -1, node)
+  std::vector<I4> lin_nodes;
 };
 
 // Validates the table and fills `out`.  On error returns the status and a
