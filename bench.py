@@ -219,7 +219,7 @@ def main_linear(args) -> int:
         "lin_qdo": 2 * tq + sb,
         "lin_rscan": 2 * sb + eb,
         "lin_dq": sb + tq + 2 * tk + tq,
-        "lin_dkdv": sb + 2 * tq + 2 * tk,  # one of dK / dV per launch
+        "lin_dkdv": sb + 2 * tq + 4 * tk,  # R, Q, dO, K, V -> dK, dV
     }
     # matrix-core work as executed (chunks padded to 64 tokens)
     f_in = 2.0 * C * d * d               # one chunk x state product
@@ -227,10 +227,10 @@ def main_linear(args) -> int:
     kern_flop = {
         "lin_kv": P * hkv * f_in, "lin_scan": 0.0, "lin_out": P * hq * (f_in + f_att),
         "lin_qdo": P * hq * f_in, "lin_rscan": 0.0, "lin_dq": P * hq * (f_in + f_att),
-        "lin_dkdv": P * hkv * f_in + P * hq * f_att,
+        "lin_dkdv": 2 * (P * hkv * f_in + P * hq * f_att),
     }
     step_flop = (2 * kern_flop["lin_kv"] + kern_flop["lin_out"] + kern_flop["lin_qdo"]
-                 + kern_flop["lin_dq"] + 2 * kern_flop["lin_dkdv"])
+                 + kern_flop["lin_dq"] + kern_flop["lin_dkdv"])
 
     def avg_ms(kind):
         r = kt[kind]
@@ -240,7 +240,7 @@ def main_linear(args) -> int:
     kname = {"lin_kv": "lin_outer_kernel", "lin_scan": "lin_scan_kernel",
              "lin_out": "lin_chunk_kernel<128, 0>", "lin_qdo": "lin_outer_kernel",
              "lin_rscan": "lin_scan_kernel", "lin_dq": "lin_chunk_kernel<128, 1>",
-             "lin_dkdv": "lin_chunk_kernel<128, 2 / 3>"}
+             "lin_dkdv": "lin_dkdv_kernel<128>"}
 
     def roof(kind):
         ach = kern_bytes[kind] / (avg_ms(kind) * 1e-3) / 1e9

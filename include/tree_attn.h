@@ -370,7 +370,7 @@ tree_attn_status_t tree_attn_lin_plan_export(tree_attn_plan_t plan, int32_t* pie
  * 8 rotary embedding, 9 linear-attention piece sums K^T V (forward and
  * the backward's recomputation), 10 its state scan, 11 linear-attention
  * output, 12 piece sums Q^T dO, 13 state-gradient scan, 14 linear-attention
- * dQ, 15 linear-attention dK and dV (two launches).  Timing is
+ * dQ, 15 linear-attention dK and dV.  Timing is
  * process-wide and not meant for concurrent callers.
  */
 typedef struct {

@@ -479,11 +479,8 @@ tree_attn_status_t tree_attn_lin_bwd(tree_attn_plan_t plan, const void* q, const
     e = timed(13, stream, [&] { return tree_attn::launch_lin_scan(a, 1, hd, stream); });
   if (e == hipSuccess) {
     a.out = dk;
-    e = timed(15, stream, [&] { return tree_attn::launch_lin_chunk(a, 2, hd, stream); });
-  }
-  if (e == hipSuccess) {
-    a.out = dv;
-    e = timed(15, stream, [&] { return tree_attn::launch_lin_chunk(a, 3, hd, stream); });
+    a.out2 = dv;
+    e = timed(15, stream, [&] { return tree_attn::launch_lin_chunk(a, 4, hd, stream); });
   }
   if (e != hipSuccess) return report_hip(e, "linear attention backward launch");
   return TREE_ATTN_OK;

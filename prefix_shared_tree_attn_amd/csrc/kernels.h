@@ -65,7 +65,8 @@ struct LinArgs {
   const void* k;
   const void* v;
   const void* dout;
-  void* out;             // chunk products: O, dQ, dK or dV
+  void* out;             // chunk products: O, dQ or dK
+  void* out2;            // dV (the fused dK / dV kernel)
   void* state;           // bf16 [pieces, Hkv, D, D] S (forward) or R (backward)
   void* delta;           // bf16 [pieces, Hkv, D, D] K^T V or sum_h Q_h^T dO_h per piece
   float* ends;           // [nodes, Hkv, D, D] fp32 state at a node's end (forward)
@@ -88,7 +89,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int head_dim, hipStream_t 
 hipError_t launch_bwd_post(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_positions(const PosArgs& a, hipStream_t stream);
 // backward = 0: delta = K^T V, state scan root first; backward = 1: delta =
-// sum_h Q_h^T dO_h, state scan leaves first.  mode: 0 O, 1 dQ, 2 dK, 3 dV.
+// sum_h Q_h^T dO_h, state scan leaves first.  mode: 0 O, 1 dQ, 4 dK and dV.
 hipError_t launch_lin_outer(const LinArgs& a, int backward, int head_dim, hipStream_t stream);
 hipError_t launch_lin_scan(const LinArgs& a, int backward, int head_dim, hipStream_t stream);
 hipError_t launch_lin_chunk(const LinArgs& a, int mode, int head_dim, hipStream_t stream);

@@ -231,24 +231,21 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(LinArgs a, int backward) 
   }
 }
 
-// (3) Chunk products, one workgroup per (piece, kv head g), a loop over the
-// query heads of the group.  With X, Z, Y the piece's rows of three operands,
-// W a D x D state and M the causal mask,
+// (3) Chunk products for O and dQ, one workgroup per (piece, kv head g), a
+// loop over the query heads of the group.  With X, Z, Y the piece's rows of
+// three operands, W a D x D state and M the causal mask (key <= query),
 //   out = scale (X W^T + (M o X Z^T) Y)          (W^T: W read as B^T)
-//   OUT: X = Q_h,  W = S^T, Z = K,    Y = V,    M: key <= query, out = O_h
-//   DQ : X = dO_h, W = S,   Z = V,    Y = K,    M: key <= query, out = dQ_h
-//   DK : X = V,    W = R,   Z = dO_h, Y = Q_h,  M: query >= key, out = dK
-//   DV : X = K,    W = R^T, Z = Q_h,  Y = dO_h, M: query >= key, out = dV
-// (DK and DV summed over the group's heads).  X, Z, Y sit row-major in
-// swizzled LDS tiles: X and Z feed X Z^T as row operands, Y feeds the second
-// product as transposed operands.  The state fragments (bf16) come from
-// global memory once per workgroup and stay in registers.  Wave w owns output
-// blocks w and w + 4 (rows 0 and 32 of column block w) at D = 128, block w
-// at D = 64, and one 32 x 32 block of M o X Z^T, which goes to LDS as bf16.
+//   OUT: X = Q_h,  W = S^T, Z = K, Y = V, out = O_h
+//   DQ : X = dO_h, W = S,   Z = V, Y = K, out = dQ_h
+// X, Z, Y sit row-major in swizzled LDS tiles: X and Z feed X Z^T as row
+// operands, Y feeds the second product as transposed operands.  The state
+// fragments (bf16) come from global memory once per workgroup and stay in
+// registers.  Wave w owns output blocks w and w + 4 (rows 0 and 32 of
+// column block w) at D = 128, block w at D = 64, and one 32 x 32 block of
+// M o X Z^T, which goes to LDS as bf16.
 template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void lin_chunk_kernel(LinArgs a) {
-  constexpr bool PER_HEAD_X = MODE < 2;  // OUT, DQ: X changes with the head
-  constexpr bool W_TR = MODE == 0 || MODE == 3;
+  static_assert(MODE == 0 || MODE == 1, "O or dQ");
   using T = Tile<D, CH>;    // CH tokens x D
   using TA = Tile<CH, CH>;  // masked X Z^T
   constexpr int NBN = D / 32, NB = 2 * NBN, PER = NB / 4, KD = D / 16;
@@ -264,32 +261,30 @@ __global__ __launch_bounds__(256, 2) void lin_chunk_kernel(LinArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t qs = static_cast<int64_t>(a.hq) * D, ks = static_cast<int64_t>(a.hkv) * D;
-  const __bf16* Q = static_cast<const __bf16*>(a.q) + static_cast<int64_t>(tok0) * qs;
-  const __bf16* dO = static_cast<const __bf16*>(a.dout) + static_cast<int64_t>(tok0) * qs;
+  // X rows of the group's heads, Z and Y rows of kv head g
+  const __bf16* X = static_cast<const __bf16*>(MODE == 0 ? a.q : a.dout) +
+                    static_cast<int64_t>(tok0) * qs;
   const __bf16* K = static_cast<const __bf16*>(a.k) + static_cast<int64_t>(tok0) * ks + g * D;
   const __bf16* V = static_cast<const __bf16*>(a.v) + static_cast<int64_t>(tok0) * ks + g * D;
   const __bf16* st =
       static_cast<const __bf16*>(a.state) + (static_cast<int64_t>(p) * a.hkv + g) * D * D;
 
-  // head-independent operands
-  if constexpr (MODE == 0) {
-    stage_tile<D>(zs, K, ks, len, tid);
-    stage_tile<D>(ys, V, ks, len, tid);
-  } else if constexpr (MODE == 1) {
-    stage_tile<D>(zs, V, ks, len, tid);
-    stage_tile<D>(ys, K, ks, len, tid);
-  } else if constexpr (MODE == 2) {
-    stage_tile<D>(xs, V, ks, len, tid);
-  } else {
-    stage_tile<D>(xs, K, ks, len, tid);
-  }
+  stage_tile<D>(zs, MODE == 0 ? K : V, ks, len, tid);
+  stage_tile<D>(ys, MODE == 0 ? V : K, ks, len, tid);
   // this wave's output column block and its state fragments
   const int n0 = 32 * (wave % NBN);
   bf16x8 wf[KD];
-  state_frags<D, W_TR>(wf, st, n0, lane);
+  state_frags<D, MODE == 0>(wf, st, n0, lane);
 
+  // head j + 1's rows are fetched into registers while head j is computed
+  TileRegs<D> rx;
+  rx.load(X + g * a.gsize * D, qs, len, tid);
   f32x16 acc[PER];
-  auto inter = [&]() __attribute__((always_inline)) {
+  for (int j = 0; j < a.gsize; ++j) {
+    const int h = g * a.gsize + j;
+    rx.store(xs, tid);
+    if (j + 1 < a.gsize) rx.load(X + (h + 1) * D, qs, len, tid);
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int m0 = 32 * ((wave + 4 * i) / NBN);
@@ -299,50 +294,6 @@ __global__ __launch_bounds__(256, 2) void lin_chunk_kernel(LinArgs a) {
       for (int kk = 0; kk < KD; ++kk)
         acc[i] = mfma32(row_operand<T>(xs, m0 + l32, 2 * kk + half), wf[kk], acc[i]);
     }
-  };
-  auto store = [&](__bf16* out, int64_t stride) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int m0 = 32 * ((wave + 4 * i) / NBN);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = m0 + acc_row(v, lane);
-        if (r < len) out[r * stride + n0 + l32] = to_bf16(a.scale * acc[i][v]);
-      }
-    }
-  };
-
-  if constexpr (!PER_HEAD_X) {
-    __syncthreads();
-    inter();
-  }
-  // per-head operands: head j + 1's rows are fetched into registers while
-  // head j is computed
-  TileRegs<D> r1, r2;
-  auto fetch = [&](int h) __attribute__((always_inline)) {
-    if constexpr (MODE == 0) r1.load(Q + h * D, qs, len, tid);
-    if constexpr (MODE == 1) r1.load(dO + h * D, qs, len, tid);
-    if constexpr (MODE == 2) {
-      r1.load(dO + h * D, qs, len, tid);
-      r2.load(Q + h * D, qs, len, tid);
-    }
-    if constexpr (MODE == 3) {
-      r1.load(Q + h * D, qs, len, tid);
-      r2.load(dO + h * D, qs, len, tid);
-    }
-  };
-  fetch(g * a.gsize);
-  for (int j = 0; j < a.gsize; ++j) {
-    const int h = g * a.gsize + j;
-    if constexpr (PER_HEAD_X) {
-      r1.store(xs, tid);
-    } else {
-      r1.store(zs, tid);
-      r2.store(ys, tid);
-    }
-    if (j + 1 < a.gsize) fetch(h + 1);
-    __syncthreads();
-    if constexpr (PER_HEAD_X) inter();
     {
       // one 32x32 block of M o X Z^T per wave, to LDS as bf16
       const int bi = wave >> 1, bj = wave & 1;
@@ -357,11 +308,11 @@ __global__ __launch_bounds__(256, 2) void lin_chunk_kernel(LinArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = 32 * bi + acc_row(v, lane);
-        const bool keep = PER_HEAD_X ? c <= r : c >= r;
-        *reinterpret_cast<LDS_PTR(__bf16)>(as + TA::elem_off(r, c)) = to_bf16(keep ? t[v] : 0.f);
+        *reinterpret_cast<LDS_PTR(__bf16)>(as + TA::elem_off(r, c)) = to_bf16(c <= r ? t[v] : 0.f);
       }
     }
     __syncthreads();
+    __bf16* out = static_cast<__bf16*>(a.out) + static_cast<int64_t>(tok0) * qs + h * D;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int m0 = 32 * ((wave + 4 * i) / NBN);
@@ -369,31 +320,145 @@ __global__ __launch_bounds__(256, 2) void lin_chunk_kernel(LinArgs a) {
       for (int kk = 0; kk < CH / 16; ++kk)
         acc[i] = mfma32(row_operand<TA>(as, m0 + l32, 2 * kk + half),
                         tr_operand<T>(ys, 16 * kk, n0, lane), acc[i]);
-    }
-    if constexpr (PER_HEAD_X) {
-      __bf16* out = static_cast<__bf16*>(a.out) + static_cast<int64_t>(tok0) * qs + h * D;
-      store(out, qs);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = m0 + acc_row(v, lane);
+        if (r < len) out[r * qs + n0 + l32] = to_bf16(a.scale * acc[i][v]);
+      }
     }
     __syncthreads();  // before the next head overwrites the staged operands
   }
-  if constexpr (!PER_HEAD_X) {
-    __bf16* out = static_cast<__bf16*>(a.out) + static_cast<int64_t>(tok0) * ks + g * D;
-    store(out, ks);
+}
+
+// (3') dK and dV in one pass, one workgroup per (piece, kv head g):
+//   dK = scale (V R^T + sum_h (M o V dO_h^T) Q_h)
+//   dV = scale (K R   + sum_h (M o K Q_h^T) dO_h),   M: query >= key,
+// which share the per-head rows Q_h and dO_h, fetched once.  Tiles: V, K (fixed), dO_h, Q_h, and the two
+// masked blocks V dO_h^T and K Q_h^T (80 KiB at D = 128, two workgroups per
+// CU).  Each wave holds its dK and dV output blocks and the R fragments of
+// both orientations.
+template <int D>
+__global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(LinArgs a) {
+  using T = Tile<D, CH>;
+  using TA = Tile<CH, CH>;
+  constexpr int NBN = D / 32, NB = 2 * NBN, PER = NB / 4, KD = D / 16;
+  extern __shared__ __attribute__((aligned(16))) char smem_dyn[];
+  LDS_PTR(char) vs = (LDS_PTR(char))(smem_dyn);
+  LDS_PTR(char) kt = (LDS_PTR(char))(smem_dyn + T::BYTES);
+  LDS_PTR(char) dos = (LDS_PTR(char))(smem_dyn + 2 * T::BYTES);
+  LDS_PTR(char) qs_t = (LDS_PTR(char))(smem_dyn + 3 * T::BYTES);
+  LDS_PTR(char) ak = (LDS_PTR(char))(smem_dyn + 4 * T::BYTES);
+  LDS_PTR(char) av = (LDS_PTR(char))(smem_dyn + 4 * T::BYTES + TA::BYTES);
+
+  const int p = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
+  const I8 pc = load_plan8(a.pieces, p);
+  const int tok0 = pc.v[0], len = pc.v[1];
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t qs = static_cast<int64_t>(a.hq) * D, ks = static_cast<int64_t>(a.hkv) * D;
+  const __bf16* Q = static_cast<const __bf16*>(a.q) + static_cast<int64_t>(tok0) * qs;
+  const __bf16* dO = static_cast<const __bf16*>(a.dout) + static_cast<int64_t>(tok0) * qs;
+  const __bf16* K = static_cast<const __bf16*>(a.k) + static_cast<int64_t>(tok0) * ks + g * D;
+  const __bf16* V = static_cast<const __bf16*>(a.v) + static_cast<int64_t>(tok0) * ks + g * D;
+  const __bf16* st =
+      static_cast<const __bf16*>(a.state) + (static_cast<int64_t>(p) * a.hkv + g) * D * D;
+
+  stage_tile<D>(vs, V, ks, len, tid);
+  stage_tile<D>(kt, K, ks, len, tid);
+  const int n0 = 32 * (wave % NBN);
+  f32x16 acc_k[PER], acc_v[PER];
+  {
+    bf16x8 wk[KD], wv[KD];
+    state_frags<D, false>(wk, st, n0, lane);  // dK: W = R
+    state_frags<D, true>(wv, st, n0, lane);   // dV: W = R^T
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int m0 = 32 * ((wave + 4 * i) / NBN);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc_k[i][v] = acc_v[i][v] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        acc_k[i] = mfma32(row_operand<T>(vs, m0 + l32, 2 * kk + half), wk[kk], acc_k[i]);
+        acc_v[i] = mfma32(row_operand<T>(kt, m0 + l32, 2 * kk + half), wv[kk], acc_v[i]);
+      }
+    }
+  }
+  TileRegs<D> rd, rq;
+  auto fetch = [&](int h) __attribute__((always_inline)) {
+    rd.load(dO + h * D, qs, len, tid);
+    rq.load(Q + h * D, qs, len, tid);
+  };
+  fetch(g * a.gsize);
+  for (int j = 0; j < a.gsize; ++j) {
+    const int h = g * a.gsize + j;
+    rd.store(dos, tid);
+    rq.store(qs_t, tid);
+    if (j + 1 < a.gsize) fetch(h + 1);
+    __syncthreads();
+    {
+      // one 32x32 block of each masked product per wave (key row r, query
+      // column c, kept for c >= r)
+      const int bi = wave >> 1, bj = wave & 1;
+      f32x16 tk, tv;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tk[v] = tv[v] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        tk = mfma32(row_operand<T>(vs, 32 * bi + l32, 2 * kk + half),
+                    row_operand<T>(dos, 32 * bj + l32, 2 * kk + half), tk);
+        tv = mfma32(row_operand<T>(kt, 32 * bi + l32, 2 * kk + half),
+                    row_operand<T>(qs_t, 32 * bj + l32, 2 * kk + half), tv);
+      }
+      const int c = 32 * bj + l32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 32 * bi + acc_row(v, lane);
+        const bool keep = c >= r;
+        *reinterpret_cast<LDS_PTR(__bf16)>(ak + TA::elem_off(r, c)) = to_bf16(keep ? tk[v] : 0.f);
+        *reinterpret_cast<LDS_PTR(__bf16)>(av + TA::elem_off(r, c)) = to_bf16(keep ? tv[v] : 0.f);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int m0 = 32 * ((wave + 4 * i) / NBN);
+#pragma unroll
+      for (int kk = 0; kk < CH / 16; ++kk) {
+        acc_k[i] = mfma32(row_operand<TA>(ak, m0 + l32, 2 * kk + half),
+                          tr_operand<T>(qs_t, 16 * kk, n0, lane), acc_k[i]);
+        acc_v[i] = mfma32(row_operand<TA>(av, m0 + l32, 2 * kk + half),
+                          tr_operand<T>(dos, 16 * kk, n0, lane), acc_v[i]);
+      }
+    }
+    __syncthreads();  // before the next head overwrites the staged operands
+  }
+  __bf16* dk = static_cast<__bf16*>(a.out) + static_cast<int64_t>(tok0) * ks + g * D;
+  __bf16* dv = static_cast<__bf16*>(a.out2) + static_cast<int64_t>(tok0) * ks + g * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int m0 = 32 * ((wave + 4 * i) / NBN);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = m0 + acc_row(v, lane);
+      if (r < len) {
+        dk[r * ks + n0 + l32] = to_bf16(a.scale * acc_k[i][v]);
+        dv[r * ks + n0 + l32] = to_bf16(a.scale * acc_v[i][v]);
+      }
+    }
   }
 }
 
+template __global__ void lin_dkdv_kernel<128>(LinArgs);
+template __global__ void lin_dkdv_kernel<64>(LinArgs);
 template __global__ void lin_outer_kernel<128>(LinArgs, int);
 template __global__ void lin_outer_kernel<64>(LinArgs, int);
 template __global__ void lin_scan_kernel<128>(LinArgs, int);
 template __global__ void lin_scan_kernel<64>(LinArgs, int);
 template __global__ void lin_chunk_kernel<128, 0>(LinArgs);
 template __global__ void lin_chunk_kernel<128, 1>(LinArgs);
-template __global__ void lin_chunk_kernel<128, 2>(LinArgs);
-template __global__ void lin_chunk_kernel<128, 3>(LinArgs);
 template __global__ void lin_chunk_kernel<64, 0>(LinArgs);
 template __global__ void lin_chunk_kernel<64, 1>(LinArgs);
-template __global__ void lin_chunk_kernel<64, 2>(LinArgs);
-template __global__ void lin_chunk_kernel<64, 3>(LinArgs);
 
 namespace {
 
@@ -452,22 +517,22 @@ hipError_t launch_lin_scan(const LinArgs& a, int backward, int head_dim, hipStre
   return hipErrorInvalidValue;
 }
 
+template <int D>
+hipError_t lin_dkdv_t(const LinArgs& a, hipStream_t s) {
+  const int bytes = 4 * Tile<D, CH>::BYTES + 2 * Tile<CH, CH>::BYTES;
+  return launch_dyn(lin_dkdv_kernel<D>, a.n_pieces * a.hkv, bytes, s, a);
+}
+
 hipError_t launch_lin_chunk(const LinArgs& a, int mode, int head_dim, hipStream_t stream) {
   if (a.n_pieces <= 0) return hipSuccess;
   if (head_dim == 128) {
-    switch (mode) {
-      case 0: return lin_chunk_t<128, 0>(a, stream);
-      case 1: return lin_chunk_t<128, 1>(a, stream);
-      case 2: return lin_chunk_t<128, 2>(a, stream);
-      case 3: return lin_chunk_t<128, 3>(a, stream);
-    }
+    if (mode == 0) return lin_chunk_t<128, 0>(a, stream);
+    if (mode == 1) return lin_chunk_t<128, 1>(a, stream);
+    if (mode == 4) return lin_dkdv_t<128>(a, stream);
   } else if (head_dim == 64) {
-    switch (mode) {
-      case 0: return lin_chunk_t<64, 0>(a, stream);
-      case 1: return lin_chunk_t<64, 1>(a, stream);
-      case 2: return lin_chunk_t<64, 2>(a, stream);
-      case 3: return lin_chunk_t<64, 3>(a, stream);
-    }
+    if (mode == 0) return lin_chunk_t<64, 0>(a, stream);
+    if (mode == 1) return lin_chunk_t<64, 1>(a, stream);
+    if (mode == 4) return lin_dkdv_t<64>(a, stream);
   }
   return hipErrorInvalidValue;
 }
