@@ -12,8 +12,11 @@ Prints one JSON line.  Default workload: the GRPO-style star tree (one
 head dim 128, bf16).  ``--config`` selects another of the five workload
 trees.  ``--workload linear`` times the chunkwise linear-attention pass over
 the same tree instead (plan + linear forward + linear backward per step),
-with its own metric line.  Only one GPU is used; ``--gpus`` above 1 is
-refused.
+with its own metric line.  ``--workload dfs`` runs the same softmax
+attention as a depth-first walk of the tree, one node per call (forward in
+preorder, accumulating backward in reverse), with the per-node plans built
+before the timed region, and reports it beside the one-call pass.  Only one
+GPU is used; ``--gpus`` above 1 is refused.
 """
 
 from __future__ import annotations
@@ -35,6 +38,8 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_FP32_TFLOPS = 157.3    # dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0
 METRIC = "tree-attn fwd+bwd unique tokens/s and TFLOP/s (% of bf16 MFMA peak), 1 GPU"
+DFS_METRIC = ("tree-attn fwd+bwd unique tokens/s, depth-first walk (one node per call, "
+              "accumulated K/V gradients), 1 GPU")
 LIN_METRIC = "tree linear-attn fwd+bwd unique tokens/s (chunkwise, state handoffs), 1 GPU"
 LIN_CHUNK = 64
 
@@ -53,8 +58,9 @@ def _args():
                     help="skip timing the oracle on the host")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
-    ap.add_argument("--workload", choices=["softmax", "linear"], default="softmax",
-                    help="softmax tree attention (default) or chunkwise linear attention")
+    ap.add_argument("--workload", choices=["softmax", "linear", "dfs"], default="softmax",
+                    help="softmax tree attention (default), chunkwise linear attention, or "
+                         "softmax tree attention as a depth-first walk, one node per call")
     return ap.parse_args()
 
 
@@ -282,6 +288,150 @@ def main_linear(args) -> int:
     return 0
 
 
+def main_dfs(args) -> int:
+    """Softmax tree attention as a depth-first walk: per step, zero the fp32
+    K/V gradient accumulators, one forward call per node in preorder, one
+    accumulating backward call per node in reverse preorder, and the casts
+    of the accumulators.  The one-call pass (plan built beforehand) is timed
+    in the same run for comparison."""
+    import torch
+    import prefix_shared_tree_attn_amd as ta
+    from tree_inputs import config_spec, config_tree, dfs_preorder, make_inputs, tree_stats
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = args.config
+    t = config_tree(cfg)
+    spec = config_spec(cfg)
+    st = tree_stats(t)
+    hq, hkv, d, dtype = spec["heads_q"], spec["heads_kv"], spec["head_dim"], spec["dtype"]
+    scale = spec["scale"]
+    n = t.num_tokens
+    log(f"dfs workload {spec['name']}: N={n} nodes={t.num_nodes} hq={hq} hkv={hkv} d={d}")
+    x = make_inputs(n, hq, hkv, d, dtype=dtype, do_std=spec["do_std"])
+
+    def up(name):
+        if dtype == "bf16":
+            a = torch.from_numpy(x.bits[name].view(np.int16)).view(torch.bfloat16)
+        else:
+            a = torch.from_numpy(getattr(x, name))
+        return a.to(dev)
+
+    q, k, v, do = up("q"), up("k"), up("v"), up("do")
+    del x
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, n), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    acc = torch.empty((2, n, hkv, d), dtype=torch.float32, device=dev)
+    order = dfs_preorder(t.parent)
+    t0 = time.perf_counter()
+    plans = [ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype, query_nodes=[i])
+             for i in order]
+    torch.cuda.synchronize()
+    plan_ms = 1e3 * (time.perf_counter() - t0)
+    ws = torch.empty(max(p.workspace_size()[1] for p in plans), dtype=torch.uint8, device=dev)
+    whole = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype)
+    ws_whole = ta.workspace(whole, "bwd")
+
+    def walk():
+        acc.zero_()
+        for p in plans:
+            ta.fwd(p, q, k, v, scale, o=o, lse=lse)
+        for p in reversed(plans):
+            ta.bwd_accum(p, q, k, v, o, lse, do, scale, acc[0], acc[1], dq=dq, ws=ws)
+        ta.accum_cast(acc[0], dtype, out=dk)
+        ta.accum_cast(acc[1], dtype, out=dv)
+
+    def one_call():
+        ta.fwd(whole, q, k, v, scale, o=o, lse=lse)
+        ta.bwd(whole, q, k, v, o, lse, do, scale, dq=dq, dk=dk, dv=dv, ws=ws_whole)
+
+    def timed(fn, steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t0) / steps
+
+    for _ in range(args.warmup):
+        walk()
+        one_call()
+    ms_one = timed(one_call, args.steps)
+    log(f"one call: {ms_one:.3f} ms")
+    ta.timing_read(reset=True)
+    ta.timing_enable(True)
+    ms_step = timed(walk, args.steps)
+    ta.timing_enable(False)
+    kt = ta.timing_read(reset=True)
+    log(f"walk: {ms_step:.3f} ms")
+    for p in plans + [whole]:
+        p.close()
+
+    pairs = st["pairs"]
+    peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
+    step_flop = 14.0 * d * hq * pairs
+    # over a whole walk the kernels do the whole tree's work
+    kern_flop = {"fwd": 4.0 * d * hq * pairs, "bwd_dkdv": 8.0 * d * hq * pairs,
+                 "bwd_dq": 6.0 * d * hq * pairs}
+    pipe = dtype == "bf16"
+    kern_name = {"fwd": f"tree_attn_fwd_kernel<{'bf16' if pipe else 'float'}, {d}>",
+                 "bwd_dkdv": (f"tree_attn_dkdv_pipe_kernel<{d}>" if pipe
+                              else f"tree_attn_dkdv_kernel<float, {d}>"),
+                 "bwd_dq": f"tree_attn_dq_kernel<{'bf16' if pipe else 'float'}, {d}>"}
+
+    def roof(kind):
+        r = kt[kind]
+        walk_ms = r["total_ms"] / args.steps  # every launch of one walk
+        ach = kern_flop[kind] / (walk_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": kern_name[kind], "achieved": ach, "peak": peak,
+                "unit": "TFLOP/s", "frac": ach / peak,
+                "flop_per_launch": kern_flop[kind] / len(plans),
+                "avg_ms": r["total_ms"] / max(r["launches"], 1), "launches_per_step": len(plans),
+                "ms_per_step": walk_ms}
+
+    dominant = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda kk: kt[kk]["total_ms"])
+    main_roof = roof(dominant)
+    main_roof["traffic"] = None
+    result = {
+        "metric": DFS_METRIC,
+        "value": n / (ms_step * 1e-3),
+        "unit": "unique tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{spec['name']} tree, depth-first walk, one node per call",
+            "unique_tokens": n, "nodes": t.num_nodes, "pairs": pairs, "heads_q": hq,
+            "heads_kv": hkv, "head_dim": d, "softmax_scale": scale, "global_batch": 1,
+            "seq_len": st["max_path"], "parallelism": "none (1 GPU)",
+        },
+        "tflops": step_flop / (ms_step * 1e-3) / 1e12,
+        "frac_of_peak": step_flop / (ms_step * 1e-3) / 1e12 / peak,
+        "one_call_ms": ms_one,
+        "walk_over_one_call": ms_step / ms_one,
+        "plans_ms_host": plan_ms,
+        "kernels_ms_per_step": {kk: kt[kk]["total_ms"] / args.steps for kk in kt
+                                if kt[kk]["launches"]},
+        "roofline": main_roof,
+        "roofline_kernels": {kk: roof(kk) for kk in ("fwd", "bwd_dkdv", "bwd_dq")},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (cpu baseline)")
+        result["cpu_baseline"] = cpu_baseline(t, spec)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def _passes_around_attention(ta, torch, t, o, q, k, pos_id, do, hq, hkv, d, reps=5):
     """The steps either side of the attention call, on the same workload:
     prefix compression of the tree's root-to-leaf trajectories (host), the
@@ -356,6 +506,8 @@ def main() -> int:
         return 2
     if args.workload == "linear":
         return main_linear(args)
+    if args.workload == "dfs":
+        return main_dfs(args)
     import torch
     import prefix_shared_tree_attn_amd as ta
     from tree_inputs import config_spec, config_tree, make_inputs, tree_stats

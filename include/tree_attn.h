@@ -157,6 +157,85 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
                                  const void* dout, float softmax_scale, void* dq, void* dk,
                                  void* dv, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Depth-first schedule.  AReaL-DTA (abstract) walks the prefix tree depth
+ * first so that only one root-to-leaf path is resident at a time, while
+ * every shared prefix is still computed once.  The entry points below run
+ * the same kernels on a plan restricted to some query nodes: visiting the
+ * nodes in depth-first preorder, one (or a few) per call, the forward pass
+ * needs only the K/V rows of the current path and writes only the current
+ * node's rows; the backward pass, in reverse order, adds each node's
+ * contribution to the K/V gradients of its path into fp32 accumulators.
+ * Summed over a partition of the nodes, the accumulated gradients equal
+ * tree_attn_bwd's (up to fp32 summation order).
+ */
+
+/*
+ * tree_attn_plan_subset -- a plan whose queries are the tokens of
+ * query_nodes[0 .. num_query_nodes) (node indices of the table; repeats are
+ * ignored; an empty list gives a plan that does nothing).  Keys are unchanged:
+ * a query still attends to every ancestor row and the earlier rows of its
+ * node.  Validation, errors and device upload are those of tree_attn_plan;
+ * INVALID_ARG also for a node index outside [0, num_nodes) or a null list
+ * with num_query_nodes > 0.
+ * On such a plan:
+ *   tree_attn_fwd  writes O and LSE of the query rows only (other rows are
+ *                  untouched) and reads Q of the query rows and K/V of the
+ *                  rows they attend to -- nothing else of q, k, v;
+ *   tree_attn_bwd  is rejected (INVALID_ARG): use tree_attn_bwd_accum;
+ *   linear attention entry points are rejected (UNSUPPORTED).
+ */
+tree_attn_status_t tree_attn_plan_subset(const int32_t* parent, const int32_t* seg_start,
+                                         const int32_t* seg_len, int32_t num_nodes,
+                                         int32_t num_tokens, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         tree_attn_dtype_t dtype, const int32_t* query_nodes,
+                                         int32_t num_query_nodes, hipStream_t stream,
+                                         tree_attn_plan_t* out);
+
+/* tree_attn_plan_host_subset -- tree_attn_plan_subset without a GPU (see
+ * tree_attn_plan_host). */
+tree_attn_status_t tree_attn_plan_host_subset(const int32_t* parent, const int32_t* seg_start,
+                                              const int32_t* seg_len, int32_t num_nodes,
+                                              int32_t num_tokens, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              tree_attn_dtype_t dtype,
+                                              const int32_t* query_nodes,
+                                              int32_t num_query_nodes, int32_t num_cus,
+                                              tree_attn_plan_t* out);
+
+/*
+ * tree_attn_bwd_accum -- backward pass of a query-subset plan: the
+ * gradients of sum over query rows t of <dout_t, O_t>.
+ *   dq      [N,Hq,D] in the plan's dtype: rows of the query nodes are
+ *           overwritten with their gradient, other rows untouched;
+ *   dk_acc, dv_acc  [N,Hkv,D] fp32 device accumulators (16-byte aligned):
+ *           the gradient with respect to every key/value row that a query
+ *           row attends to is ADDED (fp32); rows no query row sees are
+ *           untouched.  The caller zeroes them before the first call of a
+ *           schedule and converts them with tree_attn_accum_cast after the
+ *           last.
+ * Reads o, lse and dout of the query rows only.  Calls on the same
+ * accumulators must be ordered (one stream, or synchronised): each adds with
+ * plain loads and stores, no atomics, so the result is bitwise reproducible
+ * for a fixed call order.  ws: tree_attn_workspace_size's bwd_bytes of this
+ * plan.  Errors as tree_attn_bwd; INVALID_ARG for a whole-tree plan.
+ */
+tree_attn_status_t tree_attn_bwd_accum(tree_attn_plan_t plan, const void* q, const void* k,
+                                       const void* v, const void* o, const float* lse,
+                                       const void* dout, float softmax_scale, void* dq,
+                                       float* dk_acc, float* dv_acc, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/*
+ * tree_attn_accum_cast -- out[i] = acc[i] rounded to `dtype` (bf16: nearest
+ * even; fp32: copy) for i < count.  acc: device fp32, 16-byte aligned; out:
+ * device, `dtype`.  Enqueued on `stream`.  Errors: INVALID_ARG (negative
+ * count, null or misaligned pointer), UNSUPPORTED (unknown dtype).
+ */
+tree_attn_status_t tree_attn_accum_cast(const float* acc, void* out, int64_t count,
+                                        tree_attn_dtype_t dtype, hipStream_t stream);
+
 /*
  * tree_attn_positions -- per-token node index and position id.
  * Every root-to-leaf path through a unique token t places it after the
@@ -279,6 +358,8 @@ typedef struct {
   int64_t lin_pieces;       /* linear attention: pieces                     */
   int64_t lin_succ;         /* linear attention: successor entries          */
   int64_t lin_chunk;        /* linear attention: chunk (trajectory depth)   */
+  int64_t subset;           /* 1 for a query-subset plan, else 0            */
+  int64_t query_rows;       /* tokens that are queries (N for whole trees)  */
 } tree_attn_plan_stats_t;
 
 tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_stats_t* out);

@@ -16,6 +16,7 @@ from .path_expansion import (  # noqa: F401
     token_positions,
     causal_attention,
     tree_attention,
+    tree_attention_subset,
     query_rows,
     key_rows,
 )

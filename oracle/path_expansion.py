@@ -229,6 +229,36 @@ def tree_attention(q, k, v, do, parent, seg_start, seg_len, scale: float,
             "path_spread": spread}
 
 
+def tree_attention_subset(q, k, v, do, parent, seg_start, seg_len, scale: float,
+                          query_nodes: Iterable[int], **kw) -> Dict[str, np.ndarray]:
+    """One call of the depth-first schedule: tree attention whose queries are
+    the tokens of ``query_nodes`` only, fp64.
+
+    AReaL-DTA (abstract) walks the tree depth first, keeping one root-to-leaf
+    path resident, and still computes every shared prefix once.  One step of
+    that walk computes the outputs of the rows it visits and their share of
+    the gradients; the loss of such a step is sum over its query rows t of
+    <dO_t, O_t>.  That loss is the unique-token loss of ``tree_attention``
+    with dO set to zero on every other row, so this is ``tree_attention`` on
+    that dO.  Returned: ``o``, ``lse`` and ``dq`` on the query rows (NaN on
+    the other rows, which one step does not compute), ``dk``, ``dv`` on every
+    row (zero where no query row sees the key), and ``rows``, the bool [N]
+    mask of query rows.
+    """
+    n = q.shape[0]
+    rows = np.zeros(n, bool)
+    for node in query_nodes:
+        s = int(seg_start[node])
+        rows[s:s + int(seg_len[node])] = True
+    do_step = np.where(rows[:, None, None], np.asarray(do, np.float64), 0.0)
+    ref = tree_attention(q, k, v, do_step, parent, seg_start, seg_len, scale, **kw)
+    ref["o"][~rows] = np.nan
+    ref["lse"][:, ~rows] = np.nan
+    ref["dq"][~rows] = np.nan
+    ref["rows"] = rows
+    return ref
+
+
 # --------------------------------------------------------------------------
 # sampled outputs for workloads too large for the full expansion
 

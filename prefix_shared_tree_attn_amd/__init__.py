@@ -17,7 +17,8 @@ import numpy as np
 from . import _ffi
 from ._ffi import TreeAttnError, PlanStats  # noqa: F401
 
-__all__ = ["Plan", "plan", "plan_host", "fwd", "bwd", "positions", "workspace",
+__all__ = ["Plan", "plan", "plan_host", "fwd", "bwd", "bwd_accum", "accum_cast", "positions",
+           "workspace",
            "TreeAttnError", "timing_enable", "timing_read", "PrefixTree", "build_tree",
            "gather_rows", "scatter_sum_rows", "rope", "lin_fwd", "lin_bwd", "lin_workspace"]
 
@@ -113,25 +114,41 @@ def _plan_args(parent, seg_start, seg_len, num_tokens, hq, hkv, head_dim, dtype)
 
 
 def plan(parent, seg_start, seg_len, num_tokens: int, hq: int, hkv: int, head_dim: int,
-         dtype: str = "bf16", stream=None) -> Plan:
-    """Validates the node table and builds a device plan (tree_attn_plan)."""
+         dtype: str = "bf16", stream=None, query_nodes=None) -> Plan:
+    """Validates the node table and builds a device plan (tree_attn_plan), or
+    with ``query_nodes`` a query-subset plan (tree_attn_plan_subset)."""
     import torch
     par, st, ln, m = _plan_args(parent, seg_start, seg_len, num_tokens, hq, hkv, head_dim, dtype)
     h = ctypes.c_void_p(0)
-    _ffi.check(_ffi.lib().tree_attn_plan(
-        _ptr(par), _ptr(st), _ptr(ln), m, int(num_tokens), int(hq), int(hkv), int(head_dim),
-        _ffi.DTYPES[dtype], ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(h)), "plan")
+    L = _ffi.lib()
+    common = (_ptr(par), _ptr(st), _ptr(ln), m, int(num_tokens), int(hq), int(hkv),
+              int(head_dim), _ffi.DTYPES[dtype])
+    sp = ctypes.c_void_p(_stream_handle(stream))
+    if query_nodes is None:
+        _ffi.check(L.tree_attn_plan(*common, sp, ctypes.byref(h)), "plan")
+    else:
+        qn = _i32(query_nodes).reshape(-1)
+        _ffi.check(L.tree_attn_plan_subset(*common, _ptr(qn), int(qn.shape[0]), sp,
+                                           ctypes.byref(h)), "plan_subset")
     return Plan(h.value, int(num_tokens), hq, hkv, head_dim, dtype, torch.cuda.current_device())
 
 
 def plan_host(parent, seg_start, seg_len, num_tokens: int, hq: int, hkv: int, head_dim: int,
-              dtype: str = "bf16", num_cus: int = 256) -> Plan:
-    """Host-only plan (tree_attn_plan_host): validation, inspection, sizing."""
+              dtype: str = "bf16", num_cus: int = 256, query_nodes=None) -> Plan:
+    """Host-only plan (tree_attn_plan_host / tree_attn_plan_host_subset):
+    validation, inspection, sizing."""
     par, st, ln, m = _plan_args(parent, seg_start, seg_len, num_tokens, hq, hkv, head_dim, dtype)
     h = ctypes.c_void_p(0)
-    _ffi.check(_ffi.lib().tree_attn_plan_host(
-        _ptr(par), _ptr(st), _ptr(ln), m, int(num_tokens), int(hq), int(hkv), int(head_dim),
-        _ffi.DTYPES[dtype], int(num_cus), ctypes.byref(h)), "plan_host")
+    L = _ffi.lib()
+    common = (_ptr(par), _ptr(st), _ptr(ln), m, int(num_tokens), int(hq), int(hkv),
+              int(head_dim), _ffi.DTYPES[dtype])
+    if query_nodes is None:
+        _ffi.check(L.tree_attn_plan_host(*common, int(num_cus), ctypes.byref(h)), "plan_host")
+    else:
+        qn = _i32(query_nodes).reshape(-1)
+        _ffi.check(L.tree_attn_plan_host_subset(*common, _ptr(qn), int(qn.shape[0]),
+                                                int(num_cus), ctypes.byref(h)),
+                   "plan_host_subset")
     return Plan(h.value, int(num_tokens), hq, hkv, head_dim, dtype, None)
 
 
@@ -140,7 +157,8 @@ _TORCH_DTYPES = {"bf16": "bfloat16", "fp32": "float32"}
 
 def _check_tensor(x, name: str, shape, p: Plan):
     import torch
-    want = getattr(torch, _TORCH_DTYPES[p.dtype]) if name != "lse" else torch.float32
+    fp32 = name in ("lse", "dk_acc", "dv_acc")
+    want = torch.float32 if fp32 else getattr(torch, _TORCH_DTYPES[p.dtype])
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
     if x.device.type != "cuda" or x.device.index != p.device:
@@ -203,6 +221,47 @@ def bwd(p: Plan, q, k, v, o, lse, do, scale: float, dq=None, dk=None, dv=None, w
         ctypes.c_void_p(ws.data_ptr()), ws.numel(),
         ctypes.c_void_p(_stream_handle(stream))), "bwd")
     return dq, dk, dv
+
+
+def bwd_accum(p: Plan, q, k, v, o, lse, do, scale: float, dk_acc, dv_acc, dq=None, ws=None,
+              stream=None):
+    """tree_attn_bwd_accum on a query-subset plan: writes dQ of the query
+    rows and adds the K/V gradients into the fp32 ``dk_acc``/``dv_acc``
+    [N,Hkv,D].  Returns dq."""
+    import torch
+    n, hq, hkv, d = p.num_tokens, p.hq, p.hkv, p.head_dim
+    if dq is None:
+        dq = torch.empty((n, hq, d), dtype=q.dtype, device=q.device)
+    if ws is None:
+        ws = workspace(p, "bwd")
+    args = [_check_tensor(q, "q", (n, hq, d), p), _check_tensor(k, "k", (n, hkv, d), p),
+            _check_tensor(v, "v", (n, hkv, d), p), _check_tensor(o, "o", (n, hq, d), p),
+            _check_tensor(lse, "lse", (hq, n), p), _check_tensor(do, "do", (n, hq, d), p)]
+    outs = [_check_tensor(dq, "dq", (n, hq, d), p),
+            _check_tensor(dk_acc, "dk_acc", (n, hkv, d), p),
+            _check_tensor(dv_acc, "dv_acc", (n, hkv, d), p)]
+    _ffi.check(_ffi.lib().tree_attn_bwd_accum(
+        p.handle, *args, ctypes.c_float(scale), *outs, ctypes.c_void_p(ws.data_ptr()),
+        ws.numel(), ctypes.c_void_p(_stream_handle(stream))), "bwd_accum")
+    return dq
+
+
+def accum_cast(acc, dtype: str = "bf16", out=None, stream=None):
+    """tree_attn_accum_cast: fp32 accumulator -> tensor of ``dtype``."""
+    import torch
+    _dev_check(acc, "acc", torch.float32)
+    if not acc.is_contiguous():
+        raise ValueError("acc must be contiguous")
+    if out is None:
+        out = torch.empty(acc.shape, dtype=getattr(torch, _TORCH_DTYPES[dtype]),
+                          device=acc.device)
+    _dev_check(out, "out", getattr(torch, _TORCH_DTYPES[dtype]))
+    if out.numel() != acc.numel() or not out.is_contiguous():
+        raise ValueError("out must be contiguous with as many elements as acc")
+    _ffi.check(_ffi.lib().tree_attn_accum_cast(
+        ctypes.c_void_p(acc.data_ptr()), ctypes.c_void_p(out.data_ptr()), acc.numel(),
+        _ffi.DTYPES[dtype], ctypes.c_void_p(_stream_handle(stream))), "accum_cast")
+    return out
 
 
 def lin_workspace(p: Plan, which: str = "bwd"):

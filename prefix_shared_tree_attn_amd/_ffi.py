@@ -22,6 +22,8 @@ EXPORTS = (
     "tree_attn_positions", "tree_attn_build_tree", "tree_attn_gather_rows",
     "tree_attn_scatter_sum_rows", "tree_attn_rope", "tree_attn_lin_workspace_size",
     "tree_attn_lin_fwd", "tree_attn_lin_bwd", "tree_attn_lin_plan_export",
+    "tree_attn_plan_subset", "tree_attn_plan_host_subset", "tree_attn_bwd_accum",
+    "tree_attn_accum_cast",
 )
 
 
@@ -30,7 +32,7 @@ class PlanStats(ctypes.Structure):
         "num_tokens", "num_nodes", "num_q_heads", "num_kv_heads", "head_dim", "pairs",
         "fwd_tiles", "fwd_ranges", "fwd_blocks", "bwd_items", "bwd_entries",
         "bwd_split_tiles", "bwd_slots", "fwd_tile_rows", "fwd_tile_keys", "bwd_tile_keys",
-        "bwd_block_rows", "lin_pieces", "lin_succ", "lin_chunk")]
+        "bwd_block_rows", "lin_pieces", "lin_succ", "lin_chunk", "subset", "query_rows")]
 
 
 class Timing(ctypes.Structure):
@@ -93,6 +95,13 @@ def lib() -> ctypes.CDLL:
     L.tree_attn_lin_bwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
                                     ctypes.c_size_t, vp]
     L.tree_attn_lin_plan_export.argtypes = [vp, i32p, i32p]
+    L.tree_attn_plan_subset.argtypes = [i32p, i32p, i32p] + [ctypes.c_int32] * 5 + [
+        ctypes.c_int, i32p, ctypes.c_int32, vp, ctypes.POINTER(vp)]
+    L.tree_attn_plan_host_subset.argtypes = [i32p, i32p, i32p] + [ctypes.c_int32] * 5 + [
+        ctypes.c_int, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(vp)]
+    L.tree_attn_bwd_accum.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                                      vp, ctypes.c_size_t, vp]
+    L.tree_attn_accum_cast.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int, vp]
     L.tree_attn_timing_enable.argtypes = [ctypes.c_int]
     L.tree_attn_timing_read.argtypes = [ctypes.POINTER(Timing), ctypes.c_int]
     for fn in ("tree_attn_timing_enable", "tree_attn_timing_read", "tree_attn_plan",
@@ -100,7 +109,8 @@ def lib() -> ctypes.CDLL:
                "tree_attn_plan_stats", "tree_attn_plan_export", "tree_attn_positions",
                "tree_attn_build_tree", "tree_attn_gather_rows", "tree_attn_scatter_sum_rows",
                "tree_attn_rope", "tree_attn_lin_workspace_size", "tree_attn_lin_fwd",
-               "tree_attn_lin_bwd", "tree_attn_lin_plan_export"):
+               "tree_attn_lin_bwd", "tree_attn_lin_plan_export", "tree_attn_plan_subset",
+               "tree_attn_plan_host_subset", "tree_attn_bwd_accum", "tree_attn_accum_cast"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L

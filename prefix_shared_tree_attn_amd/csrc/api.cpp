@@ -83,14 +83,16 @@ size_t lin_ends(const HostPlan& p) {
 tree_attn_status_t make_host_plan(const int32_t* parent, const int32_t* seg_start,
                                   const int32_t* seg_len, int32_t num_nodes, int32_t num_tokens,
                                   int32_t hq, int32_t hkv, int32_t head_dim,
-                                  tree_attn_dtype_t dtype, int num_cus, tree_attn_plan_s** out) {
+                                  tree_attn_dtype_t dtype, int num_cus, tree_attn_plan_s** out,
+                                  const int32_t* query_nodes = nullptr,
+                                  int32_t num_query_nodes = 0) {
   if (!out) return report(Status::kInvalidArg, "null output plan pointer");
   tree_attn_plan_s* p = new (std::nothrow) tree_attn_plan_s();
   if (!p) return report(Status::kInvalidArg, "out of host memory");
   std::string err;
   const Status s = tree_attn::build_plan(parent, seg_start, seg_len, num_nodes, num_tokens, hq,
                                          hkv, head_dim, static_cast<int>(dtype), num_cus,
-                                         &p->hp, &err);
+                                         &p->hp, &err, query_nodes, num_query_nodes);
   if (s != Status::kOk) {
     delete p;
     return report(s, err);
@@ -183,12 +185,32 @@ tree_attn_status_t tree_attn_plan_host(const int32_t* parent, const int32_t* seg
                         num_kv_heads, head_dim, dtype, num_cus, out);
 }
 
-tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_start,
-                                  const int32_t* seg_len, int32_t num_nodes,
-                                  int32_t num_tokens, int32_t num_q_heads,
-                                  int32_t num_kv_heads, int32_t head_dim,
-                                  tree_attn_dtype_t dtype, hipStream_t stream,
-                                  tree_attn_plan_t* out) {
+tree_attn_status_t tree_attn_plan_host_subset(const int32_t* parent, const int32_t* seg_start,
+                                              const int32_t* seg_len, int32_t num_nodes,
+                                              int32_t num_tokens, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              tree_attn_dtype_t dtype,
+                                              const int32_t* query_nodes,
+                                              int32_t num_query_nodes, int32_t num_cus,
+                                              tree_attn_plan_t* out) {
+  if (!query_nodes && num_query_nodes != 0)
+    return report(Status::kInvalidArg, "null query-node list");
+  static const int32_t kNone = 0;
+  return make_host_plan(parent, seg_start, seg_len, num_nodes, num_tokens, num_q_heads,
+                        num_kv_heads, head_dim, dtype, num_cus, out,
+                        query_nodes ? query_nodes : &kNone, num_query_nodes);
+}
+
+}  // extern "C"
+
+namespace {
+
+tree_attn_status_t device_plan(const int32_t* parent, const int32_t* seg_start,
+                               const int32_t* seg_len, int32_t num_nodes, int32_t num_tokens,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               tree_attn_dtype_t dtype, const int32_t* query_nodes,
+                               int32_t num_query_nodes, hipStream_t stream,
+                               tree_attn_plan_t* out) {
   if (!out) return report(Status::kInvalidArg, "null output plan pointer");
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
@@ -197,8 +219,9 @@ tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_star
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return report_hip(e, "hipDeviceGetAttribute");
   tree_attn_plan_s* p = nullptr;
-  tree_attn_status_t st = make_host_plan(parent, seg_start, seg_len, num_nodes, num_tokens,
-                                         num_q_heads, num_kv_heads, head_dim, dtype, cus, &p);
+  tree_attn_status_t st =
+      make_host_plan(parent, seg_start, seg_len, num_nodes, num_tokens, num_q_heads,
+                     num_kv_heads, head_dim, dtype, cus, &p, query_nodes, num_query_nodes);
   if (st != TREE_ATTN_OK) return st;
   const HostPlan& hp = p->hp;
   const size_t o_ft = 0;
@@ -255,6 +278,35 @@ tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_star
   return TREE_ATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+tree_attn_status_t tree_attn_plan(const int32_t* parent, const int32_t* seg_start,
+                                  const int32_t* seg_len, int32_t num_nodes,
+                                  int32_t num_tokens, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  tree_attn_dtype_t dtype, hipStream_t stream,
+                                  tree_attn_plan_t* out) {
+  return device_plan(parent, seg_start, seg_len, num_nodes, num_tokens, num_q_heads,
+                     num_kv_heads, head_dim, dtype, nullptr, 0, stream, out);
+}
+
+tree_attn_status_t tree_attn_plan_subset(const int32_t* parent, const int32_t* seg_start,
+                                         const int32_t* seg_len, int32_t num_nodes,
+                                         int32_t num_tokens, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         tree_attn_dtype_t dtype, const int32_t* query_nodes,
+                                         int32_t num_query_nodes, hipStream_t stream,
+                                         tree_attn_plan_t* out) {
+  if (!query_nodes && num_query_nodes != 0)
+    return report(Status::kInvalidArg, "null query-node list");
+  static const int32_t kNone = 0;
+  return device_plan(parent, seg_start, seg_len, num_nodes, num_tokens, num_q_heads,
+                     num_kv_heads, head_dim, dtype, query_nodes ? query_nodes : &kNone,
+                     num_query_nodes, stream, out);
+}
+
 void tree_attn_plan_destroy(tree_attn_plan_t plan) {
   if (!plan) return;
   if (plan->dev_buf) {
@@ -283,7 +335,7 @@ tree_attn_status_t tree_attn_fwd(tree_attn_plan_t plan, const void* q, const voi
   tree_attn_status_t st = check_device(plan);
   if (st != TREE_ATTN_OK) return st;
   const HostPlan& hp = plan->hp;
-  if (hp.num_tokens == 0) return TREE_ATTN_OK;
+  if (hp.num_tokens == 0 || hp.query_rows == 0) return TREE_ATTN_OK;
   if (!q || !k || !v || !o || !lse) return report(Status::kInvalidArg, "null tensor pointer");
   if (!std::isfinite(softmax_scale))
     return report(Status::kInvalidArg, "softmax_scale must be finite");
@@ -309,14 +361,26 @@ tree_attn_status_t tree_attn_fwd(tree_attn_plan_t plan, const void* q, const voi
   return TREE_ATTN_OK;
 }
 
-tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const void* k,
-                                 const void* v, const void* o, const float* lse,
-                                 const void* dout, float softmax_scale, void* dq, void* dk,
-                                 void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// dk / dv are the outputs (whole-tree plans) or, with acc != 0, fp32
+// accumulators (query-subset plans).
+tree_attn_status_t bwd_common(tree_attn_plan_t plan, const void* q, const void* k,
+                              const void* v, const void* o, const float* lse, const void* dout,
+                              float softmax_scale, void* dq, void* dk, void* dv, void* ws,
+                              size_t ws_bytes, hipStream_t stream, bool acc) {
   tree_attn_status_t st = check_device(plan);
   if (st != TREE_ATTN_OK) return st;
   const HostPlan& hp = plan->hp;
-  if (hp.num_tokens == 0) return TREE_ATTN_OK;
+  if (acc && !hp.subset)
+    return report(Status::kInvalidArg,
+                  "tree_attn_bwd_accum takes a query-subset plan (tree_attn_plan_subset)");
+  if (!acc && hp.subset)
+    return report(Status::kInvalidArg,
+                  "a query-subset plan's backward is tree_attn_bwd_accum");
+  if (hp.num_tokens == 0 || hp.query_rows == 0) return TREE_ATTN_OK;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return report(Status::kInvalidArg, "null tensor pointer");
   if (!std::isfinite(softmax_scale))
@@ -336,8 +400,15 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
   a.lse = lse;
   a.dout = dout;
   a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
+  if (acc) {
+    a.acc_dk = static_cast<float*>(dk);
+    a.acc_dv = static_cast<float*>(dv);
+    a.pre_tiles = plan->d_fwd_tiles;
+    a.n_pre_tiles = static_cast<int64_t>(hp.fwd_tiles.size());
+  } else {
+    a.dk = dk;
+    a.dv = dv;
+  }
   a.neg_d = reinterpret_cast<float*>(w + l.neg_d);
   a.neg_lse2 = reinterpret_cast<float*>(w + l.neg_lse2);
   a.dk_slots = reinterpret_cast<float*>(w + l.dk_slots);
@@ -369,6 +440,41 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
   return TREE_ATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const void* k,
+                                 const void* v, const void* o, const float* lse,
+                                 const void* dout, float softmax_scale, void* dq, void* dk,
+                                 void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return bwd_common(plan, q, k, v, o, lse, dout, softmax_scale, dq, dk, dv, ws, ws_bytes, stream,
+                    false);
+}
+
+tree_attn_status_t tree_attn_bwd_accum(tree_attn_plan_t plan, const void* q, const void* k,
+                                       const void* v, const void* o, const float* lse,
+                                       const void* dout, float softmax_scale, void* dq,
+                                       float* dk_acc, float* dv_acc, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  return bwd_common(plan, q, k, v, o, lse, dout, softmax_scale, dq, dk_acc, dv_acc, ws, ws_bytes,
+                    stream, true);
+}
+
+tree_attn_status_t tree_attn_accum_cast(const float* acc, void* out, int64_t count,
+                                        tree_attn_dtype_t dtype, hipStream_t stream) {
+  if (count < 0) return report(Status::kInvalidArg, "negative count");
+  if (count == 0) return TREE_ATTN_OK;
+  if (!acc || !out) return report(Status::kInvalidArg, "null pointer");
+  if (dtype != TREE_ATTN_BF16 && dtype != TREE_ATTN_FP32)
+    return report(Status::kUnsupported, "unknown dtype");
+  if (reinterpret_cast<uintptr_t>(acc) % 16 != 0)
+    return report(Status::kInvalidArg, "acc must be 16-byte aligned");
+  const hipError_t e = tree_attn::launch_cast(acc, out, count, static_cast<int>(dtype), stream);
+  if (e != hipSuccess) return report_hip(e, "accumulator cast launch");
+  return TREE_ATTN_OK;
+}
+
 tree_attn_status_t tree_attn_lin_workspace_size(tree_attn_plan_t plan, size_t* fwd_bytes,
                                                 size_t* bwd_bytes) {
   if (!plan) return report(Status::kInvalidArg, "null plan");
@@ -386,6 +492,7 @@ tree_attn_status_t lin_common(tree_attn_plan_t plan, float scale, void* ws, size
   tree_attn_status_t st = check_device(plan);
   if (st != TREE_ATTN_OK) return st;
   const HostPlan& hp = plan->hp;
+  if (hp.subset) return report(Status::kUnsupported, "linear attention takes a whole-tree plan");
   if (hp.dtype != 0) return report(Status::kUnsupported, "linear attention takes bf16 tensors");
   if (!std::isfinite(scale)) return report(Status::kInvalidArg, "scale must be finite");
   if (hp.num_tokens == 0) return TREE_ATTN_OK;
@@ -598,6 +705,8 @@ tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_st
   out->lin_pieces = static_cast<int64_t>(hp.lin_pieces.size());
   out->lin_succ = static_cast<int64_t>(hp.lin_succ.size());
   out->lin_chunk = tree_attn::kLinChunk;
+  out->subset = hp.subset ? 1 : 0;
+  out->query_rows = hp.query_rows;
   return TREE_ATTN_OK;
 }
 

@@ -77,12 +77,21 @@ __device__ __forceinline__ bool advance(Blk& b, int ee, const I4* entries) {
 }  // namespace
 
 // --------------------------------------------------------------------------
-// 1. preprocess: D_t = dO_t . O_t
+// 1. preprocess: D_t = dO_t . O_t, over every row or (query-subset plans)
+// over the rows of the query tiles: grid (tiles, blocks per tile)
 template <typename T, int D>
 __global__ __launch_bounds__(256) void tree_attn_bwd_pre_kernel(BwdArgs a) {
   constexpr int TPR = D / 8;  // threads per (token, head) row, 8 elements each
-  const int64_t rows = a.n_tokens * a.hq;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * (256 / TPR) + threadIdx.x / TPR;
+  int64_t rows = a.n_tokens * a.hq;  // end of this block's (token, head) row range
+  int64_t row;
+  if (a.pre_tiles) {
+    const I4 t = load_plan4(a.pre_tiles, blockIdx.x);
+    row = static_cast<int64_t>(t.x) * a.hq +
+          static_cast<int64_t>(blockIdx.y) * (256 / TPR) + threadIdx.x / TPR;
+    rows = static_cast<int64_t>(t.y) * a.hq;
+  } else {
+    row = static_cast<int64_t>(blockIdx.x) * (256 / TPR) + threadIdx.x / TPR;
+  }
   const int part = threadIdx.x % TPR;
   float acc = 0.f;
   if (row < rows) {
@@ -1158,8 +1167,31 @@ __global__ __launch_bounds__(256) void tree_attn_bwd_reduce_kernel(BwdArgs a) {
       sv += a.dv_slots[so];
     }
     const int64_t o = static_cast<int64_t>(k0 + kl) * ks + static_cast<int64_t>(g) * D + d;
-    static_cast<T*>(a.dk)[o] = static_cast<T>(sk);
-    static_cast<T*>(a.dv)[o] = static_cast<T>(sv);
+    if (a.acc_dk) {
+      // each (key row, kv head) belongs to one reduction entry: no races
+      a.acc_dk[o] += sk;
+      a.acc_dv[o] += sv;
+    } else {
+      static_cast<T*>(a.dk)[o] = static_cast<T>(sk);
+      static_cast<T*>(a.dv)[o] = static_cast<T>(sv);
+    }
+  }
+}
+
+// Conversion of fp32 accumulators to the tensors' dtype (after a sequence
+// of accumulating backward calls): 4 elements per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void tree_attn_cast_kernel(const float* src, T* dst,
+                                                            int64_t n) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    const float4 x = *reinterpret_cast<const float4*>(src + i);
+    dst[i] = static_cast<T>(x.x);
+    dst[i + 1] = static_cast<T>(x.y);
+    dst[i + 2] = static_cast<T>(x.z);
+    dst[i + 3] = static_cast<T>(x.w);
+  } else {
+    for (int64_t j = i; j < n; ++j) dst[j] = static_cast<T>(src[j]);
   }
 }
 
@@ -1168,8 +1200,17 @@ __global__ __launch_bounds__(256) void tree_attn_bwd_reduce_kernel(BwdArgs a) {
 
 template <typename T, int D>
 static hipError_t pre_t(const BwdArgs& a, hipStream_t s) {
-  const int64_t rows = a.n_tokens * a.hq;
   const int64_t per = 256 / (D / 8);
+  if (a.pre_tiles) {
+    if (a.n_pre_tiles == 0) return hipSuccess;
+    // a forward query tile holds at most kFwdRows tokens
+    const int64_t blocks = (static_cast<int64_t>(kFwdRows) * a.hq + per - 1) / per;
+    hipLaunchKernelGGL((tree_attn_bwd_pre_kernel<T, D>),
+                       dim3(static_cast<unsigned>(a.n_pre_tiles), static_cast<unsigned>(blocks)),
+                       dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  const int64_t rows = a.n_tokens * a.hq;
   const int64_t blocks = (rows + per - 1) / per;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((tree_attn_bwd_pre_kernel<T, D>), dim3(static_cast<unsigned>(blocks)),
@@ -1246,6 +1287,20 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int head_dim, hipStream_t 
 }
 hipError_t launch_bwd_post(const BwdArgs& a, int dtype, int head_dim, hipStream_t s) {
   TREE_ATTN_DISPATCH(post_t)
+}
+
+hipError_t launch_cast(const float* src, void* dst, int64_t n, int dtype, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 1023) / 1024;
+  if (dtype == 0)
+    hipLaunchKernelGGL(tree_attn_cast_kernel<__bf16>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(256), 0, s, src, static_cast<__bf16*>(dst), n);
+  else if (dtype == 1)
+    hipLaunchKernelGGL(tree_attn_cast_kernel<float>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(256), 0, s, src, static_cast<float*>(dst), n);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace tree_attn

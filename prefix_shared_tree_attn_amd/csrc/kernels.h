@@ -39,6 +39,10 @@ struct BwdArgs {
   const I8* items;   // dK/dV: (k0, k1, g, entry_begin, entry_end, slot, 0, 0)
   const I4* entries; // dK/dV: (h, q0, q1, causal)
   const I8* reduce;  // (k0, k1, g, slot_begin, n_slots, 0, 0, 0)
+  float* acc_dk;     // null, or [N, Hkv, D] fp32 accumulators the reduction adds into
+  float* acc_dv;
+  const I4* pre_tiles;  // null: the preprocess covers every row; else only these tiles' rows
+  int64_t n_pre_tiles;
   const I4* tiles;   // dQ: forward query tiles (q0, q1, range_begin, range_end)
   const I4* ranges;  // dQ: forward key ranges (k0, k1, causal, 0)
   int64_t n_tokens;
@@ -87,6 +91,8 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int head_dim, hipStream_t
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_post(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
+// dst[i] = src[i] rounded to the dtype, i < n (src 16-byte aligned)
+hipError_t launch_cast(const float* src, void* dst, int64_t n, int dtype, hipStream_t stream);
 hipError_t launch_positions(const PosArgs& a, hipStream_t stream);
 // backward = 0: delta = K^T V, state scan root first; backward = 1: delta =
 // sum_h Q_h^T dO_h, state scan leaves first.  mode: 0 O, 1 dQ, 4 dK and dV.

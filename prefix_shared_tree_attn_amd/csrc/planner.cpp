@@ -82,7 +82,8 @@ void build_lin_pieces(const int32_t* parent, const int32_t* seg_start, const int
 Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
                   int32_t num_nodes, int32_t num_tokens, int32_t num_q_heads,
                   int32_t num_kv_heads, int32_t head_dim, int dtype, int num_cus,
-                  HostPlan* out, std::string* err) {
+                  HostPlan* out, std::string* err, const int32_t* query_nodes,
+                  int32_t num_query_nodes) {
   if (!out) return fail(err, Status::kInvalidArg, "null output plan");
   if (num_nodes < 0 || num_tokens < 0)
     return fail(err, Status::kInvalidArg, "negative num_nodes or num_tokens");
@@ -96,6 +97,14 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
   if (dtype != 0 && dtype != 1) return fail(err, Status::kUnsupported, "unknown dtype");
   if (num_nodes == 0 && num_tokens != 0)
     return fail(err, Status::kLayout, "tokens given but no nodes");
+  if (num_query_nodes < 0 || (num_query_nodes > 0 && !query_nodes))
+    return fail(err, Status::kInvalidArg, "bad query-node list");
+  for (int32_t j = 0; j < num_query_nodes; ++j)
+    if (query_nodes[j] < 0 || query_nodes[j] >= num_nodes) {
+      std::ostringstream os;
+      os << "query node " << query_nodes[j] << " is not a node index";
+      return fail(err, Status::kInvalidArg, os.str());
+    }
 
   const int64_t m = num_nodes, n = num_tokens;
   HostPlan& p = *out;
@@ -107,7 +116,11 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
   p.head_dim = head_dim;
   p.dtype = dtype;
   p.num_cus = num_cus > 0 ? num_cus : 256;
+  p.subset = query_nodes != nullptr;
   if (m == 0) return Status::kOk;
+  // queries: every node, or the listed ones
+  std::vector<char> active(m, p.subset ? 0 : 1);
+  for (int32_t j = 0; j < num_query_nodes; ++j) active[query_nodes[j]] = 1;
 
   // ---- validation: parents, segment lengths, exact partition of [0, N)
   for (int64_t i = 0; i < m; ++i) {
@@ -171,9 +184,12 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
     p.segments.push_back({seg_start[i], seg_len[i], static_cast<int32_t>(depth[i]), i});
   build_lin_pieces(parent, seg_start, seg_len, order, children, depth, &p);
   p.pairs = 0;
+  p.query_rows = 0;
   for (int64_t i = 0; i < m; ++i) {
+    if (!active[i]) continue;
     const int64_t L = seg_len[i];
     p.pairs += L * depth[i] + L * (L + 1) / 2;
+    p.query_rows += L;
   }
 
   // ---- forward query tiles
@@ -184,6 +200,7 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
   std::vector<FTile> ftiles;
   std::vector<I4> franges;
   for (int64_t i = 0; i < m; ++i) {
+    if (!active[i]) continue;
     const int64_t s = seg_start[i], e = s + seg_len[i];
     for (int64_t r0 = s; r0 < e; r0 += kFwdRows) {
       const int64_t r1 = std::min<int64_t>(e, r0 + kFwdRows);
@@ -214,7 +231,8 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
   p.fwd_blocks = ((p.fwd_groups + kXcds - 1) / kXcds) * kXcds * gsize;
 
   // ---- backward key tiles with descendant query ranges
-  // descendant segments of each node, sorted by start and merged
+  // descendant segments of each node that hold queries, sorted by start and
+  // merged
   std::vector<std::vector<Range>> desc(m);
   {
     std::vector<int32_t> stack;
@@ -224,7 +242,8 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
       while (!stack.empty()) {
         const int32_t c = stack.back();
         stack.pop_back();
-        segs.push_back({seg_start[c], static_cast<int64_t>(seg_start[c]) + seg_len[c]});
+        if (active[c])
+          segs.push_back({seg_start[c], static_cast<int64_t>(seg_start[c]) + seg_len[c]});
         for (int32_t cc : children[c]) stack.push_back(cc);
       }
       std::sort(segs.begin(), segs.end(), [](const Range& a, const Range& b) { return a.b < b.b; });
@@ -252,21 +271,27 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
       kt.node = i;
       kt.k0 = k0;
       kt.k1 = std::min<int64_t>(e, k0 + kBwdKeys);
-      // own node from the tile's first row on (causal), merged with the
-      // descendants that follow it contiguously in memory
-      Range own{k0, e};
-      size_t j = 0;
+      // own node from the tile's first row on (causal) when the node holds
+      // queries, merged with the descendants that follow it contiguously in
+      // memory
       const auto& d = desc[i];
-      // descendant ranges are sorted; merge those that continue `own`
       std::vector<Range> rest;
-      for (j = 0; j < d.size(); ++j) {
-        if (d[j].b == own.e) own.e = d[j].e;
-        else rest.push_back(d[j]);
+      kt.rows = 0;
+      if (active[i]) {
+        Range own{k0, e};
+        // descendant ranges are sorted; merge those that continue `own`
+        for (size_t j = 0; j < d.size(); ++j) {
+          if (d[j].b == own.e) own.e = d[j].e;
+          else rest.push_back(d[j]);
+        }
+        kt.causal.push_back(own);
+        kt.rows = own.e - own.b;
+      } else {
+        rest = d;
       }
-      kt.causal.push_back(own);
       kt.full = rest;
-      kt.rows = own.e - own.b;
       for (auto& r : rest) kt.rows += r.e - r.b;
+      if (kt.rows == 0) continue;  // no query sees this tile
       total_cost += kt.rows * (kt.k1 - kt.k0) * gsize;
       ktiles.push_back(std::move(kt));
     }
@@ -291,7 +316,7 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
                          static_cast<int32_t>(r.e), 0});
       }
       const int64_t cost = kt.rows * gsize * nk;
-      if (cost <= cap) {
+      if (cost <= cap && !p.subset) {
         items.push_back({kt.k0, kt.k1, g, -1, std::move(all), cost, kt.node, 0});
         continue;
       }

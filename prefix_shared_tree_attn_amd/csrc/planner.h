@@ -48,6 +48,12 @@ struct HostPlan {
   int64_t num_tokens = 0, num_nodes = 0, hq = 0, hkv = 0, head_dim = 0;
   int dtype = 0;  // 0 bf16, 1 fp32
   int num_cus = 256;
+  // Query-subset plan: only the rows of the listed nodes are queries (their
+  // keys are still every ancestor row).  The forward pass writes those rows
+  // only, and every backward key tile writes fp32 slots that the reduction
+  // adds into caller-owned fp32 dK / dV accumulators.
+  bool subset = false;
+  int64_t query_rows = 0;  // rows of the query nodes
   int64_t pairs = 0;
 
   // forward: tiles (q0, q1, range_begin, range_end) longest first;
@@ -81,11 +87,14 @@ struct HostPlan {
   std::vector<I4> lin_nodes;
 };
 
-// Validates the table and fills `out`.  On error returns the status and a
-// message in *err; `out` is then unspecified.
+// Validates the table and fills `out`.  `query_nodes` (num_query_nodes
+// entries, repeats allowed) makes a query-subset plan; null plans the whole
+// tree.  On error returns the status and a message in *err; `out` is then
+// unspecified.
 Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t* seg_len,
                   int32_t num_nodes, int32_t num_tokens, int32_t num_q_heads,
                   int32_t num_kv_heads, int32_t head_dim, int dtype, int num_cus,
-                  HostPlan* out, std::string* err);
+                  HostPlan* out, std::string* err, const int32_t* query_nodes = nullptr,
+                  int32_t num_query_nodes = 0);
 
 }  // namespace tree_attn

@@ -244,3 +244,83 @@ def test_config_plans_build_quickly():
         st = p.stats()
         assert st["pairs"] == tree_stats(t)["pairs"]
         assert st["fwd_tiles"] > 0 and st["bwd_items"] > 0
+
+
+# ------------------------------------------------ query-subset plans (depth-first walk)
+
+def _row_nodes(t):
+    node_of = np.empty(t.num_tokens, np.int64)
+    for i in range(t.num_nodes):
+        node_of[t.seg_start[i]:t.seg_start[i] + t.seg_len[i]] = i
+    return node_of
+
+
+@pytest.mark.parametrize("idx", range(11))
+def test_subset_plan_covers_its_query_pairs_once(idx):
+    t = _trees()[idx]
+    hq, hkv = 4, 2
+    rng = np.random.default_rng(40 + idx)
+    node_of = _row_nodes(t)
+    vis = _visible(t)
+    subsets = [[int(rng.integers(t.num_nodes))],
+               list(rng.choice(t.num_nodes, size=max(1, t.num_nodes // 2), replace=False)),
+               list(range(t.num_nodes)), []]
+    for qn in subsets:
+        p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, 64, "bf16",
+                         num_cus=4, query_nodes=qn + qn[:1])  # a repeat is ignored
+        ex = p.export()
+        want = {(q, key) for (q, key) in vis if node_of[q] in set(qn)}
+        fp = _fwd_pairs(ex, hq, hkv)
+        assert set(fp) == want and set(fp.values()) <= {1}
+        bt = _bwd_triples(ex)
+        assert set(bt) == {(q, key, h) for (q, key) in want for h in range(hq)}
+        assert set(bt.values()) <= {1}
+        st = p.stats()
+        assert st["subset"] == 1
+        assert st["pairs"] == len(want)
+        assert st["query_rows"] == int(sum(t.seg_len[i] for i in set(qn)))
+        # every working item writes fp32 slots (the reduction adds them into
+        # the caller's accumulators); slots are distinct
+        work = ex["bwd_items"][ex["bwd_items"][:, 3] < ex["bwd_items"][:, 4]]
+        assert np.all(work[:, 5] >= 0)
+        assert len(set(work[:, 5].tolist())) == len(work) == st["bwd_slots"]
+        assert st["bwd_split_tiles"] == len({(int(a), int(g)) for a, g in work[:, [0, 2]]})
+
+
+def test_whole_tree_plan_is_not_a_subset():
+    t = binary_tree(40, 70, 3)
+    st = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, 4, 2, 64).stats()
+    assert st["subset"] == 0 and st["query_rows"] == t.num_tokens
+
+
+def test_subset_plan_rejects_bad_nodes():
+    t = binary_tree(10, 10, 2)
+    for bad in ([t.num_nodes], [-1]):
+        with pytest.raises(ta.TreeAttnError) as ei:
+            ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, 2, 1, 64,
+                         query_nodes=bad)
+        assert ei.value.status == "INVALID_ARG"
+    lib = _ffi.lib()
+    h = ctypes.c_void_p(0)
+    par = np.ascontiguousarray(t.parent, np.int32)
+    ss = np.ascontiguousarray(t.seg_start, np.int32)
+    sl = np.ascontiguousarray(t.seg_len, np.int32)
+    P = ctypes.POINTER(ctypes.c_int32)
+    st = lib.tree_attn_plan_host_subset(par.ctypes.data_as(P), ss.ctypes.data_as(P),
+                                        sl.ctypes.data_as(P), t.num_nodes, t.num_tokens, 2, 1,
+                                        64, 0, None, 3, 0, ctypes.byref(h))
+    assert _ffi.STATUS[st] == "INVALID_ARG"
+
+
+def test_subset_plan_calls_are_checked_on_the_host():
+    """A host-only subset plan still reaches the argument checks of the
+    accumulating backward and the cast, which need no GPU to fail."""
+    lib = _ffi.lib()
+    assert _ffi.STATUS[lib.tree_attn_accum_cast(None, None, -1, 0, None)] == "INVALID_ARG"
+    assert _ffi.STATUS[lib.tree_attn_accum_cast(None, None, 0, 0, None)] == "OK"
+    assert _ffi.STATUS[lib.tree_attn_accum_cast(None, None, 4, 0, None)] == "INVALID_ARG"
+    t = chain_tree([8])
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, 8, 1, 1, 64, query_nodes=[0])
+    st = lib.tree_attn_bwd_accum(p.handle, *([None] * 6), ctypes.c_float(1.0), None, None, None,
+                                 None, 0, None)
+    assert _ffi.STATUS[st] == "NO_DEVICE_PLAN"

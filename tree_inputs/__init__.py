@@ -24,6 +24,7 @@ from .trees import (  # noqa: F401
     agent_tree,
     trunk_tree,
     tree_stats,
+    dfs_preorder,
 )
 from .tensors import (  # noqa: F401
     bf16_round_bits,

@@ -175,6 +175,25 @@ def random_tree(rng: np.random.Generator, n_nodes: int, max_len: int = 40,
     return _from_lists(new_par, new_len, name, order)
 
 
+def dfs_preorder(parent) -> List[int]:
+    """Node indices in depth-first preorder (roots and children in index
+    order): the order in which a depth-first walk of the tree visits each
+    node's segment as the new part of the current root-to-leaf path
+    (AReaL-DTA, abstract)."""
+    parent = np.asarray(parent, np.int64)
+    children: List[List[int]] = [[] for _ in range(parent.shape[0])]
+    roots = []
+    for i, p in enumerate(parent):
+        (children[p] if p >= 0 else roots).append(i)
+    order: List[int] = []
+    stack = roots[::-1]
+    while stack:
+        i = stack.pop()
+        order.append(i)
+        stack.extend(children[i][::-1])
+    return order
+
+
 def tree_stats(t: NodeTable) -> dict:
     """Shape statistics of a tree: leaves, paths, pair counts.
 
