@@ -1040,7 +1040,9 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
 
     const int k1 = rg.y;
     const bool causal = rg.z != 0;
-    if (!(causal && kt > wave_q0 + 31)) {
+    // skipped when every key lies past this wave's rows or the wave has no
+    // rows (the last tile of a node)
+    if (!(causal && kt > wave_q0 + 31) && wave_q0 < q1) {
       // S^T and dP^T for keys kt + 32 kb + (0..31); register v of this lane
       // is key 16 (v / 8) + 8 half + v % 8 of the block (A rows swap23).
       f32x16 sacc[2], pacc[2];

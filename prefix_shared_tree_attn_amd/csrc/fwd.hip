@@ -171,8 +171,10 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
 
     const int k1 = rg.y;
     const bool causal = rg.z != 0;
-    // every key of the tile lies past every row of this wave: nothing to do
-    const bool skip = causal && kt > wave_q0 + 31;
+    // every key of the tile lies past every row of this wave, or the wave
+    // has no rows (the last tile of a node): nothing to do, and the SIMD's
+    // other wave runs alone meanwhile
+    const bool skip = (causal && kt > wave_q0 + 31) || wave_q0 >= q1;
     if (!skip) {
     // S^T for keys kt + 32 kb + (0..31); A row r holds key swap23(r) so
     // that register v of this lane is key 16 (v / 8) + 8 half + v % 8.
