@@ -378,9 +378,13 @@ tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_st
  *                                read the same query rows share an XCD, and
  *                                empty items (entry_begin == entry_end) fill
  *                                out the per-XCD queues.
- *   bwd_entries[bwd_entries, 4]: q_head, q0, q1, causal
- * A causal range applies the mask key <= query; a query sees a key in a
- * non-causal range unconditionally (range rows are ancestors/descendants).
+ *   bwd_entries[bwd_entries, 4]: q_head, q0, q1, mask
+ * A causal range (fwd causal = 1, bwd mask = 1) applies the mask
+ * key <= query; a query sees a key in a non-causal range (0)
+ * unconditionally (range rows are ancestors/descendants).  A backward key
+ * tile may span a parent's last rows and the first rows of the child stored
+ * right after it; the rows below the parent's other children then see only
+ * the parent's keys: mask = -(limit + 1) hides keys >= limit from them.
  */
 tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_tiles,
                                          int32_t* fwd_ranges, int32_t* bwd_items,

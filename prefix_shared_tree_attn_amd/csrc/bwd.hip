@@ -250,7 +250,9 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
     for (int sb = 0; sb < NSUB; ++sb) {
       const int qs0 = cur.qb + 32 * sb;  // first row of the sub-block
       // wave-uniform: no row of the sub-block sees any key of this wave
-      if (qs0 >= cur.qe || wk0 >= k1 || (cur.causal && wk0 > qs0 + 31)) continue;
+      // (a key limit, causal = -(limit + 1), hides keys >= limit from all rows)
+      const int klimit = cur.causal < 0 ? -cur.causal - 1 : k1;
+      if (qs0 >= cur.qe || wk0 >= klimit || (cur.causal > 0 && wk0 > qs0 + 31)) continue;
       // -LSE * log2(e) and -D of the 16 rows this lane holds: rows
       // 32 sb + 8 half + (0..7) and 32 sb + 16 + 8 half + (0..7)
       f32x4 lse4[4], dv4[4];
@@ -290,7 +292,8 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
       }
       // P = 2^(c s - LSE log2 e) recomputed from the saved LSE; masked where
       // a row is past the range, a key past the tile, or (causal) key > row.
-      const bool need_mask = qs0 + 32 > cur.qe || wk0 + 32 > k1 || (cur.causal && wk0 + 31 > qs0);
+      const bool need_mask =
+          qs0 + 32 > cur.qe || wk0 + 32 > klimit || (cur.causal > 0 && wk0 + 31 > qs0);
       float p[16], ds[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v)
@@ -298,8 +301,8 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
             __builtin_fmaf(sacc[v], a.scale_log2, lse4[v >> 2][v & 3]));
       if (need_mask) {
         const int qlim = cur.qe - cur.qb;                       // local rows < qlim
-        const int kq = cur.causal ? key - cur.qb : -(1 << 30);  // local rows >= kq
-        const bool kok = key < k1;
+        const int kq = cur.causal > 0 ? key - cur.qb : -(1 << 30);  // local rows >= kq
+        const bool kok = key < klimit;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int ql = 32 * sb + 16 * (v >> 3) + 8 * half + (v & 7);
@@ -746,7 +749,8 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   // bf16 packs are formed, after the last C slot has read the old packs.
   // The fences keep this order.  Under the causal mask (rare steps) x is set
   // to -inf where key > row between the halves.
-  auto iteration = [&](int bp, int bc, int bn, bool masked, int delta) __attribute__((always_inline)) {
+  auto iteration = [&](int bp, int bc, int bn, bool masked, int delta,
+                       int rmask) __attribute__((always_inline)) {
     LDS_PTR(char) bprev = lds + bp;
     LDS_PTR(char) bcur = lds + bc;
     LDS_PTR(char) bnext = lds + bn;
@@ -782,7 +786,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = 16 * (v >> 3) + 8 * half + (v & 7);
-        x[v] = l32 - r > delta ? -__builtin_inff() : x[v];
+        x[v] = l32 - (r & rmask) > delta ? -__builtin_inff() : x[v];
       }
     }
 #pragma unroll
@@ -857,11 +861,16 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
       ld_next();
     }
     even = !even;
-    const int delta = cur.r0 - wk0;
-    const bool masked = cur.causal && delta < 32;
+    // A causal entry (w = 1) masks key > row, i.e. l32 - r > r0 - wk0; a
+    // key limit (w = -(limit + 1)) masks key >= limit on every row, i.e.
+    // l32 > limit - 1 - wk0.
+    const bool lim = cur.causal < 0;
+    const int delta = lim ? -cur.causal - 2 - wk0 : cur.r0 - wk0;
+    const bool masked = lim ? delta < 31 : (cur.causal != 0 && delta < 32);
+    const int rmask = lim ? 0 : -1;
     cur = nx;
     step_next(nx, ee, a.entries);
-    iteration(bp, bc, bn, masked, delta);
+    iteration(bp, bc, bn, masked, delta, rmask);
     bp = bc;
     bc = bn;
     bn = nexto(bn);

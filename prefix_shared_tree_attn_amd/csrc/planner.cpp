@@ -192,7 +192,21 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
     p.query_rows += L;
   }
 
-  // ---- forward query tiles
+  // ---- forward query tiles, over runs: a node whose segment starts where
+  // its parent's ends (depth-first packing puts a first child there)
+  // continues its parent's run.  Every row of a run sees the run's first
+  // node's ancestors and the run's earlier rows, so query tiles may cross
+  // node boundaries inside a run, and the last tile of a short node is not
+  // left ragged.
+  std::vector<int64_t> run_end(m, -1);  // run start node -> end row of its run
+  std::vector<int32_t> run_of(m);       // node -> start node of its run
+  for (int32_t i : order) {
+    const int32_t pa = parent[i];
+    const bool cont = pa >= 0 && active[i] && active[pa] &&
+                      static_cast<int64_t>(seg_start[pa]) + seg_len[pa] == seg_start[i];
+    run_of[i] = cont ? run_of[pa] : i;
+    run_end[run_of[i]] = static_cast<int64_t>(seg_start[i]) + seg_len[i];
+  }
   struct FTile {
     I4 t;
     int64_t cost;
@@ -200,8 +214,8 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
   std::vector<FTile> ftiles;
   std::vector<I4> franges;
   for (int64_t i = 0; i < m; ++i) {
-    if (!active[i]) continue;
-    const int64_t s = seg_start[i], e = s + seg_len[i];
+    if (!active[i] || run_of[i] != i) continue;
+    const int64_t s = seg_start[i], e = run_end[i];
     for (int64_t r0 = s; r0 < e; r0 += kFwdRows) {
       const int64_t r1 = std::min<int64_t>(e, r0 + kFwdRows);
       const int32_t rb = static_cast<int32_t>(franges.size());
@@ -230,15 +244,36 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
   p.fwd_groups = static_cast<int64_t>(p.fwd_tiles.size()) * num_kv_heads;
   p.fwd_blocks = ((p.fwd_groups + kXcds - 1) / kXcds) * kXcds * gsize;
 
-  // ---- backward key tiles with descendant query ranges
-  // descendant segments of each node that hold queries, sorted by start and
-  // merged
-  std::vector<std::vector<Range>> desc(m);
+  // ---- backward key tiles over runs.  With a run n_1 .. n_k (each node the
+  // contiguous child of the previous), a key of n_c is seen by the run's
+  // later rows (causal) and by the side subtrees -- subtrees of the
+  // children that do not continue the run -- of n_c .. n_k.  A key tile
+  // that starts in n_a and ends in n_b is therefore seen in full by the side
+  // subtrees of n_b .. n_k, and by those of n_j (a <= j < b) only up to the
+  // end of n_j: a key-limit entry.  Key tiles then cross node boundaries
+  // inside a run, so a short node does not leave a ragged tile that its
+  // whole descendant set would walk.  Query-subset plans keep one node per
+  // run (only their query nodes' rows are queries).
+  std::vector<int32_t> next_in_run(m, -1);
+  std::vector<char> continues(m, 0);
+  if (!p.subset)
+    for (int64_t i = 0; i < m; ++i) {
+      const int32_t pa = parent[i];
+      if (pa >= 0 && static_cast<int64_t>(seg_start[pa]) + seg_len[pa] == seg_start[i]) {
+        next_in_run[pa] = static_cast<int32_t>(i);
+        continues[i] = 1;
+      }
+    }
+  // side-subtree segments of each node that hold queries, sorted by start
+  // and merged
+  std::vector<std::vector<Range>> side(m);
   {
     std::vector<int32_t> stack;
     for (int64_t i = 0; i < m; ++i) {
       std::vector<Range> segs;
-      stack.assign(children[i].begin(), children[i].end());
+      stack.clear();
+      for (int32_t c : children[i])
+        if (c != next_in_run[i]) stack.push_back(c);
       while (!stack.empty()) {
         const int32_t c = stack.back();
         stack.pop_back();
@@ -247,50 +282,68 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
         for (int32_t cc : children[c]) stack.push_back(cc);
       }
       std::sort(segs.begin(), segs.end(), [](const Range& a, const Range& b) { return a.b < b.b; });
-      for (auto& r : segs) push_range(desc[i], r.b, r.e);
+      for (auto& r : segs) push_range(side[i], r.b, r.e);
     }
   }
   struct BItem {
     int64_t k0, k1, g, slot;
     std::vector<I4> entries;
     int64_t cost;
-    int64_t node, chunk;  // tree node of the key tile, chunk of a split tile
+    int64_t node, chunk;  // node of the key tile's last key, chunk of a split tile
   };
   std::vector<BItem> items;
   int64_t total_cost = 0;
   struct KTile {
     int64_t k0, k1, node;
     std::vector<Range> causal, full;  // query ranges
+    std::vector<std::pair<Range, int64_t>> limited;  // query range, keys < limit
     int64_t rows;
   };
   std::vector<KTile> ktiles;
-  for (int64_t i = 0; i < m; ++i) {
-    const int64_t s = seg_start[i], e = s + seg_len[i];
+  auto seg_end = [&](int32_t i) { return static_cast<int64_t>(seg_start[i]) + seg_len[i]; };
+  for (int64_t r = 0; r < m; ++r) {
+    if (continues[r]) continue;
+    std::vector<int32_t> run;
+    for (int32_t c = static_cast<int32_t>(r); c >= 0; c = next_in_run[c]) run.push_back(c);
+    const int64_t s = seg_start[r], e = seg_end(run.back());
+    size_t a = 0;
     for (int64_t k0 = s; k0 < e; k0 += kBwdKeys) {
       KTile kt;
-      kt.node = i;
       kt.k0 = k0;
       kt.k1 = std::min<int64_t>(e, k0 + kBwdKeys);
-      // own node from the tile's first row on (causal) when the node holds
-      // queries, merged with the descendants that follow it contiguously in
-      // memory
-      const auto& d = desc[i];
-      std::vector<Range> rest;
+      while (seg_end(run[a]) <= k0) ++a;  // node of the first key
+      size_t b = a;
+      while (seg_end(run[b]) < kt.k1) ++b;  // node of the last key
+      // placement groups tiles by the node of their last key: the tiles of
+      // one node read the same rows, those of another node of the run fewer
+      kt.node = run[b];
+      // rows that see every key: side subtrees of n_b .. n_k
+      std::vector<Range> segs, full;
+      for (size_t j = b; j < run.size(); ++j)
+        segs.insert(segs.end(), side[run[j]].begin(), side[run[j]].end());
+      std::sort(segs.begin(), segs.end(), [](const Range& x, const Range& y) { return x.b < y.b; });
+      for (auto& rg : segs) push_range(full, rg.b, rg.e);
+      // the run from the tile's first row on (causal) when its rows are
+      // queries, merged with the full ranges that follow it contiguously
       kt.rows = 0;
-      if (active[i]) {
+      if (active[run[a]]) {
         Range own{k0, e};
-        // descendant ranges are sorted; merge those that continue `own`
-        for (size_t j = 0; j < d.size(); ++j) {
-          if (d[j].b == own.e) own.e = d[j].e;
-          else rest.push_back(d[j]);
+        for (const Range& f : full) {
+          if (f.b == own.e) own.e = f.e;
+          else kt.full.push_back(f);
         }
         kt.causal.push_back(own);
         kt.rows = own.e - own.b;
       } else {
-        rest = d;
+        kt.full = full;
       }
-      kt.full = rest;
-      for (auto& r : rest) kt.rows += r.e - r.b;
+      for (auto& rg : kt.full) kt.rows += rg.e - rg.b;
+      // side subtrees of n_a .. n_(b-1): only the keys before their node's end
+      for (size_t j = a; j < b; ++j)
+        for (const Range& rg : side[run[j]]) {
+          kt.limited.push_back({rg, seg_end(run[j])});
+          kt.rows += rg.e - rg.b;
+        }
       if (kt.rows == 0) continue;  // no query sees this tile
       total_cost += kt.rows * (kt.k1 - kt.k0) * gsize;
       ktiles.push_back(std::move(kt));
@@ -314,6 +367,10 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
         for (auto& r : kt.full)
           all.push_back({static_cast<int32_t>(h), static_cast<int32_t>(r.b),
                          static_cast<int32_t>(r.e), 0});
+        for (auto& rl : kt.limited)  // keys >= limit hidden: w = -(limit + 1)
+          all.push_back({static_cast<int32_t>(h), static_cast<int32_t>(rl.first.b),
+                         static_cast<int32_t>(rl.first.e),
+                         static_cast<int32_t>(-(rl.second + 1))});
       }
       const int64_t cost = kt.rows * gsize * nk;
       if (cost <= cap && !p.subset) {

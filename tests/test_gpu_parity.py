@@ -54,6 +54,9 @@ CASES = {
     "d64-bf16": (_random(6, 9, 300), 4, 2, 64, "bf16"),
     "d64-fp32": (_random(7, 8, 200), 2, 1, 64, "fp32"),
     "d128-fp32": (_random(8, 6, 200), 2, 2, 128, "fp32"),
+    # key tiles that cross node boundaries (key-limit entries) in the fp32 kernel
+    "binary-fp32": (binary_tree(100, 70, 3), 2, 1, 128, "fp32"),
+    "star-d64-fp32": (star_tree(200, 3, 150), 2, 1, 64, "fp32"),
     "heavy-prompt-split": (star_tree(1024, 16, 64), 4, 2, 128, "bf16"),
 }
 

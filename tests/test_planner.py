@@ -68,10 +68,12 @@ def _bwd_triples(ex):
     trip = {}
     for it in ex["bwd_items"]:
         k0, k1, g, eb, ee = it[:5]
-        for h, q0, q1, causal in ex["bwd_entries"][eb:ee]:
+        for h, q0, q1, mask in ex["bwd_entries"][eb:ee]:
+            # mask 1: causal (key <= row); 0: every key; -(limit + 1): keys < limit
+            klim = -int(mask) - 1 if mask < 0 else k1
             for q in range(q0, q1):
-                for key in range(k0, k1):
-                    if causal and key > q:
+                for key in range(k0, min(k1, klim)):
+                    if mask == 1 and key > q:
                         continue
                     trip[(q, key, h)] = trip.get((q, key, h), 0) + 1
     return trip
@@ -324,3 +326,26 @@ def test_subset_plan_calls_are_checked_on_the_host():
     st = lib.tree_attn_bwd_accum(p.handle, *([None] * 6), ctypes.c_float(1.0), None, None, None,
                                  None, 0, None)
     assert _ffi.STATUS[st] == "NO_DEVICE_PLAN"
+
+
+def test_key_and_query_tiles_cross_node_boundaries_inside_runs():
+    """A first child stored right after its parent continues the parent's
+    run: query tiles and key tiles tile the run, not each node, and the
+    parent's other children get key-limit entries for the tile that crosses
+    the boundary."""
+    t = star_tree(300, 5, 257)  # prompt 300, first response stored at 300
+    hq, hkv = 2, 1
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, 128, num_cus=4)
+    ex = p.export()
+    run = 300 + 257
+    qt = [tuple(x) for x in ex["fwd_tiles"][:, :2].tolist()]
+    assert sum(1 for q0, q1 in qt if q1 <= run) == -(-run // 128)
+    assert (256, 384) in qt  # one query tile spans the prompt's end
+    work = ex["bwd_items"][ex["bwd_items"][:, 3] < ex["bwd_items"][:, 4]]
+    kt = {(int(a), int(b)) for a, b in work[:, :2]}
+    assert sum(1 for k0, k1 in kt if k1 <= run) == -(-run // 128)
+    assert (256, 384) in kt
+    lim = ex["bwd_entries"][ex["bwd_entries"][:, 3] < 0]
+    assert len(lim) > 0 and set((-lim[:, 3] - 1).tolist()) == {300}
+    # those rows are the other four responses (stored after the first)
+    assert int(lim[:, 1].min()) >= run and int(lim[:, 2].max()) <= t.num_tokens
