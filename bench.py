@@ -378,8 +378,9 @@ def main_dfs(args) -> int:
     kern_flop = {"fwd": 4.0 * d * hq * pairs, "bwd_dkdv": 8.0 * d * hq * pairs,
                  "bwd_dq": 6.0 * d * hq * pairs}
     pipe = dtype == "bf16"
+    # one-node query-subset plans keep one node per run: no key-limit entries
     kern_name = {"fwd": f"tree_attn_fwd_kernel<{'bf16' if pipe else 'float'}, {d}>",
-                 "bwd_dkdv": (f"tree_attn_dkdv_pipe_kernel<{d}>" if pipe
+                 "bwd_dkdv": (f"tree_attn_dkdv_pipe_kernel<{d}, false>" if pipe
                               else f"tree_attn_dkdv_kernel<float, {d}>"),
                  "bwd_dq": f"tree_attn_dq_kernel<{'bf16' if pipe else 'float'}, {d}>"}
 
@@ -545,6 +546,8 @@ def main() -> int:
     probe = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype)
     ws = ta.workspace(probe, "bwd")
     pstats = probe.stats()
+    # the dK/dV kernel variant with key-limit masks runs when the plan has them
+    has_limit = bool((probe.export()["bwd_entries"][:, 3] < 0).any())
     probe.close()
     del x
     log("device buffers ready")
@@ -616,8 +619,8 @@ def main() -> int:
                  "bwd_dq": 6.0 * d * hq * pairs}
     pipe = dtype == "bf16"
     kern_name = {"fwd": f"tree_attn_fwd_kernel<{'bf16' if pipe else 'float'}, {d}>",
-                 "bwd_dkdv": (f"tree_attn_dkdv_pipe_kernel<{d}>" if pipe
-                              else f"tree_attn_dkdv_kernel<float, {d}>"),
+                 "bwd_dkdv": (f"tree_attn_dkdv_pipe_kernel<{d}, {str(has_limit).lower()}>"
+                              if pipe else f"tree_attn_dkdv_kernel<float, {d}>"),
                  "bwd_dq": f"tree_attn_dq_kernel<{'bf16' if pipe else 'float'}, {d}>"}
 
     def roof(kind):

@@ -421,6 +421,7 @@ tree_attn_status_t bwd_common(tree_attn_plan_t plan, const void* q, const void* 
   a.n_tokens = hp.num_tokens;
   a.n_items = static_cast<int64_t>(hp.bwd_items.size());
   a.n_reduce = static_cast<int64_t>(hp.bwd_reduce.size());
+  a.has_limit = hp.bwd_has_limit ? 1 : 0;
   a.n_groups = hp.fwd_groups;
   a.dq_blocks = hp.fwd_blocks;
   a.hq = static_cast<int>(hp.hq);

@@ -587,7 +587,10 @@ __device__ __forceinline__ void keep(const bf16x8& x) { asm volatile("" ::"v"(x)
 
 }  // namespace
 
-template <int D>
+// LIM: the plan has key-limit entries (key tiles that cross from a parent
+// into the child stored after it); the variant without them keeps the
+// per-step mask test to the causal case.
+template <int D, bool LIM>
 __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) {
   using C = DkdvPipeCfg<D>;
   constexpr int KC = C::KC, DB = C::DB, NB = C::NB, BUF = C::BUF;
@@ -864,10 +867,14 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
     // A causal entry (w = 1) masks key > row, i.e. l32 - r > r0 - wk0; a
     // key limit (w = -(limit + 1)) masks key >= limit on every row, i.e.
     // l32 > limit - 1 - wk0.
-    const bool lim = cur.causal < 0;
-    const int delta = lim ? -cur.causal - 2 - wk0 : cur.r0 - wk0;
-    const bool masked = lim ? delta < 31 : (cur.causal != 0 && delta < 32);
-    const int rmask = lim ? 0 : -1;
+    int delta = cur.r0 - wk0, rmask = -1;
+    bool masked = cur.causal && delta < 32;
+    if constexpr (LIM) {
+      const bool lim = cur.causal < 0;
+      delta = lim ? -cur.causal - 2 - wk0 : delta;
+      masked = lim ? delta < 31 : (cur.causal != 0 && delta < 32);
+      rmask = lim ? 0 : -1;
+    }
     cur = nx;
     step_next(nx, ee, a.entries);
     iteration(bp, bc, bn, masked, delta, rmask);
@@ -1234,7 +1241,9 @@ static hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
   constexpr bool pipe = !IsSplit<T>::value;
   constexpr int bytes = pipe ? DkdvPipeCfg<D>::BYTES : DkdvCfg<T, D>::BYTES;
-  auto kern = pipe ? tree_attn_dkdv_pipe_kernel<D> : tree_attn_dkdv_kernel<T, D>;
+  auto kern = pipe ? (a.has_limit ? tree_attn_dkdv_pipe_kernel<D, true>
+                                   : tree_attn_dkdv_pipe_kernel<D, false>)
+                   : tree_attn_dkdv_kernel<T, D>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
@@ -1272,8 +1281,10 @@ static hipError_t post_t(const BwdArgs& a, hipStream_t s) {
   template __global__ void tree_attn_dkdv_kernel<T, D>(BwdArgs);            \
   template __global__ void tree_attn_dq_kernel<T, D>(BwdArgs);              \
   template __global__ void tree_attn_bwd_reduce_kernel<T, D>(BwdArgs);
-template __global__ void tree_attn_dkdv_pipe_kernel<128>(BwdArgs);
-template __global__ void tree_attn_dkdv_pipe_kernel<64>(BwdArgs);
+template __global__ void tree_attn_dkdv_pipe_kernel<128, false>(BwdArgs);
+template __global__ void tree_attn_dkdv_pipe_kernel<64, false>(BwdArgs);
+template __global__ void tree_attn_dkdv_pipe_kernel<128, true>(BwdArgs);
+template __global__ void tree_attn_dkdv_pipe_kernel<64, true>(BwdArgs);
 TREE_ATTN_INSTANTIATE(__bf16, 128)
 TREE_ATTN_INSTANTIATE(__bf16, 64)
 TREE_ATTN_INSTANTIATE(float, 128)

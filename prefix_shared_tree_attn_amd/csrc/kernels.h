@@ -48,6 +48,7 @@ struct BwdArgs {
   int64_t n_tokens;
   int64_t n_items;
   int64_t n_reduce;
+  int has_limit;     // some entry carries a key limit (mask < 0)
   int64_t n_groups;  // dQ: tiles * hkv
   int64_t dq_blocks; // dQ launch size
   int hq, hkv, gsize;

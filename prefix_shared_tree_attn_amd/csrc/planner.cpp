@@ -341,6 +341,7 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
       // side subtrees of n_a .. n_(b-1): only the keys before their node's end
       for (size_t j = a; j < b; ++j)
         for (const Range& rg : side[run[j]]) {
+          p.bwd_has_limit = true;
           kt.limited.push_back({rg, seg_end(run[j])});
           kt.rows += rg.e - rg.b;
         }

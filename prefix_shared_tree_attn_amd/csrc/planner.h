@@ -72,6 +72,7 @@ struct HostPlan {
   std::vector<I8> bwd_reduce;
   int64_t bwd_slots = 0;
   int64_t bwd_split_tiles = 0;
+  bool bwd_has_limit = false;  // some entry carries a key limit
 
   // segments sorted by start: (seg_start, seg_len, depth offset = ancestor
   // tokens of the node, node index), for the per-token position pass

@@ -67,6 +67,25 @@ def test_small_tree_elementwise(name):
     _compare_full(t, hq, hkv, d, dtype, do_std=1.0 if dtype == "fp32" else 1e-2)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_random_tree_sweep(seed):
+    """Seeded random forests, packed depth first (parent-child runs, key
+    tiles that cross node boundaries, key-limit entries) or in a random
+    order, with random head counts, head dims and both dtypes."""
+    import prefix_shared_tree_attn_amd as ta
+    rng = np.random.default_rng(1000 + seed)
+    t = random_tree(rng, int(rng.integers(2, 25)), max_len=int(rng.choice([40, 150, 300])),
+                    n_roots=int(rng.integers(1, 3)), shuffle=seed % 2 == 1)
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    dtype = "fp32" if seed % 5 == 4 else "bf16"
+    ex = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, d, dtype).export()
+    print(f"sweep seed {seed}: key-limit entries {int((ex['bwd_entries'][:, 3] < 0).sum())}",
+          flush=True)
+    _compare_full(t, hq, hkv, d, dtype, do_std=1.0 if dtype == "fp32" else 1e-2)
+
+
 def test_split_case_really_splits():
     import prefix_shared_tree_attn_amd as ta
     t, hq, hkv, d, dtype = CASES["heavy-prompt-split"]

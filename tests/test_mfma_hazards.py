@@ -27,8 +27,10 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "prefix_shared_tree_attn_amd", "csrc")
 KERNELS = [
-    "_ZN9tree_attn26tree_attn_dkdv_pipe_kernelILi128EEEvNS_7BwdArgsE",
-    "_ZN9tree_attn26tree_attn_dkdv_pipe_kernelILi64EEEvNS_7BwdArgsE",
+    "_ZN9tree_attn26tree_attn_dkdv_pipe_kernelILi128ELb0EEEvNS_7BwdArgsE",
+    "_ZN9tree_attn26tree_attn_dkdv_pipe_kernelILi64ELb0EEEvNS_7BwdArgsE",
+    "_ZN9tree_attn26tree_attn_dkdv_pipe_kernelILi128ELb1EEEvNS_7BwdArgsE",
+    "_ZN9tree_attn26tree_attn_dkdv_pipe_kernelILi64ELb1EEEvNS_7BwdArgsE",
 ]
 BEFORE, AFTER = 2, 16
 
