@@ -671,7 +671,9 @@ def main() -> int:
         "roofline_kernels": {k: roof(k) for k in ("fwd", "bwd_dkdv", "bwd_dq")},
         "hbm_passes_GBps": {
             "positions": 8 * n / (avg_ms("positions") * 1e-3) / 1e9,
-            "bwd_pre": pre_bytes / (avg_ms("bwd_pre") * 1e-3) / 1e9,
+            # bf16: the dQ kernel computes the row terms (no separate launch)
+            "bwd_pre": (pre_bytes / (avg_ms("bwd_pre") * 1e-3) / 1e9
+                        if kt["bwd_pre"]["launches"] else None),
             "bwd_reduce": (red_bytes / (avg_ms("bwd_reduce") * 1e-3) / 1e9
                            if kt["bwd_reduce"]["launches"] else None),
             "peak": PEAK_HBM_GBS,
