@@ -13,8 +13,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tree_inputs import (NodeTable, binary_tree, chain_tree, config_spec, config_tree,
-                         random_tree, star_tree, trunk_tree)
+from tree_inputs import (NodeTable, binary_tree, caterpillar_tree, chain_tree, config_spec,
+                         config_tree, random_tree, star_tree, trunk_tree)
 from gpu_util import LSE_ABS, REL_L2, make, rel_l2, run_library
 
 pytestmark = pytest.mark.gpu
@@ -58,6 +58,11 @@ CASES = {
     "binary-fp32": (binary_tree(100, 70, 3), 2, 1, 128, "fp32"),
     "star-d64-fp32": (star_tree(200, 3, 150), 2, 1, 64, "fp32"),
     "heavy-prompt-split": (star_tree(1024, 16, 64), 4, 2, 128, "bf16"),
+    # dozens of short trunk nodes per key tile, a key limit per leaf
+    "caterpillar": (caterpillar_tree([1 + (7 * i) % 3 for i in range(150)], 5), 4, 2, 128,
+                    "bf16"),
+    "caterpillar-fp32": (caterpillar_tree([1 + (5 * i) % 4 for i in range(90)], 9), 2, 1, 64,
+                         "fp32"),
 }
 
 

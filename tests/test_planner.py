@@ -14,7 +14,8 @@ import pytest
 
 import prefix_shared_tree_attn_amd as ta
 from prefix_shared_tree_attn_amd import _ffi
-from tree_inputs import NodeTable, binary_tree, chain_tree, config_tree, random_tree, star_tree, tree_stats
+from tree_inputs import (NodeTable, binary_tree, caterpillar_tree, chain_tree, config_tree,
+                         random_tree, star_tree, tree_stats)
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tree_attn.h")
 
@@ -349,3 +350,25 @@ def test_key_and_query_tiles_cross_node_boundaries_inside_runs():
     assert len(lim) > 0 and set((-lim[:, 3] - 1).tolist()) == {300}
     # those rows are the other four responses (stored after the first)
     assert int(lim[:, 1].min()) >= run and int(lim[:, 2].max()) <= t.num_tokens
+
+
+def test_caterpillar_tiles_span_many_nodes():
+    """A trunk of 1-3 token nodes, each with a leaf: one key tile spans dozens
+    of trunk nodes and carries a key-limit entry per leaf below them; every
+    (query, key, head) is still covered exactly once."""
+    rng = np.random.default_rng(4)
+    t = caterpillar_tree([int(x) for x in rng.integers(1, 4, 150)], 5)
+    hq, hkv = 2, 1
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, 64, num_cus=4)
+    ex = p.export()
+    vis = _visible(t)
+    fp = _fwd_pairs(ex, hq, hkv)
+    assert set(fp) == vis and set(fp.values()) == {1}
+    bt = _bwd_triples(ex)
+    assert set(bt) == {(q, key, h) for (q, key) in vis for h in range(hq)}
+    assert set(bt.values()) == {1}
+    trunk = int(t.seg_len[:150].sum())
+    # the deepest leaf is stored right after the trunk and continues its run;
+    # every other leaf is a run of its own
+    assert len(ex["fwd_tiles"]) == -(-(trunk + 5) // 128) + 149
+    assert int((ex["bwd_entries"][:, 3] < 0).sum()) > 100

@@ -25,6 +25,7 @@ from .trees import (  # noqa: F401
     trunk_tree,
     tree_stats,
     dfs_preorder,
+    caterpillar_tree,
 )
 from .tensors import (  # noqa: F401
     bf16_round_bits,

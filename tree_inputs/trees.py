@@ -175,6 +175,19 @@ def random_tree(rng: np.random.Generator, n_nodes: int, max_len: int = 40,
     return _from_lists(new_par, new_len, name, order)
 
 
+def caterpillar_tree(trunk_lens: List[int], leaf_len: int,
+                     name: str = "caterpillar") -> NodeTable:
+    """A trunk of nodes (each the first child of the previous) with one leaf
+    child per trunk node, packed in depth-first preorder: the whole trunk is
+    contiguous, then the leaves deepest first.  Many short trunk nodes share
+    each 128-token tile, and each of their leaves sees only part of it."""
+    n = len(trunk_lens)
+    parents = [-1] + list(range(n - 1)) + list(range(n))
+    lens = list(trunk_lens) + [leaf_len] * n
+    order = list(range(n)) + [n + i for i in reversed(range(n))]
+    return _from_lists(parents, lens, name, order)
+
+
 def dfs_preorder(parent) -> List[int]:
     """Node indices in depth-first preorder (roots and children in index
     order): the order in which a depth-first walk of the tree visits each
