@@ -6,8 +6,9 @@ time, each shared prefix computed once) runs one forward call per node in
 preorder and one accumulating backward call per node in reverse preorder.
 Summed over the walk, the results must be the whole tree's: checked against
 the fp64 oracle (whole tensors on small trees, sampled rows and keys on the
-GRPO-star workload at full size) and against the one-call library path (O,
-LSE and dQ bitwise: the same tiles run the same kernels).  One call on a
+GRPO-star and segment-search workloads at full size) and against the
+one-call library path (O, LSE and dQ bitwise: the same tiles run the same
+kernels).  One call on a
 random set of nodes is checked against ``oracle.tree_attention_subset``.
 Bar: relative L2 <= 1e-2 on O, dQ, dK, dV and max |LSE error| <= 1e-3.
 """
@@ -183,15 +184,17 @@ def test_plan_kind_checks_and_empty_subset():
         p.close()
 
 
-def test_full_size_walk_grpo_star():
-    """The GRPO-star workload at full size, one node per call (17 calls per
-    pass): sampled rows and keys against the oracle, whole tensors against
-    the one-call path."""
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_full_size_walk(cfg):
+    """The GRPO-star (17 nodes) and segment-search (127 nodes) workloads at
+    full size, one node per call: sampled rows and keys against the oracle,
+    whole tensors against the one-call path (whose query tiles are the
+    walk's on these trees, every node a multiple of 128 tokens)."""
     import torch
-    t = config_tree(2)
-    sp = config_spec(2)
+    t = config_tree(cfg)
+    sp = config_spec(cfg)
     hq, hkv, d, dtype, scale = sp["heads_q"], sp["heads_kv"], sp["head_dim"], sp["dtype"], sp["scale"]
-    print(f"config 2 walk: N={t.num_tokens} nodes={t.num_nodes}", flush=True)
+    print(f"config {cfg} walk: N={t.num_tokens} nodes={t.num_nodes}", flush=True)
     x = make(t, hq, hkv, d, dtype, do_std=sp["do_std"])
     dev = device_inputs(x, dtype)
     got = _walk(t, dev, hq, hkv, d, dtype, scale)
@@ -207,7 +210,7 @@ def test_full_size_walk_grpo_star():
     rows = sorted(set([0, t.num_tokens - 1] + [int(r) for r in rng.integers(0, t.num_tokens, 10)]))
     heads = [int(rng.integers(0, hq))]
     g = heads[0] // (hq // hkv)
-    prompt = int(t.seg_len[0])
+    prompt = int(t.seg_len[0])  # node 0 is the root on both trees
     keys = [0, prompt - 1, prompt + 5, t.num_tokens - 1]
     o, lse, dq = oracle.query_rows(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len, scale,
                                    rows, heads)
