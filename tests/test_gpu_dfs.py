@@ -225,3 +225,52 @@ def test_full_size_walk(cfg):
     for k in ("o", "dq", "dk", "dv"):
         assert errs[k] <= REL_L2, (k, errs)
     assert errs["lse"] <= LSE_ABS
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_subset_sweep(seed):
+    """Seeded random forests (depth-first or random packing, both dtypes,
+    D 64/128, GQA) with a random set of query nodes, one call, against
+    ``oracle.tree_attention_subset``; accumulators start from zero."""
+    import torch
+    import prefix_shared_tree_attn_amd as ta
+    rng = np.random.default_rng(2000 + seed)
+    t = random_tree(rng, int(rng.integers(3, 20)), max_len=int(rng.choice([60, 200])),
+                    n_roots=int(rng.integers(1, 3)), shuffle=seed % 2 == 1)
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    dtype = "fp32" if seed % 3 == 2 else "bf16"
+    qn = sorted(int(i) for i in rng.choice(t.num_nodes, size=int(rng.integers(1, t.num_nodes + 1)),
+                                           replace=False))
+    print(f"subset sweep seed {seed}: N={t.num_tokens} nodes={t.num_nodes} hq={hq} hkv={hkv} "
+          f"d={d} {dtype} query nodes={qn}", flush=True)
+    scale = 1.0 / np.sqrt(d)
+    x = make(t, hq, hkv, d, dtype, do_std=1.0 if dtype == "fp32" else 1e-2)
+    dev = device_inputs(x, dtype)
+    n = t.num_tokens
+    p = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype, query_nodes=qn)
+    tdt = dev["q"].dtype
+    o = torch.zeros((n, hq, d), dtype=tdt, device="cuda")
+    lse = torch.zeros((hq, n), dtype=torch.float32, device="cuda")
+    dq = torch.zeros((n, hq, d), dtype=tdt, device="cuda")
+    dk_acc = torch.zeros((n, hkv, d), dtype=torch.float32, device="cuda")
+    dv_acc = torch.zeros_like(dk_acc)
+    ta.fwd(p, dev["q"], dev["k"], dev["v"], scale, o=o, lse=lse)
+    ta.bwd_accum(p, dev["q"], dev["k"], dev["v"], o, lse, dev["do"], scale, dk_acc, dv_acc, dq=dq)
+    torch.cuda.synchronize()
+    p.close()
+    ref = oracle.tree_attention_subset(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len,
+                                       scale, qn)
+    rows = ref["rows"]
+    errs = {"o": rel_l2(_host(o)[rows], ref["o"][rows]),
+            "dq": rel_l2(_host(dq)[rows], ref["dq"][rows]),
+            "dk": rel_l2(_host(dk_acc), ref["dk"]),
+            "dv": rel_l2(_host(dv_acc), ref["dv"]),
+            "lse": float(np.abs(_host(lse)[:, rows] - ref["lse"][:, rows]).max())}
+    print("errors:", errs, flush=True)
+    for k in ("o", "dq", "dk", "dv"):
+        assert errs[k] <= REL_L2, (k, errs)
+    assert errs["lse"] <= LSE_ABS
+    # rows outside the subset stay as they were
+    assert not bool(o[torch.from_numpy(~rows).cuda()].any())
