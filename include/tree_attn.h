@@ -79,7 +79,11 @@ typedef struct tree_attn_plan_s* tree_attn_plan_t; /* opaque, immutable */
  *
  * The plan holds the work items of the forward pass (query tiles with the
  * key ranges of their ancestors) and of the backward pass (key tiles with
- * the query ranges of their descendants), ordered longest first.  Its small
+ * the query ranges of their descendants), ordered longest first.  A node
+ * stored right after its parent continues the parent's run, and tiles are
+ * cut over runs rather than single nodes, so packing the nodes in
+ * depth-first preorder (as tree_attn_build_tree does) leaves fewer
+ * part-filled tiles; any packing order gives the same results.  Its small
  * device arrays are copied asynchronously on `stream`; the plan may be used
  * on any stream once `stream` has passed this point, and reused by any
  * number of fwd/bwd calls (e.g. every layer of a model).
