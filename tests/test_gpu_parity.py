@@ -91,6 +91,25 @@ def test_random_tree_sweep(seed):
     _compare_full(t, hq, hkv, d, dtype, do_std=1.0 if dtype == "fp32" else 1e-2)
 
 
+@pytest.mark.parametrize("seed", range(40))
+def test_random_tree_sweep_wide(seed):
+    """Forty more seeded trees: random forests of 1-39 nodes with segments up
+    to 400 tokens (a third packed in random order) and, every eighth seed, a
+    caterpillar; 1, 2 or 4 kv heads with groups of 1-8; both dtypes."""
+    rng = np.random.default_rng(5000 + seed)
+    if seed % 8 == 7:
+        t = caterpillar_tree([int(x) for x in rng.integers(1, 40, int(rng.integers(5, 60)))],
+                             int(rng.integers(1, 200)))
+    else:
+        t = random_tree(rng, int(rng.integers(1, 40)), max_len=int(rng.choice([20, 130, 400])),
+                        min_len=1, n_roots=int(rng.integers(1, 4)), shuffle=bool(seed % 3 == 0))
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 3, 8]))
+    d = int(rng.choice([64, 128]))
+    dtype = "fp32" if seed % 6 == 5 else "bf16"
+    _compare_full(t, hq, hkv, d, dtype, do_std=1.0 if dtype == "fp32" else 1e-2)
+
+
 def test_split_case_really_splits():
     import prefix_shared_tree_attn_amd as ta
     t, hq, hkv, d, dtype = CASES["heavy-prompt-split"]
