@@ -14,8 +14,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tree_inputs import (NodeTable, binary_tree, chain_tree, config_spec, config_tree,
-                         random_tree, star_tree)
+from tree_inputs import (NodeTable, binary_tree, caterpillar_tree, chain_tree, config_spec,
+                         config_tree, random_tree, star_tree)
 from gpu_util import REL_L2, device_inputs, make, rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -51,6 +51,34 @@ CASES = {
     "star-1024": (star_tree(1024, 6, 300), 4, 1, 128),
 }
 
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_linear_random_sweep(seed):
+    """Seeded random forests and caterpillars (many nodes shorter than a
+    64-token chunk, so most pieces start at branch points), depth-first or
+    random packing, GQA groups of 1-8, D 64/128."""
+    rng = np.random.default_rng(7000 + seed)
+    if seed % 4 == 3:
+        t = caterpillar_tree([int(x) for x in rng.integers(1, 30, int(rng.integers(5, 50)))],
+                             int(rng.integers(1, 90)))
+    else:
+        t = random_tree(rng, int(rng.integers(1, 30)), max_len=int(rng.choice([10, 70, 250])),
+                        n_roots=int(rng.integers(1, 3)), shuffle=bool(seed % 3 == 0))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 8]))
+    d = int(rng.choice([64, 128]))
+    scale = 1.0 / np.sqrt(d)
+    x = make(t, hq, hkv, d, "bf16")
+    print(f"linear sweep seed {seed}: N={t.num_tokens} nodes={t.num_nodes} hq={hq} hkv={hkv} "
+          f"d={d}", flush=True)
+    got = _run(t, x, hq, hkv, d, scale)
+    ref = oracle.tree_linear_attention(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len,
+                                       scale)
+    errs = {k: rel_l2(got[k], ref[k]) for k in ("o", "dq", "dk", "dv")}
+    print("errors:", errs, flush=True)
+    for k, v in errs.items():
+        assert v <= REL_L2, (k, errs)
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_linear_parity(name):
