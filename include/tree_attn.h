@@ -55,10 +55,22 @@ typedef enum {
   TREE_ATTN_ERR_UNSUPPORTED = 4,  /* head_dim, dtype or head counts         */
   TREE_ATTN_ERR_WORKSPACE = 5,    /* workspace missing or too small         */
   TREE_ATTN_ERR_HIP = 6,          /* a HIP runtime call failed              */
-  TREE_ATTN_ERR_NO_DEVICE_PLAN = 7 /* host-only plan passed to fwd/bwd      */
+  TREE_ATTN_ERR_NO_DEVICE_PLAN = 7, /* host-only plan passed to fwd/bwd     */
+  /* Not statuses: these two make every int32 value a valid value of the
+   * type, so that a C caller's unknown value reaches the library as a
+   * number it can reject instead of undefined behaviour. */
+  TREE_ATTN_STATUS_RANGE_MIN_ = -0x7fffffff - 1,
+  TREE_ATTN_STATUS_RANGE_MAX_ = 0x7fffffff
 } tree_attn_status_t;
 
-typedef enum { TREE_ATTN_BF16 = 0, TREE_ATTN_FP32 = 1 } tree_attn_dtype_t;
+typedef enum {
+  TREE_ATTN_BF16 = 0,
+  TREE_ATTN_FP32 = 1,
+  /* not dtypes (see tree_attn_status_t): any other value is rejected with
+   * TREE_ATTN_ERR_UNSUPPORTED */
+  TREE_ATTN_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  TREE_ATTN_DTYPE_RANGE_MAX_ = 0x7fffffff
+} tree_attn_dtype_t;
 
 typedef struct tree_attn_plan_s* tree_attn_plan_t; /* opaque, immutable */
 
@@ -138,8 +150,12 @@ tree_attn_status_t tree_attn_workspace_size(tree_attn_plan_t plan, size_t* fwd_b
  * q, k, v: device inputs in the plan's dtype; o: device output [N,Hq,D]
  * (same dtype, overwritten); lse: device output [Hq,N] fp32 (overwritten).
  * ws/ws_bytes: device workspace of at least fwd_bytes (may be null when 0).
- * The softmax scale is typically 1/sqrt(D).  Accumulation is fp32; bf16
- * outputs are rounded to nearest even.
+ * The softmax scale is typically 1/sqrt(D); it must be finite and > 0
+ * (masked scores are -inf before scaling), else INVALID_ARG.  Every tensor
+ * pointer (q, k, v, o, lse) must be 16-byte aligned (rows move in 16-byte
+ * pieces), else INVALID_ARG; torch allocations and whole-row views are.
+ * Both checks happen before any launch.  Accumulation is fp32; bf16 outputs
+ * are rounded to nearest even.
  */
 tree_attn_status_t tree_attn_fwd(tree_attn_plan_t plan, const void* q, const void* k,
                                  const void* v, float softmax_scale, void* o, float* lse,
@@ -154,7 +170,9 @@ tree_attn_status_t tree_attn_fwd(tree_attn_plan_t plan, const void* q, const voi
  * dK and dV of a shared token are summed over every branch below it and over
  * the G query heads of its group.  Outputs are overwritten, not accumulated.
  * ws must hold at least bwd_bytes (256-byte aligned).  No atomics are used:
- * dQ, dK and dV are bitwise reproducible from run to run.
+ * dQ, dK and dV are bitwise reproducible from run to run.  softmax_scale
+ * and tensor-pointer alignment (16 bytes, all of q, k, v, o, lse, dout, dq,
+ * dk, dv) are checked as in tree_attn_fwd, before any launch.
  */
 tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const void* k,
                                  const void* v, const void* o, const float* lse,
@@ -426,8 +444,10 @@ tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_til
  * forward, 3 piece arrays and the node array backward);
  * it holds no result between calls.  The backward pass recomputes the
  * forward states itself, so it does not need the forward's workspace or O.
- * Errors as for tree_attn_fwd: invalid arguments are rejected before any
- * launch; TREE_ATTN_ERR_WORKSPACE for a missing or short workspace.
+ * Errors as for tree_attn_fwd: invalid arguments (null or not 16-byte
+ * aligned tensor pointers, a scale that is not finite; any finite scale,
+ * including negative, is valid here) are rejected before any launch;
+ * TREE_ATTN_ERR_WORKSPACE for a missing or short workspace.
  */
 tree_attn_status_t tree_attn_lin_workspace_size(tree_attn_plan_t plan, size_t* fwd_bytes,
                                                 size_t* bwd_bytes);

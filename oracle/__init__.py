@@ -19,6 +19,7 @@ from .path_expansion import (  # noqa: F401
     tree_attention_subset,
     query_rows,
     key_rows,
+    key_rows_by_row,
 )
 from .linear_attention import (  # noqa: F401,E402
     causal_linear_attention,

@@ -373,3 +373,92 @@ def key_rows(q, k, v, do, parent, seg_start, seg_len, scale: float,
                 dk[kl] += scale * (ds[:, pl].T @ qp[r0:r1])
                 dv[kl] += pr[:, pl].T @ dop[r0:r1]
     return dk, dv
+
+
+def key_rows_by_row(q, k, v, do, parent, seg_start, seg_len, scale: float,
+                    keys: Sequence[int], kv_head: int, row_block: int = 1024):
+    """dK and dV of selected packed key rows of one kv head, fp64, taken over
+    unique query rows rather than over paths.
+
+    The sums are those of ``key_rows``.  A unique row t lies on ``mult(t)``
+    paths; each path copy has the same forward values (its context is the
+    same ancestors-plus-earlier-rows list) and carries ``dO_t / mult(t)``, so
+    its dS row is ``1 / mult(t)`` of the dS row formed with the whole
+    ``dO_t``, and the ``mult(t)`` copies together contribute exactly that
+    row once.  So each row that can see a selected key is visited once, with
+    its whole dO: S = scale q_t K_ctx^T over its context (its node's
+    ancestors root first, then its own segment up to t), P its softmax, dP =
+    dO_t V_ctx^T, dS = P (dP - P.dP), and for every selected key u of the
+    context dK_u += scale dS_u q_t, dV_u += P_u dO_t, summed over the group's
+    query heads.  The rows that can see a key are the later rows of its node
+    and every row of every node below it.  A node's rows are taken
+    ``row_block`` at a time to bound memory.  Returns ``dk, dv`` [K, D].
+    """
+    n, hq, hkv, d = _check_shapes(q, k, v, do)
+    g_size = hq // hkv
+    parent = np.asarray(parent, np.int64)
+    seg_start = np.asarray(seg_start, np.int64)
+    seg_len = np.asarray(seg_len, np.int64)
+    keys = np.asarray(keys, np.int64)
+    m = parent.shape[0]
+    children = [[] for _ in range(m)]
+    for i in range(m):
+        if parent[i] >= 0:
+            children[parent[i]].append(i)
+    key_node = _node_of_rows(seg_start, seg_len, keys)
+    # nodes whose rows may see a selected key: the keys' nodes and everything
+    # below them
+    todo = sorted(set(int(x) for x in key_node))
+    visit = set()
+    while todo:
+        a = todo.pop()
+        if a in visit:
+            continue
+        visit.add(a)
+        todo.extend(children[a])
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), d))
+    g = kv_head
+    for node in sorted(visit):
+        chain = []
+        a = int(parent[node])
+        while a >= 0:
+            chain.append(a)
+            a = int(parent[a])
+        chain.reverse()
+        anc = (np.concatenate([np.arange(seg_start[c], seg_start[c] + seg_len[c]) for c in chain])
+               if chain else np.zeros(0, np.int64))
+        own = np.arange(seg_start[node], seg_start[node] + seg_len[node])
+        ctx_all = np.concatenate([anc, own])
+        col = {int(t): i for i, t in enumerate(ctx_all)}
+        sel = [(ki, col[int(t)]) for ki, t in enumerate(keys) if int(t) in col]
+        if not sel:
+            continue
+        kidx = np.array([s[0] for s in sel])
+        kcol = np.array([s[1] for s in sel])
+        A = anc.shape[0]
+        # rows of this node before its first selected own key see none of them
+        # unless a selected key is an ancestor row
+        first = 0 if kcol.min() < A else int(kcol.min()) - A
+        kc = np.asarray(k[ctx_all, g], np.float64)
+        vc = np.asarray(v[ctx_all, g], np.float64)
+        for r0 in range(first, own.shape[0], row_block):
+            r1 = min(own.shape[0], r0 + row_block)
+            rows = own[r0:r1]
+            width = A + r1  # context columns any of these rows can see
+            future = np.arange(width)[None, :] > (A + np.arange(r0, r1))[:, None]
+            live = kcol < width
+            kl, cl = kidx[live], kcol[live]
+            for h in range(g * g_size, (g + 1) * g_size):
+                qr = np.asarray(q[rows, h], np.float64)
+                dor = np.asarray(do[rows, h], np.float64)
+                s = scale * (qr @ kc[:width].T)
+                s[future] = -np.inf
+                mx = s.max(axis=1, keepdims=True)
+                e = np.exp(s - mx)
+                pr = e / e.sum(axis=1, keepdims=True)
+                dp = dor @ vc[:width].T
+                ds = pr * (dp - (pr * dp).sum(axis=1, keepdims=True))
+                dk[kl] += scale * (ds[:, cl].T @ qr)
+                dv[kl] += pr[:, cl].T @ dor
+    return dk, dv

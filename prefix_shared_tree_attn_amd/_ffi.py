@@ -5,7 +5,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtree_attn.so")
+# TREE_ATTN_LIBRARY selects another build of the same library (the host
+# sanitizer build that the CPU tests run the planner tests against).
+LIB_PATH = os.environ.get("TREE_ATTN_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libtree_attn.so")
 
 STATUS = {
     0: "OK", 1: "INVALID_ARG", 2: "BAD_TREE", 3: "LAYOUT", 4: "UNSUPPORTED",

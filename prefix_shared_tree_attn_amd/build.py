@@ -25,10 +25,10 @@ SOURCES = ["api.cpp", "planner.cpp", "prefix_tree.cpp", "fwd.hip", "bwd.hip", "p
            "prefix_ops.hip", "linear.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
-# Device code: no hand-picked packed fp32 ops (the feature is disabled), fast
-# hardware fp32 atomics for the dQ accumulator.
-DEVICE = [f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Device code: the packed fp32 instructions are disabled (the compiler would
+# otherwise form them from ordinary float code).  The kernels use no atomics.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE = [f"--offload-arch={ARCH}", *DEVICE_FLAGS]
 
 
 def _hipcc() -> str:
@@ -70,5 +70,48 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host sanitizer build: the host sources (planner, prefix-tree builder, C
+# ABI) compiled by the host compiler with AddressSanitizer and
+# UndefinedBehaviorSanitizer, linked with the regular device objects.  Only
+# host code is instrumented; no GPU code is built with a sanitizer.
+HOST_SOURCES = ["api.cpp", "planner.cpp", "prefix_tree.cpp"]
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(BUILD, "libtree_attn_hostsan.so")
+DEVICE_OBJECTS = [s + ".o" for s in SOURCES if s.endswith(".hip")]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Builds ``_build/libtree_attn_hostsan.so`` (see above) and returns its
+    path.  Load it with TREE_ATTN_LIBRARY set to that path and the sanitizer
+    runtime preloaded (LD_PRELOAD of the compiler's libasan)."""
+    if not all(os.path.exists(os.path.join(BUILD, o)) for o in DEVICE_OBJECTS):
+        build(verbose)
+    out_dir = os.path.join(BUILD, "hostsan")
+    os.makedirs(out_dir, exist_ok=True)
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(out_dir, src + ".o")
+        cmd = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", *SAN_FLAGS, "-D__HIP_PLATFORM_AMD__",
+               f"-I{ROCM}/include", f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"sanitizer build of {src} failed:\n{res.stderr}")
+        objs.append(obj)
+    cmd = ["g++", "-shared", *SAN_FLAGS, "-o", SAN_LIB, *objs,
+           *[os.path.join(BUILD, o) for o in DEVICE_OBJECTS], f"-L{ROCM}/lib", "-lamdhip64",
+           f"-Wl,-rpath,{ROCM}/lib"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitizer link failed:\n{res.stderr}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitizers" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

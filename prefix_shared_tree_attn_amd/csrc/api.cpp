@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <new>
 #include <string>
@@ -51,6 +52,19 @@ tree_attn_status_t report_hip(hipError_t e, const char* what) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// The kernels move tensor rows in 16-byte pieces (vector loads and
+// buffer-to-LDS transfers), so every tensor pointer must be 16-byte aligned.
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return false;
+  return true;
+}
+
+// Softmax attention masks scores with -inf and scales them afterwards, and
+// the forward pass takes row maxima on unscaled scores: the scale must be a
+// positive finite number.
+bool valid_softmax_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
 struct BwdLayout {
   size_t neg_d = 0, neg_lse2 = 0, dk_slots = 0, dv_slots = 0, total = 0;
@@ -332,13 +346,18 @@ tree_attn_status_t tree_attn_fwd(tree_attn_plan_t plan, const void* q, const voi
                                  void* ws, size_t ws_bytes, hipStream_t stream) {
   (void)ws;
   (void)ws_bytes;
+  if (!plan) return report(Status::kInvalidArg, "null plan");
+  const HostPlan& hp = plan->hp;
+  if (hp.num_tokens == 0 || hp.query_rows == 0) return check_device(plan);
+  // argument checks come first, so that a bad call is rejected the same way
+  // on any plan
+  if (!q || !k || !v || !o || !lse) return report(Status::kInvalidArg, "null tensor pointer");
+  if (!aligned16({q, k, v, o, lse}))
+    return report(Status::kInvalidArg, "tensor pointers must be 16-byte aligned");
+  if (!valid_softmax_scale(softmax_scale))
+    return report(Status::kInvalidArg, "softmax_scale must be finite and > 0");
   tree_attn_status_t st = check_device(plan);
   if (st != TREE_ATTN_OK) return st;
-  const HostPlan& hp = plan->hp;
-  if (hp.num_tokens == 0 || hp.query_rows == 0) return TREE_ATTN_OK;
-  if (!q || !k || !v || !o || !lse) return report(Status::kInvalidArg, "null tensor pointer");
-  if (!std::isfinite(softmax_scale))
-    return report(Status::kInvalidArg, "softmax_scale must be finite");
   tree_attn::FwdArgs a{};
   a.q = q;
   a.k = k;
@@ -371,8 +390,7 @@ tree_attn_status_t bwd_common(tree_attn_plan_t plan, const void* q, const void* 
                               const void* v, const void* o, const float* lse, const void* dout,
                               float softmax_scale, void* dq, void* dk, void* dv, void* ws,
                               size_t ws_bytes, hipStream_t stream, bool acc) {
-  tree_attn_status_t st = check_device(plan);
-  if (st != TREE_ATTN_OK) return st;
+  if (!plan) return report(Status::kInvalidArg, "null plan");
   const HostPlan& hp = plan->hp;
   if (acc && !hp.subset)
     return report(Status::kInvalidArg,
@@ -380,17 +398,21 @@ tree_attn_status_t bwd_common(tree_attn_plan_t plan, const void* q, const void* 
   if (!acc && hp.subset)
     return report(Status::kInvalidArg,
                   "a query-subset plan's backward is tree_attn_bwd_accum");
-  if (hp.num_tokens == 0 || hp.query_rows == 0) return TREE_ATTN_OK;
+  if (hp.num_tokens == 0 || hp.query_rows == 0) return check_device(plan);
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return report(Status::kInvalidArg, "null tensor pointer");
-  if (!std::isfinite(softmax_scale))
-    return report(Status::kInvalidArg, "softmax_scale must be finite");
+  if (!aligned16({q, k, v, o, lse, dout, dq, dk, dv}))
+    return report(Status::kInvalidArg, "tensor pointers must be 16-byte aligned");
+  if (!valid_softmax_scale(softmax_scale))
+    return report(Status::kInvalidArg, "softmax_scale must be finite and > 0");
   const BwdLayout l = bwd_layout(hp);
   if (!ws || ws_bytes < l.total)
     return report(Status::kWorkspace, "backward workspace needs " + std::to_string(l.total) +
                                           " bytes, got " + std::to_string(ws_bytes));
   if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
     return report(Status::kWorkspace, "workspace must be 256-byte aligned");
+  tree_attn_status_t st = check_device(plan);
+  if (st != TREE_ATTN_OK) return st;
   char* w = static_cast<char*>(ws);
   tree_attn::BwdArgs a{};
   a.q = q;
@@ -531,6 +553,8 @@ tree_attn_status_t tree_attn_lin_fwd(tree_attn_plan_t plan, const void* q, const
   tree_attn_status_t st = lin_common(plan, scale, ws, ws_bytes, 2 * blk + lin_ends(plan->hp));
   if (st != TREE_ATTN_OK || plan->hp.num_tokens == 0) return st;
   if (!q || !k || !v || !o) return report(Status::kInvalidArg, "null tensor pointer");
+  if (!aligned16({q, k, v, o}))
+    return report(Status::kInvalidArg, "tensor pointers must be 16-byte aligned");
   tree_attn::LinArgs a = lin_args(plan, scale);
   a.q = q;
   a.k = k;
@@ -559,6 +583,8 @@ tree_attn_status_t tree_attn_lin_bwd(tree_attn_plan_t plan, const void* q, const
   if (st != TREE_ATTN_OK || plan->hp.num_tokens == 0) return st;
   if (!q || !k || !v || !dout || !dq || !dk || !dv)
     return report(Status::kInvalidArg, "null tensor pointer");
+  if (!aligned16({q, k, v, dout, dq, dk, dv}))
+    return report(Status::kInvalidArg, "tensor pointers must be 16-byte aligned");
   char* w = static_cast<char*>(ws);
   tree_attn::LinArgs a = lin_args(plan, scale);
   a.q = q;
@@ -727,10 +753,15 @@ tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_til
                                          int32_t* bwd_entries) {
   if (!plan) return report(Status::kInvalidArg, "null plan");
   const HostPlan& hp = plan->hp;
-  if (fwd_tiles) std::memcpy(fwd_tiles, hp.fwd_tiles.data(), bytes_of(hp.fwd_tiles));
-  if (fwd_ranges) std::memcpy(fwd_ranges, hp.fwd_ranges.data(), bytes_of(hp.fwd_ranges));
-  if (bwd_items) std::memcpy(bwd_items, hp.bwd_items.data(), bytes_of(hp.bwd_items));
-  if (bwd_entries) std::memcpy(bwd_entries, hp.bwd_entries.data(), bytes_of(hp.bwd_entries));
+  // (memcpy from the null data() of an empty vector is undefined even for 0 bytes)
+  if (fwd_tiles && !hp.fwd_tiles.empty())
+    std::memcpy(fwd_tiles, hp.fwd_tiles.data(), bytes_of(hp.fwd_tiles));
+  if (fwd_ranges && !hp.fwd_ranges.empty())
+    std::memcpy(fwd_ranges, hp.fwd_ranges.data(), bytes_of(hp.fwd_ranges));
+  if (bwd_items && !hp.bwd_items.empty())
+    std::memcpy(bwd_items, hp.bwd_items.data(), bytes_of(hp.bwd_items));
+  if (bwd_entries && !hp.bwd_entries.empty())
+    std::memcpy(bwd_entries, hp.bwd_entries.data(), bytes_of(hp.bwd_entries));
   return TREE_ATTN_OK;
 }
 
@@ -781,6 +812,7 @@ const char* tree_attn_status_string(tree_attn_status_t s) {
     case TREE_ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case TREE_ATTN_ERR_HIP: return "HIP runtime error";
     case TREE_ATTN_ERR_NO_DEVICE_PLAN: return "plan has no device data";
+    default: break;
   }
   return "unknown status";
 }

@@ -1239,11 +1239,17 @@ static hipError_t pre_t(const BwdArgs& a, hipStream_t s) {
 template <typename T, int D>
 static hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
-  constexpr bool pipe = !IsSplit<T>::value;
-  constexpr int bytes = pipe ? DkdvPipeCfg<D>::BYTES : DkdvCfg<T, D>::BYTES;
-  auto kern = pipe ? (a.has_limit ? tree_attn_dkdv_pipe_kernel<D, true>
-                                   : tree_attn_dkdv_pipe_kernel<D, false>)
-                   : tree_attn_dkdv_kernel<T, D>;
+  // bf16: the software-pipelined kernel; fp32: the kernel with split
+  // operands (the only instantiation of tree_attn_dkdv_kernel)
+  void (*kern)(BwdArgs);
+  int bytes;
+  if constexpr (IsSplit<T>::value) {
+    kern = tree_attn_dkdv_kernel<T, D>;
+    bytes = DkdvCfg<T, D>::BYTES;
+  } else {
+    kern = a.has_limit ? tree_attn_dkdv_pipe_kernel<D, true> : tree_attn_dkdv_pipe_kernel<D, false>;
+    bytes = DkdvPipeCfg<D>::BYTES;
+  }
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
@@ -1278,13 +1284,14 @@ static hipError_t post_t(const BwdArgs& a, hipStream_t s) {
 // always emits its launch stub.
 #define TREE_ATTN_INSTANTIATE(T, D)                                          \
   template __global__ void tree_attn_bwd_pre_kernel<T, D>(BwdArgs);         \
-  template __global__ void tree_attn_dkdv_kernel<T, D>(BwdArgs);            \
   template __global__ void tree_attn_dq_kernel<T, D>(BwdArgs);              \
   template __global__ void tree_attn_bwd_reduce_kernel<T, D>(BwdArgs);
 template __global__ void tree_attn_dkdv_pipe_kernel<128, false>(BwdArgs);
 template __global__ void tree_attn_dkdv_pipe_kernel<64, false>(BwdArgs);
 template __global__ void tree_attn_dkdv_pipe_kernel<128, true>(BwdArgs);
 template __global__ void tree_attn_dkdv_pipe_kernel<64, true>(BwdArgs);
+template __global__ void tree_attn_dkdv_kernel<float, 128>(BwdArgs);
+template __global__ void tree_attn_dkdv_kernel<float, 64>(BwdArgs);
 TREE_ATTN_INSTANTIATE(__bf16, 128)
 TREE_ATTN_INSTANTIATE(__bf16, 64)
 TREE_ATTN_INSTANTIATE(float, 128)

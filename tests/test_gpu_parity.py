@@ -263,6 +263,65 @@ def test_full_size_sampled(cfg):
     assert abs(lhs - rhs) <= 6.0 * noise + 1e-2 * max(abs(lhs), abs(rhs))
     for name in ("o", "dq", "dk", "dv", "lse"):
         assert bool(torch.isfinite(got[name]).all()), name
+    _check_split_tiles(cfg, t, x, got)
+
+
+def _split_slots(t: NodeTable, sp, key: int, g: int):
+    """Number of partial slots of the backward items that hold `key` for kv
+    head g (0 when its key tile is not split)."""
+    import prefix_shared_tree_attn_amd as ta
+    ex = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, sp["heads_q"],
+                      sp["heads_kv"], sp["head_dim"], sp["dtype"]).export()
+    it = ex["bwd_items"]
+    hit = it[(it[:, 0] <= key) & (key < it[:, 1]) & (it[:, 2] == g) & (it[:, 4] > it[:, 3])]
+    return int((hit[:, 5] >= 0).sum())
+
+
+def _check_split_tiles(cfg: int, t: NodeTable, x, got):
+    """dK / dV of keys in heavily shared key tiles whose gradient the library
+    sums from several partial slots (the tile's query rows are split for load
+    balance), in the first and the last kv head, element-wise against the
+    fp64 oracle: live on the GRPO star (its 1024-token prompt), and on the
+    agent, segment-search and long-trunk trees against values the oracle
+    wrote beforehand (tests/golden/make_split_tile_golden.py), checked to
+    come from these very inputs."""
+    import json
+    import os
+    sp = config_spec(cfg)
+    hkv = sp["heads_kv"]
+    if cfg == 2:
+        keys, heads = [0, 511, 1023], [0, hkv - 1]
+        want = {}
+        for g in heads:
+            want[g] = oracle.key_rows_by_row(x.q, x.k, x.v, x.do, t.parent, t.seg_start,
+                                             t.seg_len, sp["scale"], keys, g)
+    else:
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "make_split_tile_golden",
+            os.path.join(os.path.dirname(__file__), "golden", "make_split_tile_golden.py"))
+        msg = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(msg)
+        with open(msg.golden_path(cfg)) as f:
+            rec = json.load(f)
+        assert rec["input_fingerprint"] == msg.input_fingerprint(x), "golden from other inputs"
+        keys, heads = rec["keys"], rec["kv_heads"]
+        want = {g: (np.asarray(rec["dk"][str(g)]), np.asarray(rec["dv"][str(g)]))
+                for g in heads}
+    for g in heads:
+        for kk in keys:
+            n_slots = _split_slots(t, sp, kk, g)
+            print(f"config {cfg} key {kk} kv head {g}: {n_slots} partial slots", flush=True)
+            assert n_slots >= 2, "the sampled key's tile is not split in this plan"
+        import torch
+        ki = torch.tensor(keys, device="cuda")
+        g_dk = got["dk"][ki, g].double().cpu().numpy()
+        g_dv = got["dv"][ki, g].double().cpu().numpy()
+        dk, dv = want[g]
+        for i, kk in enumerate(keys):
+            e_k, e_v = rel_l2(g_dk[i], dk[i]), rel_l2(g_dv[i], dv[i])
+            print(f"  key {kk}: dk rel-L2 {e_k:.2e}, dv rel-L2 {e_v:.2e}", flush=True)
+            assert e_k <= REL_L2 and e_v <= REL_L2
 
 
 def _position_trees():
@@ -286,3 +345,56 @@ def test_positions_bit_exact():
         np.testing.assert_array_equal(node_id.cpu().numpy(), ref_node)
         np.testing.assert_array_equal(pos_id.cpu().numpy(), ref_pos)
         p.close()
+
+
+@pytest.mark.parametrize("name,dtype", [("heavy-prompt-split", "bf16"), ("caterpillar", "bf16"),
+                                        ("binary-fp32", "fp32")])
+def test_outputs_and_workspace_stay_inside_their_buffers(name, dtype):
+    """Canary margins: O, LSE, dQ, dK, dV and the backward workspace are
+    views into larger buffers whose margins (64 KiB before and after) hold
+    a fixed byte pattern; after the forward and backward passes the margins
+    are unchanged and the results still match the oracle."""
+    import torch
+    import prefix_shared_tree_attn_amd as ta
+    from gpu_util import device_inputs
+    t, hq, hkv, d, _ = CASES[name]
+    x = make(t, hq, hkv, d, dtype, do_std=1.0 if dtype == "fp32" else 1e-2)
+    dev = device_inputs(x, dtype)
+    n = t.num_tokens
+    tdt = dev["q"].dtype
+    esz = dev["q"].element_size()
+    MARGIN = 64 * 1024  # bytes, a multiple of 256 so the views keep their alignment
+    PATTERN = 0xA5
+
+    def fenced(nbytes):
+        buf = torch.full((MARGIN + nbytes + MARGIN,), PATTERN, dtype=torch.uint8, device="cuda")
+        return buf, buf[MARGIN:MARGIN + nbytes]
+
+    def view(inner, shape, dt):
+        return inner.view(dt).view(shape)
+
+    bufs = {}
+    shapes = {"o": ((n, hq, d), tdt, esz), "lse": ((hq, n), torch.float32, 4),
+              "dq": ((n, hq, d), tdt, esz), "dk": ((n, hkv, d), tdt, esz),
+              "dv": ((n, hkv, d), tdt, esz)}
+    outs = {}
+    for key, (shape, dt, es) in shapes.items():
+        buf, inner = fenced(int(np.prod(shape)) * es)
+        bufs[key] = buf
+        outs[key] = view(inner, shape, dt)
+    p = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype)
+    wsz = p.workspace_size()[1]
+    bufs["ws"], ws = fenced(wsz)
+    scale = 1.0 / np.sqrt(d)
+    ta.fwd(p, dev["q"], dev["k"], dev["v"], scale, o=outs["o"], lse=outs["lse"])
+    ta.bwd(p, dev["q"], dev["k"], dev["v"], outs["o"], outs["lse"], dev["do"], scale,
+           dq=outs["dq"], dk=outs["dk"], dv=outs["dv"], ws=ws)
+    torch.cuda.synchronize()
+    for key, buf in bufs.items():
+        head, tail = buf[:MARGIN], buf[-MARGIN:]
+        assert bool((head == PATTERN).all()) and bool((tail == PATTERN).all()), key
+    ref = oracle.tree_attention(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len, scale)
+    for key in ("o", "dq", "dk", "dv"):
+        got = outs[key].float().cpu().numpy().astype(np.float64)
+        assert rel_l2(got, ref[key]) <= REL_L2, key
+    p.close()

@@ -48,9 +48,10 @@ def asm(tmp_path_factory):
     if hipcc is None:
         pytest.skip("hipcc not available")
     out = str(tmp_path_factory.mktemp("asm") / "bwd.s")
-    cmd = [hipcc, "-O3", "-std=c++17", "-x", "hip", "--offload-arch=gfx950",
-           "--cuda-device-only", "-S", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+    # the library's own flags (prefix_shared_tree_attn_amd/build.py), so that
+    # the checked code is the code that ships
+    from prefix_shared_tree_attn_amd import build as libbuild
+    cmd = [hipcc, *libbuild.COMMON, "-x", "hip", *libbuild.DEVICE, "--cuda-device-only", "-S",
            os.path.join(CSRC, "bwd.hip"), "-o", out]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr

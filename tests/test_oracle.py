@@ -466,3 +466,59 @@ def test_workload_trees():
     for i in (1, 2, 4):
         t = config_tree(i)
         assert len(oracle.root_to_leaf_paths(t.parent, t.seg_start, t.seg_len)) == s[i]["leaves"]
+
+
+# ------------------------------------------------- key gradients by unique row
+
+@pytest.mark.parametrize("seed,nodes,roots,hq,hkv,d,shuffle,block", [
+    (21, 1, 1, 2, 1, 8, False, 1024), (22, 9, 1, 4, 2, 8, False, 3),
+    (23, 15, 2, 6, 2, 4, True, 5), (24, 20, 3, 3, 3, 16, True, 1024),
+    (25, 12, 1, 8, 1, 8, False, 2),
+])
+def test_key_rows_by_row_against_bruteforce(seed, nodes, roots, hq, hkv, d, shuffle, block):
+    """The per-row arrangement of the key gradients against the dense
+    closure-mask softmax differentiated by torch autograd, on every key of
+    every kv head, with row blocks shorter than the segments and nodes
+    packed in random order."""
+    rng = np.random.default_rng(seed)
+    t = random_tree(rng, nodes, max_len=14, n_roots=roots, shuffle=shuffle)
+    q, k, v, do = _rand_qkvdo(rng, t.num_tokens, hq, hkv, d)
+    scale = 1.0 / np.sqrt(d)
+    b = brute_force(t, q, k, v, do, scale)
+    keys = list(range(t.num_tokens))
+    for g in range(hkv):
+        dk, dv = oracle.key_rows_by_row(q, k, v, do, t.parent, t.seg_start, t.seg_len, scale,
+                                        keys, g, row_block=block)
+        assert _rel(dk, b["dk"][:, g]) < 1e-12
+        assert _rel(dv, b["dv"][:, g]) < 1e-12
+    # a subset of keys, repeated and out of order
+    sub = [t.num_tokens - 1, 0, t.num_tokens // 2, 0]
+    dk, dv = oracle.key_rows_by_row(q, k, v, do, t.parent, t.seg_start, t.seg_len, scale, sub,
+                                    hkv - 1, row_block=block)
+    np.testing.assert_allclose(dk, b["dk"][sub, hkv - 1], atol=1e-12)
+    np.testing.assert_allclose(dv, b["dv"][sub, hkv - 1], atol=1e-12)
+
+
+def test_key_rows_by_row_catches_planted_mistakes():
+    """Plausible mistakes must fail the brute-force pin: a wrong scale, the
+    per-copy dO / mult(t) carried into the per-row sums (each row is visited
+    once, so it must carry its whole dO), and a dropped parent edge."""
+    rng = np.random.default_rng(31)
+    t = random_tree(rng, 7, max_len=9)
+    q, k, v, do = _rand_qkvdo(rng, t.num_tokens, 2, 1, 8)
+    b = brute_force(t, q, k, v, do, 0.4)
+    keys = list(range(t.num_tokens))
+
+    def run(tt, dd, scale):
+        return oracle.key_rows_by_row(q, k, v, dd, tt.parent, tt.seg_start, tt.seg_len, scale,
+                                      keys, 0)[0]
+    assert _rel(run(t, do, 0.4), b["dk"][:, 0]) < 1e-12
+    assert _rel(run(t, do, 0.4 * 1.01), b["dk"][:, 0]) > 1e-4
+    mult = oracle.path_multiplicity(oracle.root_to_leaf_paths(t.parent, t.seg_start, t.seg_len),
+                                    t.num_tokens)
+    assert mult.max() > 1
+    assert _rel(run(t, do / mult[:, None, None], 0.4), b["dk"][:, 0]) > 1e-4
+    child = int(np.nonzero(t.parent >= 0)[0][0])
+    t2 = t.copy()
+    t2.parent[child] = -1
+    assert _rel(run(t2, do, 0.4), b["dk"][:, 0]) > 1e-4

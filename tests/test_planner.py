@@ -230,11 +230,74 @@ def test_host_plan_rejected_by_fwd():
     t = chain_tree([8])
     p = ta.plan_host(t.parent, t.seg_start, t.seg_len, 8, 1, 1, 64)
     lib = _ffi.lib()
-    st = lib.tree_attn_fwd(p.handle, None, None, None, ctypes.c_float(1.0), None, None, None, 0,
+    # well-formed arguments (addresses that are never dereferenced: the
+    # device check fails first) reach the device check
+    a = [ctypes.c_void_p(0x10000 + 0x1000 * i) for i in range(5)]
+    st = lib.tree_attn_fwd(p.handle, a[0], a[1], a[2], ctypes.c_float(1.0), a[3], a[4], None, 0,
                            None)
     assert _ffi.STATUS[st] == "NO_DEVICE_PLAN"
     st = lib.tree_attn_positions(p.handle, None, None, None)
     assert _ffi.STATUS[st] == "NO_DEVICE_PLAN"
+
+
+def _fake(n, misaligned=()):
+    """n distinct fake device addresses, 16-byte aligned except the listed
+    positions (8 bytes off).  Argument checks reject them before any device
+    work, so they are never dereferenced."""
+    return [ctypes.c_void_p(0x100000 + 0x1000 * i + (8 if i in misaligned else 0))
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("bad", range(5))
+def test_fwd_rejects_misaligned_tensors_before_any_launch(bad):
+    t = chain_tree([8])
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, 8, 1, 1, 64)
+    lib = _ffi.lib()
+    a = _fake(5, misaligned=(bad,))
+    st = lib.tree_attn_fwd(p.handle, a[0], a[1], a[2], ctypes.c_float(0.125), a[3], a[4], None,
+                           0, None)
+    assert _ffi.STATUS[st] == "INVALID_ARG"
+    assert b"16-byte" in lib.tree_attn_last_error()
+
+
+@pytest.mark.parametrize("bad", range(9))
+def test_bwd_rejects_misaligned_tensors_before_any_launch(bad):
+    t = chain_tree([8])
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, 8, 1, 1, 64)
+    lib = _ffi.lib()
+    a = _fake(9, misaligned=(bad,))  # q, k, v, o, lse, dout, dq, dk, dv
+    ws = ctypes.c_void_p(0x900000)
+    st = lib.tree_attn_bwd(p.handle, a[0], a[1], a[2], a[3], a[4], a[5], ctypes.c_float(0.125),
+                           a[6], a[7], a[8], ws, 1 << 20, None)
+    assert _ffi.STATUS[st] == "INVALID_ARG"
+    assert b"16-byte" in lib.tree_attn_last_error()
+    good = _fake(9)
+    st = lib.tree_attn_bwd(p.handle, good[0], good[1], good[2], good[3], good[4], good[5],
+                           ctypes.c_float(0.125), good[6], good[7], good[8], ws, 1 << 20, None)
+    assert _ffi.STATUS[st] == "NO_DEVICE_PLAN"
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan"), -0.0])
+def test_softmax_scale_must_be_positive(scale):
+    """Scores are masked with -inf and scaled afterwards, and the forward's
+    row max is taken on unscaled scores: a scale <= 0 or not finite is
+    rejected by the forward, the backward and the accumulating backward."""
+    t = chain_tree([8])
+    lib = _ffi.lib()
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, 8, 1, 1, 64)
+    a = _fake(9)
+    st = lib.tree_attn_fwd(p.handle, a[0], a[1], a[2], ctypes.c_float(scale), a[3], a[4], None,
+                           0, None)
+    assert _ffi.STATUS[st] == "INVALID_ARG"
+    ws = ctypes.c_void_p(0x900000)
+    st = lib.tree_attn_bwd(p.handle, a[0], a[1], a[2], a[3], a[4], a[5], ctypes.c_float(scale),
+                           a[6], a[7], a[8], ws, 1 << 20, None)
+    assert _ffi.STATUS[st] == "INVALID_ARG"
+    ps = ta.plan_host(t.parent, t.seg_start, t.seg_len, 8, 1, 1, 64, query_nodes=[0])
+    st = lib.tree_attn_bwd_accum(ps.handle, a[0], a[1], a[2], a[3], a[4], a[5],
+                                 ctypes.c_float(scale), a[6], a[7], a[8], ws, 1 << 20, None)
+    assert _ffi.STATUS[st] == "INVALID_ARG"
+    assert b"softmax_scale" in lib.tree_attn_last_error()
 
 
 def test_config_plans_build_quickly():
@@ -326,6 +389,11 @@ def test_subset_plan_calls_are_checked_on_the_host():
     p = ta.plan_host(t.parent, t.seg_start, t.seg_len, 8, 1, 1, 64, query_nodes=[0])
     st = lib.tree_attn_bwd_accum(p.handle, *([None] * 6), ctypes.c_float(1.0), None, None, None,
                                  None, 0, None)
+    assert _ffi.STATUS[st] == "INVALID_ARG"  # null tensors, before the device check
+    a = _fake(9)
+    st = lib.tree_attn_bwd_accum(p.handle, a[0], a[1], a[2], a[3], a[4], a[5],
+                                 ctypes.c_float(1.0), a[6], a[7], a[8], ctypes.c_void_p(0x900000),
+                                 1 << 20, None)
     assert _ffi.STATUS[st] == "NO_DEVICE_PLAN"
 
 
