@@ -179,6 +179,30 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
                                  const void* dout, float softmax_scale, void* dq, void* dk,
                                  void* dv, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * tree_attn_bwd_noalloc -- tree_attn_bwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and checks as
+ * tree_attn_bwd, without ws/ws_bytes: the backward scratch (row terms and
+ * split slots) comes from a fixed array of TREE_ATTN_STATIC_SCRATCH_BYTES
+ * inside the library, one per GPU, held until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * the plan's own device arrays were allocated by tree_attn_plan.
+ * A plan whose bwd_bytes (tree_attn_workspace_size) exceed
+ * TREE_ATTN_STATIC_SCRATCH_BYTES is rejected with WORKSPACE before any
+ * launch; a query-subset plan with INVALID_ARG.  Every call on one GPU
+ * shares that GPU's array and leaves its contents behind; nothing in it has
+ * to start at zero.  Calls that overlap on one GPU (other streams, other
+ * threads, other plans) race on it: the caller orders them, e.g. on one
+ * stream.  The first call on a device looks up that device's address of
+ * the array (hipGetSymbolAddress).
+ */
+#define TREE_ATTN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+tree_attn_status_t tree_attn_bwd_noalloc(tree_attn_plan_t plan, const void* q, const void* k,
+                                         const void* v, const void* o, const float* lse,
+                                         const void* dout, float softmax_scale, void* dq,
+                                         void* dk, void* dv, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Depth-first schedule.  AReaL-DTA (abstract) walks the prefix tree depth
  * first so that only one root-to-leaf path is resident at a time, while

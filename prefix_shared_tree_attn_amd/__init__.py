@@ -17,7 +17,7 @@ import numpy as np
 from . import _ffi
 from ._ffi import TreeAttnError, PlanStats  # noqa: F401
 
-__all__ = ["Plan", "plan", "plan_host", "fwd", "bwd", "bwd_accum", "accum_cast", "positions",
+__all__ = ["Plan", "plan", "plan_host", "fwd", "bwd", "bwd_noalloc", "bwd_accum", "accum_cast", "positions",
            "workspace",
            "TreeAttnError", "timing_enable", "timing_read", "PrefixTree", "build_tree",
            "gather_rows", "scatter_sum_rows", "rope", "lin_fwd", "lin_bwd", "lin_workspace"]
@@ -220,6 +220,30 @@ def bwd(p: Plan, q, k, v, o, lse, do, scale: float, dq=None, dk=None, dv=None, w
         p.handle, *args[:5], args[5], ctypes.c_float(scale), *outs,
         ctypes.c_void_p(ws.data_ptr()), ws.numel(),
         ctypes.c_void_p(_stream_handle(stream))), "bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(p: Plan, q, k, v, o, lse, do, scale: float, dq=None, dk=None, dv=None,
+                stream=None):
+    """tree_attn_bwd_noalloc: tree_attn_bwd with the library's fixed scratch
+    instead of a caller workspace; returns (dq, dk, dv).  Outputs that are
+    not passed in are allocated here, by torch, before the call."""
+    import torch
+    n, hq, hkv, d = p.num_tokens, p.hq, p.hkv, p.head_dim
+    if dq is None:
+        dq = torch.empty((n, hq, d), dtype=q.dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty((n, hkv, d), dtype=q.dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((n, hkv, d), dtype=q.dtype, device=q.device)
+    args = [_check_tensor(q, "q", (n, hq, d), p), _check_tensor(k, "k", (n, hkv, d), p),
+            _check_tensor(v, "v", (n, hkv, d), p), _check_tensor(o, "o", (n, hq, d), p),
+            _check_tensor(lse, "lse", (hq, n), p), _check_tensor(do, "do", (n, hq, d), p)]
+    outs = [_check_tensor(dq, "dq", (n, hq, d), p), _check_tensor(dk, "dk", (n, hkv, d), p),
+            _check_tensor(dv, "dv", (n, hkv, d), p)]
+    _ffi.check(_ffi.lib().tree_attn_bwd_noalloc(
+        p.handle, *args, ctypes.c_float(scale), *outs,
+        ctypes.c_void_p(_stream_handle(stream))), "bwd_noalloc")
     return dq, dk, dv
 
 

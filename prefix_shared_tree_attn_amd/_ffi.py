@@ -26,7 +26,7 @@ EXPORTS = (
     "tree_attn_scatter_sum_rows", "tree_attn_rope", "tree_attn_lin_workspace_size",
     "tree_attn_lin_fwd", "tree_attn_lin_bwd", "tree_attn_lin_plan_export",
     "tree_attn_plan_subset", "tree_attn_plan_host_subset", "tree_attn_bwd_accum",
-    "tree_attn_accum_cast",
+    "tree_attn_accum_cast", "tree_attn_bwd_noalloc",
 )
 
 
@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         ctypes.c_int, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(vp)]
     L.tree_attn_bwd_accum.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                       vp, ctypes.c_size_t, vp]
+    L.tree_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                                        vp]
     L.tree_attn_accum_cast.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int, vp]
     L.tree_attn_timing_enable.argtypes = [ctypes.c_int]
     L.tree_attn_timing_read.argtypes = [ctypes.POINTER(Timing), ctypes.c_int]
@@ -113,7 +115,8 @@ def lib() -> ctypes.CDLL:
                "tree_attn_build_tree", "tree_attn_gather_rows", "tree_attn_scatter_sum_rows",
                "tree_attn_rope", "tree_attn_lin_workspace_size", "tree_attn_lin_fwd",
                "tree_attn_lin_bwd", "tree_attn_lin_plan_export", "tree_attn_plan_subset",
-               "tree_attn_plan_host_subset", "tree_attn_bwd_accum", "tree_attn_accum_cast"):
+               "tree_attn_plan_host_subset", "tree_attn_bwd_accum", "tree_attn_accum_cast",
+               "tree_attn_bwd_noalloc"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L

@@ -22,7 +22,7 @@ ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 SOURCES = ["api.cpp", "planner.cpp", "prefix_tree.cpp", "fwd.hip", "bwd.hip", "positions.hip",
-           "prefix_ops.hip", "linear.hip"]
+           "prefix_ops.hip", "linear.hip", "scratch.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Device code: the packed fp32 instructions are disabled (the compiler would

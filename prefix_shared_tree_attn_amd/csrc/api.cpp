@@ -475,6 +475,34 @@ tree_attn_status_t tree_attn_bwd(tree_attn_plan_t plan, const void* q, const voi
                     false);
 }
 
+tree_attn_status_t tree_attn_bwd_noalloc(tree_attn_plan_t plan, const void* q, const void* k,
+                                         const void* v, const void* o, const float* lse,
+                                         const void* dout, float softmax_scale, void* dq,
+                                         void* dk, void* dv, hipStream_t stream) {
+  static_assert(tree_attn::kStaticScratchBytes == TREE_ATTN_STATIC_SCRATCH_BYTES,
+                "library scratch size and its documented value differ");
+  if (!plan) return report(Status::kInvalidArg, "null plan");
+  const HostPlan& hp = plan->hp;
+  if (hp.subset)
+    return report(Status::kInvalidArg,
+                  "a query-subset plan's backward is tree_attn_bwd_accum");
+  const size_t need = bwd_layout(hp).total;
+  if (need > tree_attn::kStaticScratchBytes)
+    return report(Status::kWorkspace,
+                  "backward scratch needs " + std::to_string(need) +
+                      " bytes, more than the library's fixed " +
+                      std::to_string(tree_attn::kStaticScratchBytes) +
+                      "; use tree_attn_bwd with a caller workspace");
+  if (hp.num_tokens == 0 || hp.query_rows == 0) return check_device(plan);
+  tree_attn_status_t st = check_device(plan);
+  if (st != TREE_ATTN_OK) return st;
+  void* ws = nullptr;
+  const hipError_t e = tree_attn::static_scratch(&ws);
+  if (e != hipSuccess) return report_hip(e, "hipGetSymbolAddress(library scratch)");
+  return bwd_common(plan, q, k, v, o, lse, dout, softmax_scale, dq, dk, dv, ws,
+                    tree_attn::kStaticScratchBytes, stream, false);
+}
+
 tree_attn_status_t tree_attn_bwd_accum(tree_attn_plan_t plan, const void* q, const void* k,
                                        const void* v, const void* o, const float* lse,
                                        const void* dout, float softmax_scale, void* dq,

@@ -110,4 +110,10 @@ hipError_t launch_scatter_sum(const void* src, void* dst, const int32_t* offsets
 hipError_t launch_rope(void* x, const int32_t* pos, int64_t n_tokens, int heads, int head_dim,
                        double log2_theta, int inverse, int dtype, hipStream_t stream);
 
+// Library-owned backward scratch (scratch.hip): kStaticScratchBytes of
+// device memory per GPU, 256-byte aligned.  *out receives the current
+// device's address of it (looked up once per device).
+constexpr size_t kStaticScratchBytes = static_cast<size_t>(64) << 20;
+hipError_t static_scratch(void** out);
+
 }  // namespace tree_attn
