@@ -13,11 +13,25 @@ REL_L2 = 1e-2
 LSE_ABS = 1e-3
 
 
-def rel_l2(x: np.ndarray, ref: np.ndarray) -> float:
+def rel_l2(x: np.ndarray, ref: np.ndarray, zero_scale: float = 0.0) -> float:
+    """||x - ref|| / ||ref||.  A reference that is exactly zero (a gradient
+    whose terms cancel, such as dK of a lone token, where P = 1 and
+    dP = D) has no size of its own: the error is then measured against
+    `zero_scale`, the size of the terms that cancel (see cancel_scale)."""
     x = np.asarray(x, np.float64)
     ref = np.asarray(ref, np.float64)
     den = np.linalg.norm(ref.ravel())
+    if den == 0.0:
+        den = zero_scale
     return float(np.linalg.norm((x - ref).ravel()) / max(den, 1e-300))
+
+
+def cancel_scale(other: np.ndarray, o: np.ndarray, do: np.ndarray, scale: float) -> float:
+    """scale * ||D|| * ||other|| with D = rowwise dO . O: the size of the two
+    terms P dP and P D whose difference dS forms dK (other = Q) and dQ
+    (other = K); they cancel exactly when a row attends to one key."""
+    d = np.einsum("thd,thd->th", np.asarray(do, np.float64), np.asarray(o, np.float64))
+    return float(scale * np.linalg.norm(d) * np.linalg.norm(np.asarray(other, np.float64)))
 
 
 def to_device(x, dtype: str):

@@ -15,7 +15,7 @@ import pytest
 import oracle
 from tree_inputs import (NodeTable, binary_tree, caterpillar_tree, chain_tree, config_spec,
                          config_tree, random_tree, star_tree, trunk_tree)
-from gpu_util import LSE_ABS, REL_L2, make, rel_l2, run_library
+from gpu_util import LSE_ABS, REL_L2, cancel_scale, make, rel_l2, run_library
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +27,9 @@ def _compare_full(t: NodeTable, hq, hkv, d, dtype, scale=None, do_std=1e-2, seed
           flush=True)
     got = run_library(t, x, hq, hkv, d, dtype, scale)
     ref = oracle.tree_attention(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len, scale)
-    errs = {k: rel_l2(got[k], ref[k]) for k in ("o", "dq", "dk", "dv")}
+    zero = {"dk": cancel_scale(x.q, ref["o"], x.do, scale),
+            "dq": cancel_scale(x.k, ref["o"], x.do, scale)}
+    errs = {k: rel_l2(got[k], ref[k], zero.get(k, 0.0)) for k in ("o", "dq", "dk", "dv")}
     errs["lse"] = float(np.abs(got["lse"] - ref["lse"]).max())
     print("errors:", errs, flush=True)
     for k in ("o", "dq", "dk", "dv"):
