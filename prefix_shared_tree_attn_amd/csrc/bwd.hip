@@ -33,7 +33,7 @@ namespace tree_attn {
 namespace {
 
 // Shared memory of the dK / dV kernel: QB query rows per step (two 32-row
-// sub-blocks for bf16; one for fp32 inputs, whose hi/lo planes double every
+// sub-blocks for bf16; one for fp32 inputs, whose two 16-bit planes double every
 // tile), Q / dO / (LSE, D) double-buffered.
 template <typename T, int D>
 struct DkdvCfg {
@@ -199,8 +199,10 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
           bf16x4 h, l;
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2) {
-            h[s2] = to_bf16(f[s2]);
-            l[s2] = to_bf16(f[s2] - static_cast<float>(h[s2]));
+            __bf16 hs, ls;
+            split_bits(f[s2], hs, ls);
+            h[s2] = hs;
+            l[s2] = ls;
           }
           LDS_PTR(char) hi = t ? do_tile(buf, 0) : q_tile(buf, 0);
           LDS_PTR(char) lo = t ? do_tile(buf, 1) : q_tile(buf, 1);
@@ -1014,8 +1016,10 @@ __global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
           bf16x4 hi, lo;
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2) {
-            hi[s2] = to_bf16(f[s2]);
-            lo[s2] = to_bf16(f[s2] - static_cast<float>(hi[s2]));
+            __bf16 hs, ls;
+            split_bits(f[s2], hs, ls);
+            hi[s2] = hs;
+            lo[s2] = ls;
           }
           const int off = KT::elem_off(r, cc * 4);
           *reinterpret_cast<LDS_PTR(bf16x4)>((tv ? v_tile(buf, 0) : k_tile(buf, 0)) + off) = hi;
@@ -1239,8 +1243,8 @@ static hipError_t pre_t(const BwdArgs& a, hipStream_t s) {
 template <typename T, int D>
 static hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
-  // bf16: the software-pipelined kernel; fp32: the kernel with split
-  // operands (the only instantiation of tree_attn_dkdv_kernel)
+  // bf16: the software-pipelined kernel; fp32: the kernel with fp32 MFMAs
+  // (the only instantiation of tree_attn_dkdv_kernel)
   void (*kern)(BwdArgs);
   int bytes;
   if constexpr (IsSplit<T>::value) {

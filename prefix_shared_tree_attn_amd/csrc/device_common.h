@@ -39,11 +39,29 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// An MFMA operand fragment.  For fp32 inputs a value x is carried as
-// hi = bf16(x) and lo = bf16(x - hi) and products use hi*hi + hi*lo + lo*hi,
-// the split-bf16 emulation of fp32 products (Henry, Tang, Heinecke,
-// "Leveraging the bfloat16 Artificial Intelligence Datatype For
-// Higher-Precision Computations", ARITH 2019): about 16 mantissa bits.
+__device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
+
+// fp32 values travel through the bf16 tile and fragment machinery as two
+// 16-bit planes: hi holds the upper and lo the lower 16 bits of each fp32
+// bit pattern (stored in bf16-typed slots; the split is exact, no rounding),
+// so LDS tiles, transposed reads and operand layouts are those of bf16.
+__device__ __forceinline__ void split_bits(float x, __bf16& hi, __bf16& lo) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  hi = __builtin_bit_cast(__bf16, static_cast<uint16_t>(u >> 16));
+  lo = __builtin_bit_cast(__bf16, static_cast<uint16_t>(u & 0xFFFFu));
+}
+__device__ __forceinline__ float join_bits(__bf16 hi, __bf16 lo) {
+  const uint32_t h = __builtin_bit_cast(uint16_t, hi), l = __builtin_bit_cast(uint16_t, lo);
+  return __builtin_bit_cast(float, (h << 16) | l);
+}
+
+// An MFMA operand fragment: this lane's 8 values of a 32 x 16 (A) or
+// 16 x 32 (B) operand.  bf16: one register quad, one 32x32x16 MFMA.  fp32
+// (SPLIT): the two 16-bit planes (split_bits); mma rebuilds the fp32 values
+// and issues eight v_mfma_f32_32x32x2_f32, the s-th taking this lane's
+// value s, so that lane halves 0 and 1 contribute reduction indices s and
+// 8 + s -- together the same 16 reduction indices as the bf16 MFMA, with
+// fp32 products and fp32 accumulation.
 template <bool SPLIT>
 struct Frag;
 template <>
@@ -57,24 +75,31 @@ struct Frag<true> {
 
 template <bool SPLIT>
 __device__ __forceinline__ void mma(f32x16& c, const Frag<SPLIT>& a, const Frag<SPLIT>& b) {
-  c = mfma32(a.h, b.h, c);
   if constexpr (SPLIT) {
-    c = mfma32(a.h, b.l, c);
-    c = mfma32(a.l, b.h, c);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(join_bits(a.h[s], a.l[s]),
+                                               join_bits(b.h[s], b.l[s]), c, 0, 0, 0);
+  } else {
+    c = mfma32(a.h, b.h, c);
   }
 }
 
-__device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
-
-// Packs eight fp32 values into an operand fragment (hi, and lo when split).
+// Packs eight fp32 values into an operand fragment (bf16 rounding, or the
+// exact 16-bit planes for fp32).
 template <bool SPLIT>
 __device__ __forceinline__ Frag<SPLIT> pack8(const float* x) {
   Frag<SPLIT> f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const __bf16 hi = to_bf16(x[s]);
-    f.h[s] = hi;
-    if constexpr (SPLIT) f.l[s] = to_bf16(x[s] - static_cast<float>(hi));
+    if constexpr (SPLIT) {
+      __bf16 hi, lo;
+      split_bits(x[s], hi, lo);
+      f.h[s] = hi;
+      f.l[s] = lo;
+    } else {
+      f.h[s] = to_bf16(x[s]);
+    }
   }
   return f;
 }
@@ -195,7 +220,7 @@ __device__ __forceinline__ Frag<true> load_frag8(const float* p) {
 
 // Copies rows [row0, row0 + ROWS) of a global tensor (D elements per row
 // starting at `base`, rows `row_stride` elements apart) into a bf16 LDS tile,
-// and for fp32 inputs also the low-order plane (x - bf16(x)).  Rows past
+// or for fp32 inputs into the two 16-bit planes of one (split_bits).  Rows past
 // `last_row` are clamped to it; callers mask their contributions.  All
 // global loads are issued before the LDS writes.
 template <typename T, int D, int ROWS, int NT>
@@ -226,8 +251,10 @@ __device__ __forceinline__ void load_tile(LDS_PTR(char) hi, LDS_PTR(char) lo, co
       bf16x4 h, l;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        h[s] = to_bf16(f[s]);
-        l[s] = to_bf16(f[s] - static_cast<float>(h[s]));
+        __bf16 hs, ls;
+        split_bits(f[s], hs, ls);
+        h[s] = hs;
+        l[s] = ls;
       }
       *reinterpret_cast<LDS_PTR(bf16x4)>(hi + Tile<D, ROWS>::elem_off(r, cc * 4)) = h;
       *reinterpret_cast<LDS_PTR(bf16x4)>(lo + Tile<D, ROWS>::elem_off(r, cc * 4)) = l;

@@ -25,7 +25,7 @@ struct FwdCfg {
   static constexpr bool SPLIT = IsSplit<T>::value;
   static constexpr int NP = SPLIT ? 2 : 1;
   // K / V buffers: two (the next key tile streams in while the current one
-  // is used) unless fp32 hi/lo planes at D = 128 would not fit.
+  // is used) unless fp32 tiles (two 16-bit planes) at D = 128 would not fit.
   static constexpr int NBUF = (SPLIT && D == 128) ? 1 : 2;
   static constexpr int PLANE = kFwdKeys * D * 2;
   static constexpr int BYTES = NBUF * 2 * NP * PLANE;
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   }
 
   // Key-tile prefetch: buffer loads straight to LDS for bf16, through
-  // registers (hi/lo split) for fp32.
+  // registers (split into 16-bit planes) for fp32.
   constexpr int SPLIT_PER = SPLIT ? kFwdKeys * D / 4 / 256 : 1;
   i32x4 kreg[SPLIT_PER], vreg[SPLIT_PER];
   TileLoader<D, kFwdKeys, 4> tl;
@@ -124,8 +124,10 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
           bf16x4 hi, lo;
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2) {
-            hi[s2] = to_bf16(f[s2]);
-            lo[s2] = to_bf16(f[s2] - static_cast<float>(hi[s2]));
+            __bf16 hs, ls;
+            split_bits(f[s2], hs, ls);
+            hi[s2] = hs;
+            lo[s2] = ls;
           }
           const int off = KT::elem_off(r, cc * 4);
           *reinterpret_cast<LDS_PTR(bf16x4)>((tv ? v_tile(buf, 0) : k_tile(buf, 0)) + off) = hi;
