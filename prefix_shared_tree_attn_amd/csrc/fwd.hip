@@ -224,48 +224,61 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
           sacc[kb][v] = kl < klim ? sacc[kb][v] : -INFINITY;
         }
     }
-    // Online softmax in base 2.  The row max is taken on raw scores (the
-    // scale is positive) and the running reference m is moved only when the
-    // max grows by more than 8: p = 2^(c s - m) then stays below 2^8, and O
-    // and l always share the same m, so the result is exact either way.
-    // The max and the sum run as four independent chains each (a single
-    // chain would make every step wait out 16 or 32 dependent ALU latencies)
-    // and the two lane halves meet through a lane swap, not through LDS.
-    float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // Online softmax in base 2 against a running reference m: p = 2^(c s - m),
+    // with O and l always sharing the same m, so the result is exact
+    // whichever m is used.  The common step does not look at the block's
+    // maximum at all: it forms p with the current m and keeps it unless some
+    // lane's partial sum of this block reaches 2^64 (or is not a number: the
+    // first block, where m = -inf).  Only then is the row max taken (on raw
+    // scores, the scale being positive; four chains, the lane halves joined
+    // by a lane swap), m moved to it if it grew by more than 8, O and l
+    // rescaled, and p formed again.  p < 2^64 keeps P, O and l far inside the
+    // fp32 and bf16 range.
+    float pr[2][16], blk[4];
+    auto soft = [&](float neg_m) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 4; ++i) blk[i] = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx4[v & 3] = fmaxf(mx4[v & 3], sacc[kb][v]);
-    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-    mx = max_across_halves(mx) * a.scale_log2;
-    if (__any(mx > m + 8.f)) {
-      const float m_new = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      m = m_new;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lsum[i] *= alpha;
+        for (int v = 0; v < 16; ++v) {
+          pr[kb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], a.scale_log2, neg_m));
+          blk[v & 3] += pr[kb][v];
+        }
+    };
+    soft(-m);
+    constexpr float kBig = 18446744073709551616.f;  // 2^64
+    const bool ok = (blk[0] < kBig) && (blk[1] < kBig) && (blk[2] < kBig) && (blk[3] < kBig);
+    if (__any(!ok)) {
+      float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-    }
-    const float neg_m = -m;
+        for (int v = 0; v < 16; ++v) mx4[v & 3] = fmaxf(mx4[v & 3], sacc[kb][v]);
+      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+      mx = max_across_halves(mx) * a.scale_log2;
+      if (__any(mx > m + 8.f)) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+        for (int i = 0; i < 4; ++i) lsum[i] *= alpha;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], a.scale_log2, neg_m));
-        sacc[kb][v] = p;
-        lsum[v & 3] += p;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
       }
+      soft(-m);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lsum[i] += blk[i];
 
     // O^T += V^T P^T over four 16-key chunks
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float pv[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) pv[s] = sacc[c >> 1][8 * (c & 1) + s];
+      for (int s = 0; s < 8; ++s) pv[s] = pr[c >> 1][8 * (c & 1) + s];
       const Frag<SPLIT> pf = pack8<SPLIT>(pv);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {

@@ -114,6 +114,48 @@ def test_random_tree_sweep_wide(seed):
     _compare_full(t, hq, hkv, d, dtype, do_std=1.0 if dtype == "fp32" else 1e-2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_scores_growing_past_the_rescale_bound(dtype):
+    """Keys scaled by 1, 12 and 25 in the first three 64-key blocks: the best
+    base-2 score of a row grows by more than 64 from block 0 to block 1 and
+    passes 128 in block 2 (2^128 overflows fp32), so those forward key
+    blocks take the path that finds the row max and rescales O and l."""
+    t = chain_tree([640])
+    hq, hkv, d = 2, 1, 128
+    scale = 1.0 / np.sqrt(d)
+    x = make(t, hq, hkv, d, dtype)
+    f = np.minimum(1.0 + 12.0 * (np.arange(t.num_tokens) // 64), 25.0).astype(np.float32)
+    k = x.k * f[:, None, None]
+    if dtype == "bf16":
+        from tree_inputs.tensors import bf16_bits_to_f32, bf16_round_bits
+        bits = bf16_round_bits(k)
+        k = bf16_bits_to_f32(bits)
+        x.bits["k"] = bits
+    x.k[...] = k
+    # the largest base-2 score per 64-key block, to show the jumps are there
+    s = np.einsum("thd,jd->thj", x.q[:, :, :].astype(np.float64), x.k[:, 0, :].astype(np.float64))
+    blocks = [float(np.abs(s[:, :, b:b + 64]).max()) * scale / np.log(2.0) for b in (0, 64, 128)]
+    assert blocks[1] - blocks[0] > 64 and blocks[2] > 128, blocks
+    print("largest base-2 score of blocks 0, 1, 2:", blocks, flush=True)
+    got = run_library(t, x, hq, hkv, d, dtype, scale)
+    ref = oracle.tree_attention(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len, scale)
+    # The backward recomputes P = 2^(c s - LSE log2 e), a difference of two
+    # numbers as large as the largest base-2 score M; fp32 rounds it to about
+    # M 2^-24, so fp32 results carry relative errors of that order here (the
+    # bf16 bar is far above it).
+    big = float(np.abs(s).max()) * scale / np.log(2.0)
+    rel_bar, lse_bar = ((max(FP32_REL_L2, 4.0 * big * 2.0 ** -24), FP32_LSE_ABS)
+                        if dtype == "fp32" else (REL_L2, LSE_ABS))
+    errs = {k_: rel_l2(got[k_], ref[k_]) for k_ in ("o", "dq", "dk", "dv")}
+    # LSE reaches about 125 here, where fp32 values lie 7.6e-6 apart: its
+    # error is taken relative to max(1, |LSE|)
+    errs["lse"] = float(np.abs(got["lse"] - ref["lse"]).max() / max(1.0, np.abs(ref["lse"]).max()))
+    print("errors:", errs, flush=True)
+    for k_ in ("o", "dq", "dk", "dv"):
+        assert errs[k_] <= rel_bar, (k_, errs)
+    assert errs["lse"] <= lse_bar, errs
+
+
 def test_split_case_really_splits():
     import prefix_shared_tree_attn_amd as ta
     t, hq, hkv, d, dtype = CASES["heavy-prompt-split"]
