@@ -483,24 +483,21 @@ struct PdsPack {
 // gives every MFMA result to the accumulation registers, and each element
 // would then need a v_accvgpr_read -- one more instruction for a wave that
 // can issue only one every four cycles.  The compiler does not see these
-// statements as MFMAs and inserts no hazard wait states after them, so the
-// last MFMA of each chain carries its own: sixteen wait states, more than an
-// 8-pass XDL result needs before a VALU op may read or overwrite it (CDNA3 /
-// CDNA4 ISA, dependency rules).  Within a chain the accumulator is read back
-// as source C in the same registers, which needs none.  Their A operands
-// come from LDS loads and their B operands from registers loaded before the
-// loop, never from a VALU op just before; a CPU test checks the compiled
-// code for both conditions.
+// statements as MFMAs and inserts no hazard wait states around them, so the
+// kernel's order keeps them apart from every other access of their
+// registers: the first read of S or dP comes two MFMA slots into the next
+// iteration, well over the sixteen wait states an 8-pass XDL result needs
+// before a VALU op may read or overwrite it (CDNA3 / CDNA4 ISA, dependency
+// rules).  Within a chain the accumulator is read back as source C in the
+// same registers, which needs none.  Their A operands come from LDS loads
+// and their B operands from registers loaded before the loop, never from a
+// VALU op just before; a CPU test checks the compiled code for all of these
+// distances on every path.
 __device__ __forceinline__ void mfma_v_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_v_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v_last(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7"
-               : "+v"(d)
-               : "v"(a), "v"(b));
 }
 
 // The LDS-DMA loads of one query step of the pipelined kernel in one
@@ -578,7 +575,14 @@ __device__ __forceinline__ void wait_lgkm(int n) {
     case 5: wait_lgkm_c<5>(); break;
     case 6: wait_lgkm_c<6>(); break;
     case 7: wait_lgkm_c<7>(); break;
-    default: wait_lgkm_c<8>(); break;
+    case 8: wait_lgkm_c<8>(); break;
+    case 9: wait_lgkm_c<9>(); break;
+    case 10: wait_lgkm_c<10>(); break;
+    case 11: wait_lgkm_c<11>(); break;
+    case 12: wait_lgkm_c<12>(); break;
+    case 13: wait_lgkm_c<13>(); break;
+    case 14: wait_lgkm_c<14>(); break;
+    default: wait_lgkm_c<15>(); break;
   }
 }
 
@@ -700,14 +704,31 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   // NC + 2 kc + 1 for dP).
   constexpr int NC = 4 * DB, NS = NC + 2 * KC;
   constexpr int LA = 4;  // operands are read this many slots ahead
-  // LDS reads issued after operand i + 1 once slot i has issued its own read
-  // ahead (a transposed operand takes two reads).  Even slots wait for their
-  // operand and the next one together: one s_waitcnt per two MFMAs, each an
-  // issue slot of the only wave on the SIMD.
-  auto younger = [&](int i) constexpr {
-    int n = 0;
-    for (int j = i + 2; j <= i + LA && j < NS; ++j) n += j < NC ? 2 : 1;
+  constexpr int NRT = 8;  // row-term reads of a step (-LSE log2 e and -D, 4 x 16 bytes each)
+  // LDS reads of an iteration, in issue order: its first LA operands (read
+  // during the previous iteration), the row terms of its step, then the
+  // operand LA slots ahead in every slot; the last LA slots read the next
+  // iteration's first operands instead.  A transposed (dK / dV) operand
+  // takes two reads.
+  auto slot_reads = [&](int t) constexpr {
+    const int k = t + LA;  // operand read in slot t
+    return k < NC || k >= NS ? 2 : 1;
+  };
+  // reads up to and including operand k
+  auto through_op = [&](int k) constexpr {
+    if (k < LA) return 2 * (k + 1);
+    int n = 2 * LA + NRT;
+    for (int t = 0; t + LA <= k; ++t) n += slot_reads(t);
     return n;
+  };
+  // reads issued after operand i + 1 once slot i has issued its own.  Even
+  // slots wait for their operand and the next one together: one s_waitcnt
+  // per two MFMAs, each an issue slot of the only wave on the SIMD.  (The
+  // compiler adds a wait of its own before any use these do not cover.)
+  auto younger = [&](int i) constexpr {
+    int n = 2 * LA + NRT;
+    for (int t = 0; t <= i; ++t) n += slot_reads(t);
+    return n - through_op(i + 1);
   };
   auto fetch = [&](int i, LDS_PTR(char) bprev, LDS_PTR(char) bnext)
                    __attribute__((always_inline)) -> bf16x8 {
@@ -742,10 +763,13 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
       f32x16& acc = ((i - NC) & 1) ? pacc : sacc;
       const bf16x8& b = ((i - NC) & 1) ? vf[kc] : kf[kc];
       if (kc == 0) mfma_v_first(acc, op, b);
-      else if (kc == KC - 1) mfma_v_last(acc, op, b);
       else mfma_v_acc(acc, op, b);
     }
   };
+
+  // The first LA operands of an iteration, read during the previous one so
+  // that its first MFMAs need not wait out an LDS round trip.
+  bf16x8 carry[LA];
 
   // One pipelined iteration j: C(j-1) then A(j+1) on the matrix cores, B(j)
   // on the vector ALUs beside them.  During the C slots each element's S and
@@ -753,12 +777,17 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   // slots may overwrite them; during the A slots P = 2^x, dS = P y and the
   // bf16 packs are formed, after the last C slot has read the old packs.
   // The fences keep this order.  Under the causal mask (rare steps) x is set
-  // to -inf where key > row between the halves.
-  auto iteration = [&](int bp, int bc, int bn, bool masked, int delta,
-                       int rmask) __attribute__((always_inline)) {
+  // to -inf where key > row between the halves.  work(i) is scalar work
+  // (loads, step bookkeeping) placed in C slot i, where the matrix core is
+  // busy with that slot's MFMA.
+  auto iteration = [&](int bp, int bc, int bn, bool masked, int delta, int rmask,
+                       auto&& work) __attribute__((always_inline)) {
     LDS_PTR(char) bprev = lds + bp;
     LDS_PTR(char) bcur = lds + bc;
     LDS_PTR(char) bnext = lds + bn;
+    bf16x8 op[NS];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) op[i] = carry[i];
     f32x4 nl[4], nd[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -766,11 +795,11 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
       nl[i] = *reinterpret_cast<const LDS_PTR(f32x4)>(bcur + C::NL_OFF + off);
       nd[i] = *reinterpret_cast<const LDS_PTR(f32x4)>(bcur + C::ND_OFF + off);
     }
-    bf16x8 op[NS];
-#pragma unroll
-    for (int i = 0; i < LA; ++i) op[i] = fetch(i, bprev, bnext);
     float x[16], y[16];
-    constexpr int EC = 16 / NC;       // elements per C slot
+    // C slots 0 and 1 leave S and dP alone (the MFMAs that wrote them may
+    // still run, and the row terms are still on their way); slots 2 .. NC - 1
+    // take the 16 elements between them
+    auto c_first = [&](int i) constexpr { return i < 2 ? 0 : ((i - 2) * 16) / (NC - 2); };
     constexpr int EA = 16 / (NS - NC);  // elements per A slot
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
@@ -779,12 +808,13 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
       if ((i & 1) == 0) wait_lgkm(younger(i));
       mfma_slot(i, op[i]);
 #pragma unroll
-      for (int e = EC * i; e < EC * (i + 1); ++e) {
+      for (int e = c_first(i); e < c_first(i + 1); ++e) {
         x[e] = __builtin_fmaf(sacc[e], a.scale_log2, nl[e >> 2][e & 3]);
         y[e] = pacc[e] + nd[e >> 2][e & 3];
         keep(x[e]);
         keep(y[e]);
       }
+      work(i);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (masked) {
@@ -797,7 +827,12 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
 #pragma unroll
     for (int i = NC; i < NS; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      if (i + LA < NS) op[i + LA] = fetch(i + LA, bprev, bnext);
+      if (i + LA < NS) {
+        op[i + LA] = fetch(i + LA, bprev, bnext);
+      } else {
+        // the next iteration's first operands (its C slots read step j's tiles)
+        carry[i + LA - NS] = fetch(i + LA - NS, bcur, bcur);
+      }
       if (((i - NC) & 1) == 0) wait_lgkm(younger(i));
       mfma_slot(i, op[i]);
 #pragma unroll
@@ -845,27 +880,22 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
     LDS_PTR(char) b0 = lds + bc;
 #pragma unroll
     for (int i = NC; i < NS; ++i) mfma_slot(i, fetch(i, b0, b0));
+#pragma unroll
+    for (int i = 0; i < LA; ++i) carry[i] = fetch(i, lds + bp, lds + bp);
   }
 
   int bw = 3 * BUF;  // buffer of step j + 3
+  // Even iterations j: steps j + 1 and j + 2 (loaded during iteration j - 2)
+  // must be in for every wave, and every wave past iteration j - 1; then
+  // steps j + 3 and j + 4 go to the buffers of steps j - 3 and j - 2.
+  // Iterations j and j + 1 read only the buffers of steps j - 1 .. j + 2.
+  // This runs in the first C slots of the iteration, beside their MFMAs.
+  // The barrier needs no memory fence: every LDS read of iteration j - 1
+  // was waited for before the MFMA that used it, and the tiles arrive by
+  // LDS DMA, whose completion the vmcnt wait covers.
   bool even = true;
   while (true) {
     const bool more = nx.e < ee;
-    // Even iterations: steps j + 1 and j + 2 (loaded during iteration j - 2)
-    // must be in for every wave, and every wave past iteration j - 1; then
-    // steps j + 3 and j + 4 go to the buffers of steps j - 3 and j - 2.
-    // Iterations j and j + 1 read only the buffers of steps j - 1 .. j + 2.
-    if (even) {
-      wait_vmcnt<0>();
-      __syncthreads();
-      issue(ld, bw);
-      bw = nexto(bw);
-      ld_next();
-      issue(ld, bw);
-      bw = nexto(bw);
-      ld_next();
-    }
-    even = !even;
     // A causal entry (w = 1) masks key > row, i.e. l32 - r > r0 - wk0; a
     // key limit (w = -(limit + 1)) masks key >= limit on every row, i.e.
     // l32 > limit - 1 - wk0.
@@ -877,15 +907,35 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
       masked = lim ? delta < 31 : (cur.causal != 0 && delta < 32);
       rmask = lim ? 0 : -1;
     }
-    cur = nx;
-    step_next(nx, ee, a.entries);
-    iteration(bp, bc, bn, masked, delta, rmask);
+    iteration(bp, bc, bn, masked, delta, rmask, [&](int i) __attribute__((always_inline)) {
+      if (even) {
+        if (i == 1) {
+          wait_vmcnt<0>();
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+        } else if (i == 2 || i == 4) {
+          issue(ld, bw);
+          bw = nexto(bw);
+        } else if (i == 3 || i == 5) {
+          ld_next();
+        }
+      }
+      if (i == 7) {
+        cur = nx;
+        step_next(nx, ee, a.entries);
+      }
+    });
+    even = !even;
     bp = bc;
     bc = bn;
     bn = nexto(bn);
     if (!more) break;
   }
   wait_vmcnt<0>();  // no load may land in LDS after the workgroup has left
+  // the last S / dP MFMAs may still be writing registers that the code
+  // below reuses: sixteen wait states
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
   // C of the last step (its buffer is bp now)
   {
     LDS_PTR(char) bl = lds + bp;
