@@ -383,12 +383,11 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_kernel(BwdArgs a) {
 // ALUs run B(j), so the element-wise work of a wave hides under its own
 // MFMAs.  Q, dO and the row terms go from memory straight into a ring of
 // six LDS buffers (inline-asm LDS DMA, which the compiler's wait analysis
-// does not see; the kernel counts its own loads): every other iteration j
-// waits for steps j + 1 and j + 2, passes a barrier and issues the loads of
-// steps j + 3 and j + 4, so each step has two iterations to arrive.
-// Iterations j and j + 1 read the buffers of steps j - 1 .. j + 2; the
-// barrier makes sure no wave still reads the buffers of steps j - 3 and
-// j - 2 that the new loads overwrite.  The S and dP MFMAs are inline
+// does not see; the kernel counts its own loads): iteration j waits for step
+// j + 1, passes a barrier and issues the loads of step j + 3, so each step
+// has two iterations to arrive.  Iteration j reads the buffers of steps
+// j - 1 .. j + 1; the barrier makes sure no wave still reads the buffer of
+// step j - 3 that the new loads overwrite.  The S and dP MFMAs are inline
 // asm as well, to keep their results out of the accumulation registers.
 //
 // No branch masks anything inside the loop:
@@ -885,15 +884,14 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
   }
 
   int bw = 3 * BUF;  // buffer of step j + 3
-  // Even iterations j: steps j + 1 and j + 2 (loaded during iteration j - 2)
-  // must be in for every wave, and every wave past iteration j - 1; then
-  // steps j + 3 and j + 4 go to the buffers of steps j - 3 and j - 2.
-  // Iterations j and j + 1 read only the buffers of steps j - 1 .. j + 2.
-  // This runs in the first C slots of the iteration, beside their MFMAs.
-  // The barrier needs no memory fence: every LDS read of iteration j - 1
-  // was waited for before the MFMA that used it, and the tiles arrive by
-  // LDS DMA, whose completion the vmcnt wait covers.
-  bool even = true;
+  // Iteration j: step j + 1 (loaded during iteration j - 2) must be in for
+  // every wave, and every wave past iteration j - 1; then step j + 3 goes to
+  // the buffer of step j - 3, leaving the load of step j + 2 in flight.
+  // Iteration j reads only the buffers of steps j - 1 .. j + 1.  This runs
+  // in the first C slots of the iteration, beside their MFMAs, the same in
+  // every iteration (no branch).  The barrier needs no memory fence: every
+  // LDS read of iteration j - 1 was waited for before the MFMA that used it,
+  // and the tiles arrive by LDS DMA, whose completion the vmcnt wait covers.
   while (true) {
     const bool more = nx.e < ee;
     // A causal entry (w = 1) masks key > row, i.e. l32 - r > r0 - wk0; a
@@ -908,25 +906,22 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
       rmask = lim ? 0 : -1;
     }
     iteration(bp, bc, bn, masked, delta, rmask, [&](int i) __attribute__((always_inline)) {
-      if (even) {
-        if (i == 1) {
-          wait_vmcnt<0>();
-          asm volatile("" ::: "memory");
-          __builtin_amdgcn_s_barrier();
-          asm volatile("" ::: "memory");
-        } else if (i == 2 || i == 4) {
-          issue(ld, bw);
-          bw = nexto(bw);
-        } else if (i == 3 || i == 5) {
-          ld_next();
-        }
+      if (i == 1) {
+        wait_vmcnt<LPS>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      } else if (i == 2) {
+        issue(ld, bw);
+        bw = nexto(bw);
+      } else if (i == 3) {
+        ld_next();
       }
       if (i == 7) {
         cur = nx;
         step_next(nx, ee, a.entries);
       }
     });
-    even = !even;
     bp = bc;
     bc = bn;
     bn = nexto(bn);
