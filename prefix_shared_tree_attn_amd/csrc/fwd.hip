@@ -196,6 +196,12 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
       Frag<SPLIT> kop[NSL];
 #pragma unroll
       for (int i = 0; i < KLA; ++i) kop[i] = kfetch(i);
+      // The two waves of a SIMD come from different workgroups and drift in
+      // and out of step.  A wave raises its issue priority over its MFMA
+      // runs (here and over O += V^T P^T) and drops it for the element-wise
+      // softmax, so that the other wave's MFMAs go first while this one does
+      // vector work: the matrix core idles less when both want it at once.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < NSL; ++i) {
         __builtin_amdgcn_sched_barrier(0);
@@ -208,6 +214,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
         mma<SPLIT>(sacc[kb], kop[i], qf[i % KC]);
       }
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
     }
 
     // Mask only on tiles that reach past the range or cross the diagonal of
@@ -274,6 +281,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
     for (int i = 0; i < 4; ++i) lsum[i] += blk[i];
 
     // O^T += V^T P^T over four 16-key chunks
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float pv[8];
@@ -288,6 +296,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
         mma<SPLIT>(oacc[db], vf, pf);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     }  // !skip
 
     if (!has_next) break;
