@@ -977,7 +977,7 @@ struct DqCfg {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void tree_attn_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void tree_attn_dq_kernel(BwdArgs a) {
   using C = DqCfg<T, D>;
   constexpr bool SPLIT = C::SPLIT;
   constexpr int NP = C::NP, NBUF = C::NBUF;
