@@ -391,20 +391,24 @@ def main_dfs(args) -> int:
     torch.cuda.synchronize()
     plan_ms = 1e3 * (time.perf_counter() - t0)
     ws = torch.empty(max(p.workspace_size()[1] for p in plans), dtype=torch.uint8, device=dev)
+    # split query tiles keep their key parts' partial results here
+    ws_f = torch.empty(max(1, max(p.workspace_size()[0] for p in plans)), dtype=torch.uint8,
+                       device=dev)
     whole = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype)
     ws_whole = ta.workspace(whole, "bwd")
+    ws_whole_f = ta.workspace(whole, "fwd")
 
     def walk():
         acc.zero_()
         for p in plans:
-            ta.fwd(p, q, k, v, scale, o=o, lse=lse)
+            ta.fwd(p, q, k, v, scale, o=o, lse=lse, ws=ws_f)
         for p in reversed(plans):
             ta.bwd_accum(p, q, k, v, o, lse, do, scale, acc[0], acc[1], dq=dq, ws=ws)
         ta.accum_cast(acc[0], dtype, out=dk)
         ta.accum_cast(acc[1], dtype, out=dv)
 
     def one_call():
-        ta.fwd(whole, q, k, v, scale, o=o, lse=lse)
+        ta.fwd(whole, q, k, v, scale, o=o, lse=lse, ws=ws_whole_f)
         ta.bwd(whole, q, k, v, o, lse, do, scale, dq=dq, dk=dk, dv=dv, ws=ws_whole)
 
     def timed(fn, steps):
@@ -605,6 +609,7 @@ def main() -> int:
     dv = torch.empty_like(v)
     probe = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype)
     ws = ta.workspace(probe, "bwd")
+    ws_f = ta.workspace(probe, "fwd")  # key parts of split query tiles (small trees)
     pstats = probe.stats()
     # the dK/dV kernel variant with key-limit masks runs when the plan has them
     has_limit = bool((probe.export()["bwd_entries"][:, 3] < 0).any())
@@ -621,7 +626,7 @@ def main() -> int:
     def step():
         p = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype)
         ta.positions(p, node_id=node_id, pos_id=pos_id)
-        ta.fwd(p, q, k, v, scale, o=o, lse=lse)
+        ta.fwd(p, q, k, v, scale, o=o, lse=lse, ws=ws_f)
         ta.bwd(p, q, k, v, o, lse, do, scale, dq=dq, dk=dk, dv=dv, ws=ws)
         plans.append(p)
 

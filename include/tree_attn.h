@@ -137,8 +137,13 @@ void tree_attn_plan_destroy(tree_attn_plan_t plan);
  * The backward workspace holds two fp32 row-term arrays [Hq, N] (-D_t with
  * D_t = dO_t . O_t, and -LSE_t * log2 e), each padded to 256 bytes, and fp32
  * partial dK/dV slots of key tiles whose descendant work was split
- * for load balance.  The forward pass needs none (fwd_bytes = 0).  Either
- * pointer may be null.
+ * for load balance, and fp32 partial dQ of the key parts below.  A plan
+ * whose (query tile, head) workgroups would not fill the GPU twice over
+ * (small trees, one-node calls of a depth-first walk) splits the keys of
+ * its query tiles into parts (tree_attn_plan_export_split); the forward
+ * workspace then holds their fp32 partial outputs (unnormalised O, the
+ * running maximum and the row sum per row and head), and fwd_bytes is 0
+ * for a plan without such parts.  Either pointer may be null.
  */
 tree_attn_status_t tree_attn_workspace_size(tree_attn_plan_t plan, size_t* fwd_bytes,
                                             size_t* bwd_bytes);
@@ -149,7 +154,9 @@ tree_attn_status_t tree_attn_workspace_size(tree_attn_plan_t plan, size_t* fwd_b
  *   O_{t,h} = sum_j softmax(s)_j v_{j,h/G},   LSE_{h,t} = log sum_j exp(s_j).
  * q, k, v: device inputs in the plan's dtype; o: device output [N,Hq,D]
  * (same dtype, overwritten); lse: device output [Hq,N] fp32 (overwritten).
- * ws/ws_bytes: device workspace of at least fwd_bytes (may be null when 0).
+ * ws/ws_bytes: device workspace of at least fwd_bytes, 256-byte aligned
+ * (may be null when fwd_bytes is 0), else WORKSPACE; a plan with split
+ * query tiles merges their key parts in a second launch on the same stream.
  * The softmax scale is typically 1/sqrt(D); it must be finite and > 0
  * (masked scores are -inf before scaling), else INVALID_ARG.  Every tensor
  * pointer (q, k, v, o, lse) must be 16-byte aligned (rows move in 16-byte
@@ -406,6 +413,8 @@ typedef struct {
   int64_t lin_chunk;        /* linear attention: chunk (trajectory depth)   */
   int64_t subset;           /* 1 for a query-subset plan, else 0            */
   int64_t query_rows;       /* tokens that are queries (N for whole trees)  */
+  int64_t fwd_split_tiles;  /* query tiles whose keys were split into parts */
+  int64_t fwd_slots;        /* key parts of those tiles (forward / dQ slots) */
 } tree_attn_plan_stats_t;
 
 tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_stats_t* out);
@@ -435,6 +444,21 @@ tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_st
 tree_attn_status_t tree_attn_plan_export(tree_attn_plan_t plan, int32_t* fwd_tiles,
                                          int32_t* fwd_ranges, int32_t* bwd_items,
                                          int32_t* bwd_entries);
+
+/*
+ * tree_attn_plan_export_split -- the key parts of split forward tiles (for
+ * tests and debugging); pass null to skip one:
+ *   fwd_part    [fwd_tiles]          : slot of the tile's key part, or -1 for
+ *                                      a tile that holds all of its rows'
+ *                                      keys and writes O / LSE and dQ itself
+ *   fwd_combine [fwd_split_tiles, 4] : q0, q1, slot_begin, num_slots of every
+ *                                      split query tile; its parts are the
+ *                                      tiles with those rows and slots, and
+ *                                      together they hold every key of the
+ *                                      rows exactly once
+ */
+tree_attn_status_t tree_attn_plan_export_split(tree_attn_plan_t plan, int32_t* fwd_part,
+                                               int32_t* fwd_combine);
 
 /*
  * Chunkwise causal linear attention over the same tree (HARTS, abstract:

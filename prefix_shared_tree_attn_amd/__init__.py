@@ -101,6 +101,10 @@ class Plan:
         _ffi.check(_ffi.lib().tree_attn_plan_export(
             self.handle, _ptr(out["fwd_tiles"]), _ptr(out["fwd_ranges"]),
             _ptr(out["bwd_items"]), _ptr(out["bwd_entries"])), "plan_export")
+        out["fwd_part"] = np.zeros((st["fwd_tiles"],), np.int32)
+        out["fwd_combine"] = np.zeros((st["fwd_split_tiles"], 4), np.int32)
+        _ffi.check(_ffi.lib().tree_attn_plan_export_split(
+            self.handle, _ptr(out["fwd_part"]), _ptr(out["fwd_combine"])), "plan_export_split")
         return out
 
 
@@ -192,6 +196,8 @@ def fwd(p: Plan, q, k, v, scale: float, o=None, lse=None, ws=None, stream=None):
             _check_tensor(v, "v", (n, hkv, d), p)]
     po = _check_tensor(o, "o", (n, hq, d), p)
     pl = _check_tensor(lse, "lse", (hq, n), p)
+    if ws is None and p.workspace_size()[0] > 0:
+        ws = workspace(p, "fwd")
     wptr, wbytes = (ctypes.c_void_p(ws.data_ptr()), ws.numel()) if ws is not None else (None, 0)
     _ffi.check(_ffi.lib().tree_attn_fwd(p.handle, *args, ctypes.c_float(scale), po, pl, wptr,
                                         wbytes, ctypes.c_void_p(_stream_handle(stream))), "fwd")

@@ -28,6 +28,9 @@ struct tree_attn_plan_s {
   char* dev_buf = nullptr;
   const I4* d_fwd_tiles = nullptr;
   const I4* d_fwd_ranges = nullptr;
+  const int32_t* d_fwd_part = nullptr;
+  const I4* d_fwd_combine = nullptr;
+  const I4* d_fwd_qtiles = nullptr;
   const I8* d_bwd_items = nullptr;
   const I4* d_bwd_entries = nullptr;
   const I8* d_bwd_reduce = nullptr;
@@ -66,8 +69,27 @@ bool aligned16(std::initializer_list<const void*> ptrs) {
 // positive finite number.
 bool valid_softmax_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
+// Key parts of split forward tiles: fp32 [slots, Hq, kFwdRows, D] partial O
+// (forward) or partial dQ (backward), and [slots, Hq, kFwdRows, 2] reference
+// and row sum (forward).
+size_t part_rows(const HostPlan& p) {
+  return static_cast<size_t>(p.fwd_slots) * p.hq * tree_attn::kFwdRows;
+}
+
+struct FwdLayout {
+  size_t o_part = 0, ml_part = 0, total = 0;
+};
+
+FwdLayout fwd_layout(const HostPlan& p) {
+  FwdLayout l;
+  if (p.fwd_slots == 0 || p.num_tokens == 0) return l;
+  l.ml_part = align256(part_rows(p) * p.head_dim * 4);
+  l.total = l.ml_part + align256(part_rows(p) * 2 * 4);
+  return l;
+}
+
 struct BwdLayout {
-  size_t neg_d = 0, neg_lse2 = 0, dk_slots = 0, dv_slots = 0, total = 0;
+  size_t neg_d = 0, neg_lse2 = 0, dk_slots = 0, dv_slots = 0, dq_part = 0, total = 0;
 };
 
 BwdLayout bwd_layout(const HostPlan& p) {
@@ -79,7 +101,8 @@ BwdLayout bwd_layout(const HostPlan& p) {
   l.neg_lse2 = align256(dv);
   l.dk_slots = l.neg_lse2 + align256(dv);
   l.dv_slots = l.dk_slots + align256(slot);
-  l.total = l.dv_slots + align256(slot);
+  l.dq_part = l.dv_slots + align256(slot);
+  l.total = l.dq_part + align256(part_rows(p) * p.head_dim * 4);
   if (p.num_tokens == 0) l.total = 0;
   return l;
 }
@@ -240,7 +263,10 @@ tree_attn_status_t device_plan(const int32_t* parent, const int32_t* seg_start,
   const HostPlan& hp = p->hp;
   const size_t o_ft = 0;
   const size_t o_fr = o_ft + align256(bytes_of(hp.fwd_tiles));
-  const size_t o_bi = o_fr + align256(bytes_of(hp.fwd_ranges));
+  const size_t o_fp = o_fr + align256(bytes_of(hp.fwd_ranges));
+  const size_t o_fc = o_fp + align256(bytes_of(hp.fwd_part));
+  const size_t o_fq = o_fc + align256(bytes_of(hp.fwd_combine));
+  const size_t o_bi = o_fq + align256(bytes_of(hp.fwd_qtiles));
   const size_t o_be = o_bi + align256(bytes_of(hp.bwd_items));
   const size_t o_br = o_be + align256(bytes_of(hp.bwd_entries));
   const size_t o_sg = o_br + align256(bytes_of(hp.bwd_reduce));
@@ -260,6 +286,9 @@ tree_attn_status_t device_plan(const int32_t* parent, const int32_t* seg_start,
       size_t n;
     } parts[] = {{o_ft, hp.fwd_tiles.data(), bytes_of(hp.fwd_tiles)},
                  {o_fr, hp.fwd_ranges.data(), bytes_of(hp.fwd_ranges)},
+                 {o_fp, hp.fwd_part.data(), bytes_of(hp.fwd_part)},
+                 {o_fc, hp.fwd_combine.data(), bytes_of(hp.fwd_combine)},
+                 {o_fq, hp.fwd_qtiles.data(), bytes_of(hp.fwd_qtiles)},
                  {o_bi, hp.bwd_items.data(), bytes_of(hp.bwd_items)},
                  {o_be, hp.bwd_entries.data(), bytes_of(hp.bwd_entries)},
                  {o_br, hp.bwd_reduce.data(), bytes_of(hp.bwd_reduce)},
@@ -279,6 +308,9 @@ tree_attn_status_t device_plan(const int32_t* parent, const int32_t* seg_start,
   }
   p->d_fwd_tiles = reinterpret_cast<const I4*>(p->dev_buf + o_ft);
   p->d_fwd_ranges = reinterpret_cast<const I4*>(p->dev_buf + o_fr);
+  p->d_fwd_part = reinterpret_cast<const int32_t*>(p->dev_buf + o_fp);
+  p->d_fwd_combine = reinterpret_cast<const I4*>(p->dev_buf + o_fc);
+  p->d_fwd_qtiles = reinterpret_cast<const I4*>(p->dev_buf + o_fq);
   p->d_bwd_items = reinterpret_cast<const I8*>(p->dev_buf + o_bi);
   p->d_bwd_entries = reinterpret_cast<const I4*>(p->dev_buf + o_be);
   p->d_bwd_reduce = reinterpret_cast<const I8*>(p->dev_buf + o_br);
@@ -336,7 +368,7 @@ void tree_attn_plan_destroy(tree_attn_plan_t plan) {
 tree_attn_status_t tree_attn_workspace_size(tree_attn_plan_t plan, size_t* fwd_bytes,
                                             size_t* bwd_bytes) {
   if (!plan) return report(Status::kInvalidArg, "null plan");
-  if (fwd_bytes) *fwd_bytes = 0;
+  if (fwd_bytes) *fwd_bytes = fwd_layout(plan->hp).total;
   if (bwd_bytes) *bwd_bytes = bwd_layout(plan->hp).total;
   return TREE_ATTN_OK;
 }
@@ -344,8 +376,6 @@ tree_attn_status_t tree_attn_workspace_size(tree_attn_plan_t plan, size_t* fwd_b
 tree_attn_status_t tree_attn_fwd(tree_attn_plan_t plan, const void* q, const void* k,
                                  const void* v, float softmax_scale, void* o, float* lse,
                                  void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!plan) return report(Status::kInvalidArg, "null plan");
   const HostPlan& hp = plan->hp;
   if (hp.num_tokens == 0 || hp.query_rows == 0) return check_device(plan);
@@ -356,6 +386,14 @@ tree_attn_status_t tree_attn_fwd(tree_attn_plan_t plan, const void* q, const voi
     return report(Status::kInvalidArg, "tensor pointers must be 16-byte aligned");
   if (!valid_softmax_scale(softmax_scale))
     return report(Status::kInvalidArg, "softmax_scale must be finite and > 0");
+  const FwdLayout l = fwd_layout(hp);
+  if (l.total > 0) {
+    if (!ws || ws_bytes < l.total)
+      return report(Status::kWorkspace, "forward workspace needs " + std::to_string(l.total) +
+                                            " bytes, got " + std::to_string(ws_bytes));
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+      return report(Status::kWorkspace, "workspace must be 256-byte aligned");
+  }
   tree_attn_status_t st = check_device(plan);
   if (st != TREE_ATTN_OK) return st;
   tree_attn::FwdArgs a{};
@@ -366,15 +404,24 @@ tree_attn_status_t tree_attn_fwd(tree_attn_plan_t plan, const void* q, const voi
   a.lse = lse;
   a.tiles = plan->d_fwd_tiles;
   a.ranges = plan->d_fwd_ranges;
+  a.part = plan->d_fwd_part;
+  if (l.total > 0) {
+    a.o_part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.o_part);
+    a.ml_part = reinterpret_cast<float*>(static_cast<char*>(ws) + l.ml_part);
+  }
+  a.combine = plan->d_fwd_combine;
+  a.n_combine = static_cast<int64_t>(hp.fwd_combine.size());
   a.n_tokens = hp.num_tokens;
   a.n_groups = hp.fwd_groups;
   a.hq = static_cast<int>(hp.hq);
   a.hkv = static_cast<int>(hp.hkv);
   a.gsize = static_cast<int>(hp.hq / hp.hkv);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  const int hd = static_cast<int>(hp.head_dim);
   const hipError_t e = timed(0, stream, [&] {
-    return tree_attn::launch_fwd(a, hp.dtype, static_cast<int>(hp.head_dim), hp.fwd_blocks,
-                                 stream);
+    hipError_t r = tree_attn::launch_fwd(a, hp.dtype, hd, hp.fwd_blocks, stream);
+    if (r == hipSuccess) r = tree_attn::launch_fwd_combine(a, hp.dtype, hd, stream);
+    return r;
   });
   if (e != hipSuccess) return report_hip(e, "forward launch");
   return TREE_ATTN_OK;
@@ -425,8 +472,8 @@ tree_attn_status_t bwd_common(tree_attn_plan_t plan, const void* q, const void* 
   if (acc) {
     a.acc_dk = static_cast<float*>(dk);
     a.acc_dv = static_cast<float*>(dv);
-    a.pre_tiles = plan->d_fwd_tiles;
-    a.n_pre_tiles = static_cast<int64_t>(hp.fwd_tiles.size());
+    a.pre_tiles = plan->d_fwd_qtiles;
+    a.n_pre_tiles = static_cast<int64_t>(hp.fwd_qtiles.size());
   } else {
     a.dk = dk;
     a.dv = dv;
@@ -440,6 +487,10 @@ tree_attn_status_t bwd_common(tree_attn_plan_t plan, const void* q, const void* 
   a.reduce = plan->d_bwd_reduce;
   a.tiles = plan->d_fwd_tiles;
   a.ranges = plan->d_fwd_ranges;
+  a.part = plan->d_fwd_part;
+  a.dq_part = reinterpret_cast<float*>(w + l.dq_part);
+  a.combine = plan->d_fwd_combine;
+  a.n_combine = static_cast<int64_t>(hp.fwd_combine.size());
   a.n_tokens = hp.num_tokens;
   a.n_items = static_cast<int64_t>(hp.bwd_items.size());
   a.n_reduce = static_cast<int64_t>(hp.bwd_reduce.size());
@@ -458,7 +509,11 @@ tree_attn_status_t bwd_common(tree_attn_plan_t plan, const void* q, const void* 
   if (e != hipSuccess) return report_hip(e, "backward dK/dV launch");
   e = timed(3, stream, [&] { return tree_attn::launch_bwd_post(a, hp.dtype, hd, stream); });
   if (e != hipSuccess) return report_hip(e, "backward reduction launch");
-  e = timed(4, stream, [&] { return tree_attn::launch_bwd_dq(a, hp.dtype, hd, stream); });
+  e = timed(4, stream, [&] {
+    hipError_t r = tree_attn::launch_bwd_dq(a, hp.dtype, hd, stream);
+    if (r == hipSuccess) r = tree_attn::launch_bwd_dq_sum(a, hp.dtype, hd, stream);
+    return r;
+  });
   if (e != hipSuccess) return report_hip(e, "backward dQ launch");
   return TREE_ATTN_OK;
 }
@@ -762,6 +817,19 @@ tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_st
   out->lin_chunk = tree_attn::kLinChunk;
   out->subset = hp.subset ? 1 : 0;
   out->query_rows = hp.query_rows;
+  out->fwd_split_tiles = static_cast<int64_t>(hp.fwd_combine.size());
+  out->fwd_slots = hp.fwd_slots;
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_plan_export_split(tree_attn_plan_t plan, int32_t* fwd_part,
+                                               int32_t* fwd_combine) {
+  if (!plan) return report(Status::kInvalidArg, "null plan");
+  const HostPlan& hp = plan->hp;
+  if (fwd_part && !hp.fwd_part.empty())
+    std::memcpy(fwd_part, hp.fwd_part.data(), bytes_of(hp.fwd_part));
+  if (fwd_combine && !hp.fwd_combine.empty())
+    std::memcpy(fwd_combine, hp.fwd_combine.data(), bytes_of(hp.fwd_combine));
   return TREE_ATTN_OK;
 }
 

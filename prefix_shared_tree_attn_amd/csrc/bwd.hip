@@ -1202,14 +1202,58 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void tree_attn_dq_kern
   }
 
   if (qrow < q1) {
-    T* op = static_cast<T*>(a.dq) + static_cast<int64_t>(qrow) * qs + static_cast<int64_t>(h) * D;
+    // a key part of a split tile writes its fp32 partial sum, which
+    // tree_attn_dq_sum_kernel adds up; a whole tile writes dQ
+    const int part = load_plan1(a.part, tile);
     const float sc = a.scale;
+    if (part >= 0) {
+      float* op = a.dq_part +
+                  ((static_cast<int64_t>(part) * a.hq + h) * kFwdRows + (qrow - q0)) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        store4(op + 32 * db + 8 * j + 4 * half, sc * qacc[db][4 * j], sc * qacc[db][4 * j + 1],
-               sc * qacc[db][4 * j + 2], sc * qacc[db][4 * j + 3]);
+        for (int j = 0; j < 4; ++j)
+          store4(op + 32 * db + 8 * j + 4 * half, sc * qacc[db][4 * j],
+                 sc * qacc[db][4 * j + 1], sc * qacc[db][4 * j + 2], sc * qacc[db][4 * j + 3]);
+    } else {
+      T* op =
+          static_cast<T*>(a.dq) + static_cast<int64_t>(qrow) * qs + static_cast<int64_t>(h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          store4(op + 32 * db + 8 * j + 4 * half, sc * qacc[db][4 * j],
+                 sc * qacc[db][4 * j + 1], sc * qacc[db][4 * j + 2], sc * qacc[db][4 * j + 3]);
+    }
+  }
+}
+
+// dQ of a split query tile: the fixed-order sum of its key parts' partial
+// sums (deterministic), rounded once.  One workgroup per (split tile, query
+// head); D / 8 threads per row, 8 columns each.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void tree_attn_dq_sum_kernel(BwdArgs a) {
+  const I4 c = load_plan4(a.combine, blockIdx.x);
+  const int q0 = c.x, q1 = c.y, s0 = c.z, ns = c.w;
+  const int h = blockIdx.y;
+  constexpr int TPR = D / 8, RPP = 256 / TPR;
+  const int col = (threadIdx.x % TPR) * 8;
+  for (int r = q0 + static_cast<int>(threadIdx.x) / TPR; r < q1; r += RPP) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ns; ++s) {
+      const int64_t row = (static_cast<int64_t>(s0 + s) * a.hq + h) * kFwdRows + (r - q0);
+      const f32x4* p = reinterpret_cast<const f32x4*>(a.dq_part + row * D + col);
+      const f32x4 x0 = p[0], x1 = p[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += x0[e];
+        acc[e + 4] += x1[e];
+      }
+    }
+    T* op = static_cast<T*>(a.dq) + static_cast<int64_t>(r) * a.hq * D +
+            static_cast<int64_t>(h) * D + col;
+    store4(op, acc[0], acc[1], acc[2], acc[3]);
+    store4(op + 4, acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
@@ -1321,6 +1365,15 @@ static hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
 }
 
 template <typename T, int D>
+static hipError_t dq_sum_t(const BwdArgs& a, hipStream_t s) {
+  if (a.n_combine <= 0) return hipSuccess;
+  hipLaunchKernelGGL((tree_attn_dq_sum_kernel<T, D>),
+                     dim3(static_cast<unsigned>(a.n_combine), static_cast<unsigned>(a.hq)),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
 static hipError_t post_t(const BwdArgs& a, hipStream_t s) {
   if (a.n_reduce == 0) return hipSuccess;
   // 16 blocks per split key tile: enough parallel streams over the slots
@@ -1334,6 +1387,7 @@ static hipError_t post_t(const BwdArgs& a, hipStream_t s) {
 #define TREE_ATTN_INSTANTIATE(T, D)                                          \
   template __global__ void tree_attn_bwd_pre_kernel<T, D>(BwdArgs);         \
   template __global__ void tree_attn_dq_kernel<T, D>(BwdArgs);              \
+  template __global__ void tree_attn_dq_sum_kernel<T, D>(BwdArgs);          \
   template __global__ void tree_attn_bwd_reduce_kernel<T, D>(BwdArgs);
 template __global__ void tree_attn_dkdv_pipe_kernel<128, false>(BwdArgs);
 template __global__ void tree_attn_dkdv_pipe_kernel<64, false>(BwdArgs);
@@ -1365,6 +1419,9 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int head_dim, hipStream_t 
 }
 hipError_t launch_bwd_post(const BwdArgs& a, int dtype, int head_dim, hipStream_t s) {
   TREE_ATTN_DISPATCH(post_t)
+}
+hipError_t launch_bwd_dq_sum(const BwdArgs& a, int dtype, int head_dim, hipStream_t s) {
+  TREE_ATTN_DISPATCH(dq_sum_t)
 }
 
 hipError_t launch_cast(const float* src, void* dst, int64_t n, int dtype, hipStream_t s) {

@@ -266,7 +266,9 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
       mx = max_across_halves(mx) * a.scale_log2;
       if (__any(mx > m + 8.f)) {
         const float m_new = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        // a row that has seen no key yet (in a key part of a split tile,
+        // keys may all lie past some rows) keeps m = -inf and zero sums
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
         m = m_new;
 #pragma unroll
         for (int i = 0; i < 4; ++i) lsum[i] *= alpha;
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
       }
-      soft(-m);
+      soft(m == -INFINITY ? 0.f : -m);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) lsum[i] += blk[i];
@@ -314,6 +316,26 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
   // finalize: O = O^T / l, LSE = ln 2 * (m + log2 l)
   const float lpart = (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
   const float ltot = lpart + __shfl_xor(lpart, 32);
+  const int part = load_plan1(a.part, tile);
+  if (part >= 0) {
+    // a key part of a split tile: unnormalised O, the running reference and
+    // the row sum, merged by tree_attn_fwd_combine_kernel
+    if (qrow < q1) {
+      const int64_t row = (static_cast<int64_t>(part) * a.hq + h) * kFwdRows + (qrow - q0);
+      float* op = a.o_part + row * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          store4(op + 32 * db + 8 * j + 4 * half, oacc[db][4 * j], oacc[db][4 * j + 1],
+                 oacc[db][4 * j + 2], oacc[db][4 * j + 3]);
+      if (half == 0) {
+        a.ml_part[2 * row] = m;
+        a.ml_part[2 * row + 1] = ltot;
+      }
+    }
+    return;
+  }
   if (qrow < q1) {
     const float inv = 1.f / ltot;
     T* op = static_cast<T*>(a.o) + static_cast<int64_t>(qrow) * qs + static_cast<int64_t>(h) * D;
@@ -347,6 +369,71 @@ static hipError_t fwd_t(const FwdArgs& a, int64_t n_blocks, hipStream_t s) {
   }
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(n_blocks)), dim3(256), bytes, s, a);
   return hipGetLastError();
+}
+
+// Merges the key parts of a split query tile: with m_c the reference and
+// l_c the row sum of part c and M = max_c m_c, O = sum_c 2^(m_c - M) O_c / L
+// and LSE = ln 2 (M + log2 L), L = sum_c 2^(m_c - M) l_c -- the online
+// softmax's own rescaling, across parts.  A part without keys for a row
+// (m_c = -inf) weighs 0.  One workgroup per (split tile, query head); D / 8
+// threads per row, 8 columns each.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void tree_attn_fwd_combine_kernel(FwdArgs a) {
+  const I4 c = load_plan4(a.combine, blockIdx.x);
+  const int q0 = c.x, q1 = c.y, s0 = c.z, ns = c.w;
+  const int h = blockIdx.y;
+  constexpr int TPR = D / 8, RPP = 256 / TPR;
+  const int col = (threadIdx.x % TPR) * 8;
+  for (int r = q0 + static_cast<int>(threadIdx.x) / TPR; r < q1; r += RPP) {
+    auto slot_row = [&](int s) {
+      return (static_cast<int64_t>(s0 + s) * a.hq + h) * kFwdRows + (r - q0);
+    };
+    float mref = -INFINITY;
+    for (int s = 0; s < ns; ++s) mref = fmaxf(mref, a.ml_part[2 * slot_row(s)]);
+    float l = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ns; ++s) {
+      const int64_t row = slot_row(s);
+      const float w = __builtin_amdgcn_exp2f(a.ml_part[2 * row] - mref);
+      l += w * a.ml_part[2 * row + 1];
+      const f32x4* po = reinterpret_cast<const f32x4*>(a.o_part + row * D + col);
+      const f32x4 x0 = po[0], x1 = po[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += w * x0[e];
+        acc[e + 4] += w * x1[e];
+      }
+    }
+    const float inv = 1.f / l;
+    T* op = static_cast<T*>(a.o) + static_cast<int64_t>(r) * a.hq * D +
+            static_cast<int64_t>(h) * D + col;
+    store4(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    store4(op + 4, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    if (col == 0)
+      a.lse[static_cast<int64_t>(h) * a.n_tokens + r] =
+          kLn2 * (mref + __builtin_amdgcn_logf(l));
+  }
+}
+
+template __global__ void tree_attn_fwd_combine_kernel<__bf16, 128>(FwdArgs);
+template __global__ void tree_attn_fwd_combine_kernel<__bf16, 64>(FwdArgs);
+template __global__ void tree_attn_fwd_combine_kernel<float, 128>(FwdArgs);
+template __global__ void tree_attn_fwd_combine_kernel<float, 64>(FwdArgs);
+
+template <typename T, int D>
+static hipError_t combine_t(const FwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((tree_attn_fwd_combine_kernel<T, D>),
+                     dim3(static_cast<unsigned>(a.n_combine), static_cast<unsigned>(a.hq)),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_combine(const FwdArgs& a, int dtype, int head_dim, hipStream_t stream) {
+  if (a.n_combine <= 0) return hipSuccess;
+  if (dtype == 0 && head_dim == 128) return combine_t<__bf16, 128>(a, stream);
+  if (dtype == 0 && head_dim == 64) return combine_t<__bf16, 64>(a, stream);
+  if (dtype == 1 && head_dim == 128) return combine_t<float, 128>(a, stream);
+  if (dtype == 1 && head_dim == 64) return combine_t<float, 64>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, int64_t n_blocks,

@@ -16,6 +16,11 @@ struct FwdArgs {
   float* lse;
   const I4* tiles;   // (q0, q1, range_begin, range_end)
   const I4* ranges;  // (k0, k1, causal, 0)
+  const int32_t* part;  // per tile: slot of a key part, or -1 (writes O and LSE)
+  float* o_part;     // [slots, Hq, kFwdRows, D] fp32 partial O (unnormalised)
+  float* ml_part;    // [slots, Hq, kFwdRows, 2] fp32 (base-2 running max, row sum)
+  const I4* combine; // (q0, q1, slot_begin, n_slots) per split query tile
+  int64_t n_combine;
   int64_t n_tokens;
   int64_t n_groups;  // tiles * hkv
   int hq, hkv, gsize;
@@ -45,6 +50,10 @@ struct BwdArgs {
   int64_t n_pre_tiles;
   const I4* tiles;   // dQ: forward query tiles (q0, q1, range_begin, range_end)
   const I4* ranges;  // dQ: forward key ranges (k0, k1, causal, 0)
+  const int32_t* part;  // dQ: per tile, slot of a key part or -1 (writes dQ)
+  float* dq_part;    // [slots, Hq, kFwdRows, D] fp32 partial dQ (scaled)
+  const I4* combine; // (q0, q1, slot_begin, n_slots) per split query tile
+  int64_t n_combine;
   int64_t n_tokens;
   int64_t n_items;
   int64_t n_reduce;
@@ -88,9 +97,13 @@ struct LinArgs {
 // dtype: 0 bf16, 1 fp32.  Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int head_dim, int64_t n_blocks,
                       hipStream_t stream);
+// merges the key parts of split query tiles into O and LSE
+hipError_t launch_fwd_combine(const FwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
+// adds the key parts' partial dQ of split query tiles into dQ
+hipError_t launch_bwd_dq_sum(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_post(const BwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 // dst[i] = src[i] rounded to the dtype, i < n (src 16-byte aligned)
 hipError_t launch_cast(const float* src, void* dst, int64_t n, int dtype, hipStream_t stream);

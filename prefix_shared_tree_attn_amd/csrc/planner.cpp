@@ -5,6 +5,7 @@
 #include "planner.h"
 
 #include <algorithm>
+#include <cmath>
 #include <map>
 #include <numeric>
 #include <sstream>
@@ -210,6 +211,7 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
   struct FTile {
     I4 t;
     int64_t cost;
+    int32_t part;
   };
   std::vector<FTile> ftiles;
   std::vector<I4> franges;
@@ -232,13 +234,98 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
       keys += r1 - cb;
       ftiles.push_back({{static_cast<int32_t>(r0), static_cast<int32_t>(r1), rb,
                          static_cast<int32_t>(franges.size())},
-                        (r1 - r0) * keys});
+                        (r1 - r0) * keys, -1});
+    }
+  }
+  p.fwd_qtiles.reserve(ftiles.size());
+  for (auto& t : ftiles) p.fwd_qtiles.push_back({t.t.x, t.t.y, 0, 0});
+  // ---- forward key splitting.  When (tile, head) workgroups would leave
+  // CUs idle (small trees, and the one-node calls of a depth-first walk,
+  // whose few query tiles each see a long ancestor path), a tile's keys are
+  // cut into parts, with parts in proportion to the tile's cost and at most
+  // kFwdFill workgroups per CU in all: a part then runs alone on its CU at
+  // full speed, where two workgroups sharing one would each run slower and
+  // a launch past one round would add a second.  Each part keeps at least
+  // kFwdMinPartSteps steps (a
+  // shorter part would save less time than the merge costs).  The merge
+  // passes (forward and dQ) are two more launches of fixed cost, about as
+  // long as 15 key steps of one workgroup, so a plan splits only when its
+  // longest tile has at least kFwdSplitSteps steps.  A part keeps
+  // the tile's rows and a contiguous run of its key steps (cuts fall on
+  // kFwdKeys boundaries of a range, so no part adds a ragged step); the
+  // parts' partial softmax results are merged after the launch.  Every
+  // (query, key) pair stays in exactly one item.
+  {
+    const int64_t items = static_cast<int64_t>(ftiles.size()) * num_q_heads;
+    const int64_t target = static_cast<int64_t>(kFwdFill) * num_cus;
+    auto tile_steps = [&](const FTile& t) {
+      int64_t steps = 0;
+      for (int32_t r = t.t.z; r < t.t.w; ++r)
+        steps += (static_cast<int64_t>(franges[r].y) - franges[r].x + kFwdKeys - 1) / kFwdKeys;
+      return steps;
+    };
+    int64_t longest = 0;
+    for (const FTile& t : ftiles) longest = std::max(longest, tile_steps(t));
+    if (items > 0 && items < target && longest >= kFwdSplitSteps) {
+      const double want = static_cast<double>(target) / static_cast<double>(num_q_heads);
+      double total = 0;
+      for (const FTile& t : ftiles) total += static_cast<double>(t.cost);
+      std::vector<FTile> out;
+      out.reserve(ftiles.size() * 2);
+      for (const FTile& t : ftiles) {
+        const int64_t steps = tile_steps(t);
+        int64_t parts =
+            total > 0 ? static_cast<int64_t>(want * static_cast<double>(t.cost) / total) : 1;
+        parts = std::max<int64_t>(
+            1, std::min<int64_t>({parts, steps / kFwdMinPartSteps, kFwdMaxParts}));
+        if (parts == 1) {
+          out.push_back(t);
+          continue;
+        }
+        const int32_t slot0 = static_cast<int32_t>(p.fwd_slots);
+        p.fwd_combine.push_back({t.t.x, t.t.y, slot0, static_cast<int32_t>(parts)});
+        p.fwd_slots += parts;
+        int32_t r = t.t.z;
+        int64_t pos = franges[r].x;
+        for (int64_t i = 0; i < parts; ++i) {
+          int64_t need = steps / parts + (i < steps % parts ? 1 : 0);
+          const int32_t rb = static_cast<int32_t>(franges.size());
+          int64_t keys = 0;
+          while (need > 0) {
+            const I4 rg = franges[r];  // copy: franges grows below
+            const int64_t left = (static_cast<int64_t>(rg.y) - pos + kFwdKeys - 1) / kFwdKeys;
+            if (left <= 0) {  // an empty range (none are built; kept safe)
+              if (r + 1 >= t.t.w) break;
+              ++r;
+              pos = franges[r].x;
+              continue;
+            }
+            const int64_t take = std::min(need, left);
+            const int64_t end = std::min<int64_t>(rg.y, pos + take * kFwdKeys);
+            franges.push_back({static_cast<int32_t>(pos), static_cast<int32_t>(end), rg.z, 0});
+            keys += end - pos;
+            need -= take;
+            pos = end;
+            if (pos == rg.y && r + 1 < t.t.w) {
+              ++r;
+              pos = franges[r].x;
+            }
+          }
+          out.push_back({{t.t.x, t.t.y, rb, static_cast<int32_t>(franges.size())},
+                         (t.t.y - t.t.x) * keys, slot0 + static_cast<int32_t>(i)});
+        }
+      }
+      ftiles = std::move(out);
     }
   }
   std::stable_sort(ftiles.begin(), ftiles.end(),
                    [](const FTile& a, const FTile& b) { return a.cost > b.cost; });
   p.fwd_tiles.reserve(ftiles.size());
-  for (auto& t : ftiles) p.fwd_tiles.push_back(t.t);
+  p.fwd_part.reserve(ftiles.size());
+  for (auto& t : ftiles) {
+    p.fwd_tiles.push_back(t.t);
+    p.fwd_part.push_back(t.part);
+  }
   p.fwd_ranges = std::move(franges);
   const int64_t gsize = num_q_heads / num_kv_heads;
   p.fwd_groups = static_cast<int64_t>(p.fwd_tiles.size()) * num_kv_heads;

@@ -36,6 +36,10 @@ constexpr int kBwdKeys = 128;  // keys per backward workgroup (4 waves x 32)
 constexpr int kBwdRows = 32;   // query rows per backward step
 constexpr int kXcds = 8;       // MI355X: 8 accelerator complex dies, 8 L2s
 constexpr int kLinChunk = 64;  // chunk of chunkwise linear attention (trajectory depth)
+constexpr int kFwdFill = 1;      // forward workgroups per CU a split launch may reach
+constexpr int kFwdMaxParts = 16; // most parts one query tile's keys are split into
+constexpr int kFwdMinPartSteps = 16;  // fewest key steps a part of a split tile keeps
+constexpr int kFwdSplitSteps = 48;    // a plan splits only if a tile has this many key steps
 
 struct I4 {
   int32_t x, y, z, w;
@@ -62,6 +66,18 @@ struct HostPlan {
   std::vector<I4> fwd_ranges;
   int64_t fwd_groups = 0;  // tiles * hkv
   int64_t fwd_blocks = 0;  // launch size (padded to whole XCD rounds) * group size
+  // A launch with too few (tile, head) workgroups to fill the chip splits the
+  // keys of its query tiles into parts: fwd_part[tile] is the part's slot
+  // (-1: the tile holds all of its rows' keys and writes the outputs), and
+  // fwd_combine holds (q0, q1, slot_begin, num_slots) per split query tile,
+  // whose parts' partial results a combine pass merges.  The same tiles
+  // drive the dQ pass, whose parts' partial sums are added the same way.
+  std::vector<int32_t> fwd_part;
+  std::vector<I4> fwd_combine;
+  int64_t fwd_slots = 0;
+  // every query tile once, (q0, q1, 0, 0): the rows a query-subset plan's
+  // backward preprocess covers
+  std::vector<I4> fwd_qtiles;
 
   // backward: items (k0, k1, kv_head, entry_begin, entry_end, slot, xcd, 0)
   // in launch order (item b runs on XCD b % 8; empty items pad the per-XCD

@@ -7,8 +7,10 @@ preorder and one accumulating backward call per node in reverse preorder.
 Summed over the walk, the results must be the whole tree's: checked against
 the fp64 oracle (whole tensors on small trees, sampled rows and keys on the
 GRPO-star and segment-search workloads at full size) and against the
-one-call library path (O, LSE and dQ bitwise: the same tiles run the same
-kernels).  One call on a
+one-call library path, to rounding: a one-node call has few query tiles, so
+the planner cuts their keys into parts that run side by side and merges the
+parts' partial results, where the whole-tree pass may not (another
+summation order, then one rounding).  One call on a
 random set of nodes is checked against ``oracle.tree_attention_subset``.
 Bar: relative L2 <= 1e-2 on O, dQ, dK, dV and max |LSE error| <= 1e-3.
 """
@@ -96,10 +98,11 @@ def test_depth_first_walk_equals_whole_tree(name):
         assert errs[k] <= rel_bar, (k, errs)
     assert errs["lse"] <= lse_bar
     whole = _whole(t, dev, hq, hkv, d, dtype, scale)
-    for k in ("o", "lse", "dq"):
-        assert torch.equal(got[k], whole[k]), k
-    for k in ("dk", "dv"):  # fp32 sums in another order, then one rounding
-        assert rel_l2(_host(got[k]), _host(whole[k])) <= 4e-3, k
+    # fp32 sums in another order, then one rounding to the output type
+    close = 2 * FP32_REL_L2 if dtype == "fp32" else 4e-3
+    for k in ("o", "dq", "dk", "dv"):
+        assert rel_l2(_host(got[k]), _host(whole[k])) <= close, k
+    assert float((got["lse"] - whole["lse"]).abs().max()) <= 1e-4
 
 
 def test_one_call_on_a_node_subset():
@@ -189,8 +192,9 @@ def test_plan_kind_checks_and_empty_subset():
 def test_full_size_walk(cfg):
     """The GRPO-star (17 nodes) and segment-search (127 nodes) workloads at
     full size, one node per call: sampled rows and keys against the oracle,
-    whole tensors against the one-call path (whose query tiles are the
-    walk's on these trees, every node a multiple of 128 tokens)."""
+    whole tensors against the one-call path to rounding (the walk's query
+    tiles are the one call's on these trees, every node a multiple of 128
+    tokens, but a one-node call cuts their keys into parts)."""
     import torch
     t = config_tree(cfg)
     sp = config_spec(cfg)
@@ -201,12 +205,11 @@ def test_full_size_walk(cfg):
     got = _walk(t, dev, hq, hkv, d, dtype, scale)
     print("walk done", flush=True)
     whole = _whole(t, dev, hq, hkv, d, dtype, scale)
-    for k in ("o", "lse", "dq"):
-        assert torch.equal(got[k], whole[k]), k
-    for k in ("dk", "dv"):
+    for k in ("o", "dq", "dk", "dv"):
         e = rel_l2(_host(got[k]), _host(whole[k]))
         print(f"{k}: walk vs one call rel-L2 {e:.2e}", flush=True)
         assert e <= 4e-3, k
+    assert float((got["lse"] - whole["lse"]).abs().max()) <= 1e-4
     rng = np.random.default_rng(7)
     rows = sorted(set([0, t.num_tokens - 1] + [int(r) for r in rng.integers(0, t.num_tokens, 10)]))
     heads = [int(rng.integers(0, hq))]

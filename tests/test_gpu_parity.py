@@ -67,7 +67,15 @@ CASES = {
                     "bf16"),
     "caterpillar-fp32": (caterpillar_tree([1 + (5 * i) % 4 for i in range(90)], 9), 2, 1, 64,
                          "fp32"),
+    # few query tiles over long key paths: the planner cuts their keys into
+    # parts (forward and dQ partial results merged after the launch); some
+    # parts hold no key of some rows (causal ranges cut mid-way)
+    "long-chain-key-parts": (chain_tree([3500, 300]), 4, 2, 128, "bf16"),
+    "star-key-parts-fp32": (star_tree(3200, 3, 200), 2, 1, 64, "fp32"),
+    "caterpillar-key-parts": (caterpillar_tree([1200, 1100, 1000, 900], 150), 4, 2, 128,
+                              "bf16"),
 }
+KEY_PART_CASES = ("long-chain-key-parts", "star-key-parts-fp32", "caterpillar-key-parts")
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -161,6 +169,10 @@ def test_split_case_really_splits():
     t, hq, hkv, d, dtype = CASES["heavy-prompt-split"]
     p = ta.plan(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, d, dtype)
     assert p.stats()["bwd_split_tiles"] > 0
+    for name in KEY_PART_CASES:
+        t, hq, hkv, d, dtype = CASES[name]
+        p = ta.plan(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, d, dtype)
+        assert p.stats()["fwd_split_tiles"] > 0, name
 
 
 def test_config1_full():
@@ -394,7 +406,8 @@ def test_positions_bit_exact():
 
 
 @pytest.mark.parametrize("name,dtype", [("heavy-prompt-split", "bf16"), ("caterpillar", "bf16"),
-                                        ("binary-fp32", "fp32")])
+                                        ("binary-fp32", "fp32"),
+                                        ("long-chain-key-parts", "bf16")])
 def test_outputs_and_workspace_stay_inside_their_buffers(name, dtype):
     """Canary margins: O, LSE, dQ, dK, dV and the backward workspace are
     views into larger buffers whose margins (64 KiB before and after) hold
@@ -429,10 +442,11 @@ def test_outputs_and_workspace_stay_inside_their_buffers(name, dtype):
         bufs[key] = buf
         outs[key] = view(inner, shape, dt)
     p = ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype)
-    wsz = p.workspace_size()[1]
+    wsf, wsz = p.workspace_size()
     bufs["ws"], ws = fenced(wsz)
+    bufs["ws_fwd"], ws_f = fenced(max(wsf, 256))
     scale = 1.0 / np.sqrt(d)
-    ta.fwd(p, dev["q"], dev["k"], dev["v"], scale, o=outs["o"], lse=outs["lse"])
+    ta.fwd(p, dev["q"], dev["k"], dev["v"], scale, o=outs["o"], lse=outs["lse"], ws=ws_f)
     ta.bwd(p, dev["q"], dev["k"], dev["v"], outs["o"], outs["lse"], dev["do"], scale,
            dq=outs["dq"], dk=outs["dk"], dv=outs["dv"], ws=ws)
     torch.cuda.synchronize()

@@ -440,3 +440,88 @@ def test_caterpillar_tiles_span_many_nodes():
     # every other leaf is a run of its own
     assert len(ex["fwd_tiles"]) == -(-(trunk + 5) // 128) + 149
     assert int((ex["bwd_entries"][:, 3] < 0).sum()) > 100
+
+
+def _key_intervals(ex, tiles):
+    """(k0, k1, causal) intervals of the given forward tiles, sorted, with
+    adjacent intervals of equal causality merged."""
+    iv = sorted((int(k0), int(k1), int(c)) for i in tiles
+                for k0, k1, c, _ in ex["fwd_ranges"][ex["fwd_tiles"][i][2]:ex["fwd_tiles"][i][3]])
+    out = []
+    for k0, k1, c in iv:
+        if out and out[-1][1] == k0 and out[-1][2] == c:
+            out[-1] = (out[-1][0], k1, c)
+        else:
+            out.append((k0, k1, c))
+    return out
+
+
+SPLIT_TREES = {
+    "chain": chain_tree([3500, 300]),
+    "star": star_tree(3200, 3, 200),
+    "binary": binary_tree(2000, 400, 3),
+    "caterpillar": caterpillar_tree([1200, 1100, 1000, 900], 150),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_TREES))
+@pytest.mark.parametrize("subset", [False, True])
+def test_split_forward_tiles(name, subset):
+    """A plan whose (query tile, head) workgroups would leave CUs idle
+    cuts the keys of its long query tiles into parts of at least
+    kFwdMinPartSteps steps: each split query tile's parts are the tiles with
+    its rows and its consecutive slots, together they hold exactly the keys of
+    the unsplit tile (the plan for a one-CU chip, which never splits), the
+    parts share the tile's key steps evenly, and the forward and backward
+    workspaces hold the parts' fp32 partial results."""
+    t = SPLIT_TREES[name]
+    hq, hkv, d = 2, 1, 64
+    qn = [t.num_nodes - 1] if subset else None
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, d, "bf16",
+                     query_nodes=qn)
+    whole = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, d, "bf16",
+                         num_cus=1, query_nodes=qn)
+    ex, st = p.export(), p.stats()
+    ew = whole.export()
+    assert st["fwd_split_tiles"] > 0 and whole.stats()["fwd_split_tiles"] == 0
+    part, comb = ex["fwd_part"], ex["fwd_combine"]
+    assert comb.shape == (st["fwd_split_tiles"], 4)
+    assert sorted(part[part >= 0].tolist()) == list(range(st["fwd_slots"]))
+    by_rows = {tuple(int(x) for x in ew["fwd_tiles"][i][:2]): i
+               for i in range(len(ew["fwd_tiles"]))}
+    split_rows = set()
+    for q0, q1, s0, ns in comb:
+        assert ns >= 2
+        idx_t = np.nonzero((part >= s0) & (part < s0 + ns))[0]
+        assert len(idx_t) == ns
+        assert all(tuple(ex["fwd_tiles"][i][:2]) == (q0, q1) for i in idx_t)
+        assert _key_intervals(ex, idx_t) == _key_intervals(ew, [by_rows[(int(q0), int(q1))]])
+        steps = []
+        for i in idx_t:
+            rb, re_ = ex["fwd_tiles"][i][2:]
+            steps.append(sum((k1 - k0 + 63) // 64 for k0, k1, _, _ in ex["fwd_ranges"][rb:re_]))
+        assert min(steps) >= 16 and max(steps) - min(steps) <= 1
+        split_rows.add((int(q0), int(q1)))
+    # the unsplit tiles are the whole plan's other tiles, unchanged
+    rest = sorted(tuple(int(x) for x in ex["fwd_tiles"][i][:2]) for i in np.nonzero(part < 0)[0])
+    assert rest == sorted(r for r in by_rows if r not in split_rows)
+    for i in np.nonzero(part < 0)[0]:
+        r = tuple(int(x) for x in ex["fwd_tiles"][i][:2])
+        assert _key_intervals(ex, [i]) == _key_intervals(ew, [by_rows[r]])
+    f, b = p.workspace_size()
+    al = lambda x: (x + 255) // 256 * 256
+    rows = st["fwd_slots"] * hq * 128
+    assert f == al(rows * d * 4) + al(rows * 2 * 4)
+    n = t.num_tokens
+    slot = st["bwd_slots"] * 128 * d * 4
+    assert b == 2 * al(n * hq * 4) + 2 * al(slot) + al(rows * d * 4)
+
+
+def test_large_plans_do_not_split_forward_tiles():
+    for cfg, hq, hkv in ((2, 32, 8), (4, 28, 4)):
+        t = config_tree(cfg)
+        p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, 128)
+        ex, st = p.export(), p.stats()
+        assert st["fwd_split_tiles"] == 0 and st["fwd_slots"] == 0
+        assert np.all(ex["fwd_part"] == -1)
+        assert p.workspace_size()[0] == 0
