@@ -6,7 +6,7 @@
 // descendant branch in registers (Tree Training in the HARTS page's related
 // list: reuse shared-prefix work in forward and backward).
 //
-// Four launches, no atomics anywhere:
+// Four launches (five with split query tiles), no atomics anywhere:
 //  1. preprocess: D_t = sum_d dO_t O_t per (token, head);
 //  2. dK / dV, one workgroup per key tile (up to 128 keys of one node) and kv
 //     head.  It walks every query step that sees the tile -- the rest of its
@@ -23,8 +23,10 @@
 //     key ranges like the forward pass: S^T = K Q^T and dP^T = V dO^T, then
 //     dS^T = P^T (dP^T - D) and dQ^T += K^T dS^T in registers, written once.
 //     Recomputing S and dP here costs MFMA work but replaces a per-key-tile
-//     fp32 atomic reduction of dQ whose memory traffic would dominate the pass;
-//  4. a fixed-order sum of the partial slots (deterministic dK / dV).
+//     fp32 atomic reduction of dQ whose memory traffic would dominate the pass.
+//     The key parts of a split query tile write fp32 partial dQ instead;
+//  4. a fixed-order sum of the partial slots (deterministic dK / dV), and of
+//     the key parts' partial dQ where the plan split query tiles.
 #include "device_common.h"
 #include "kernels.h"
 

@@ -15,6 +15,10 @@
 // operand without leaving registers, and V^T is read from the row-major LDS
 // tile with transpose loads.  K and V tiles are staged through LDS once per
 // step and shared by the four waves.
+//
+// In a launch with too few (tile, head) workgroups to occupy the chip, the
+// planner may cut a tile's keys into parts; a part writes its unnormalised
+// partial result and tree_attn_fwd_combine_kernel merges the parts.
 #include "device_common.h"
 #include "kernels.h"
 
