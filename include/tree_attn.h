@@ -415,6 +415,9 @@ typedef struct {
   int64_t query_rows;       /* tokens that are queries (N for whole trees)  */
   int64_t fwd_split_tiles;  /* query tiles whose keys were split into parts */
   int64_t fwd_slots;        /* key parts of those tiles (forward / dQ slots) */
+  int64_t lin_chains;       /* linear attention: heavy paths of the scans   */
+  int64_t lin_phases;       /* linear attention: scan launches per pass     */
+  int64_t lin_nodes;        /* linear attention: nodes in the scan order    */
 } tree_attn_plan_stats_t;
 
 tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_stats_t* out);
@@ -513,6 +516,19 @@ tree_attn_status_t tree_attn_lin_bwd(tree_attn_plan_t plan, const void* q, const
  * successor end, node, 0, 0) in root-first order, and successors [lin_succ].
  * Either pointer may be null.
  */
+/*
+ * Copies the order of the linear-attention state scans to host arrays (for
+ * tests): chains [lin_chains x 4] = (begin, end, phase, 0) into chain_nodes
+ * [lin_nodes], which lists positions in the root-first node order, each
+ * chain a heavy path from its head (every node followed by its child with
+ * the most pieces below it); phases [lin_phases x 4] = (chain begin, chain
+ * end, 0, 0).  A pass scans the phases in order (forward) or in reverse
+ * (backward), the chains of one phase side by side.  Any pointer may be
+ * null.
+ */
+tree_attn_status_t tree_attn_lin_plan_export_chains(tree_attn_plan_t plan, int32_t* chains,
+                                                    int32_t* chain_nodes, int32_t* phases);
+
 tree_attn_status_t tree_attn_lin_plan_export(tree_attn_plan_t plan, int32_t* pieces,
                                              int32_t* successors);
 

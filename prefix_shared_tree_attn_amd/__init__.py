@@ -77,12 +77,19 @@ class Plan:
         return int(f.value), int(b.value)
 
     def lin_export(self) -> dict:
-        """Linear-attention piece table: ``pieces [P, 8]`` and ``succ``."""
+        """Linear-attention piece table: ``pieces [P, 8]`` and ``succ``, and the
+        state scans' order: ``chains``, ``chain_nodes`` and ``phases``."""
         st = self.stats()
         out = {"pieces": np.zeros((st["lin_pieces"], 8), np.int32),
                "succ": np.zeros((st["lin_succ"],), np.int32)}
         _ffi.check(_ffi.lib().tree_attn_lin_plan_export(
             self.handle, _ptr(out["pieces"]), _ptr(out["succ"])), "lin_plan_export")
+        out["chains"] = np.zeros((st["lin_chains"], 4), np.int32)
+        out["chain_nodes"] = np.zeros((st["lin_nodes"],), np.int32)
+        out["phases"] = np.zeros((st["lin_phases"], 4), np.int32)
+        _ffi.check(_ffi.lib().tree_attn_lin_plan_export_chains(
+            self.handle, _ptr(out["chains"]), _ptr(out["chain_nodes"]), _ptr(out["phases"])),
+            "lin_plan_export_chains")
         return out
 
     def stats(self) -> dict:

@@ -27,6 +27,7 @@ EXPORTS = (
     "tree_attn_lin_fwd", "tree_attn_lin_bwd", "tree_attn_lin_plan_export",
     "tree_attn_plan_subset", "tree_attn_plan_host_subset", "tree_attn_bwd_accum",
     "tree_attn_accum_cast", "tree_attn_bwd_noalloc", "tree_attn_plan_export_split",
+    "tree_attn_lin_plan_export_chains",
 )
 
 
@@ -36,7 +37,7 @@ class PlanStats(ctypes.Structure):
         "fwd_tiles", "fwd_ranges", "fwd_blocks", "bwd_items", "bwd_entries",
         "bwd_split_tiles", "bwd_slots", "fwd_tile_rows", "fwd_tile_keys", "bwd_tile_keys",
         "bwd_block_rows", "lin_pieces", "lin_succ", "lin_chunk", "subset", "query_rows",
-        "fwd_split_tiles", "fwd_slots")]
+        "fwd_split_tiles", "fwd_slots", "lin_chains", "lin_phases", "lin_nodes")]
 
 
 class Timing(ctypes.Structure):
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
     L.tree_attn_plan_stats.argtypes = [vp, ctypes.POINTER(PlanStats)]
     L.tree_attn_plan_export.argtypes = [vp, i32p, i32p, i32p, i32p]
     L.tree_attn_plan_export_split.argtypes = [vp, i32p, i32p]
+    L.tree_attn_lin_plan_export_chains.argtypes = [vp, i32p, i32p, i32p]
     L.tree_attn_status_string.argtypes = [ctypes.c_int]
     L.tree_attn_status_string.restype = ctypes.c_char_p
     L.tree_attn_last_error.argtypes = []
@@ -118,7 +120,8 @@ def lib() -> ctypes.CDLL:
                "tree_attn_rope", "tree_attn_lin_workspace_size", "tree_attn_lin_fwd",
                "tree_attn_lin_bwd", "tree_attn_lin_plan_export", "tree_attn_plan_subset",
                "tree_attn_plan_host_subset", "tree_attn_bwd_accum", "tree_attn_accum_cast",
-               "tree_attn_bwd_noalloc", "tree_attn_plan_export_split"):
+               "tree_attn_bwd_noalloc", "tree_attn_plan_export_split",
+               "tree_attn_lin_plan_export_chains"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L

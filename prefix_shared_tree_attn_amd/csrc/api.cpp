@@ -38,6 +38,8 @@ struct tree_attn_plan_s {
   const I8* d_lin_pieces = nullptr;
   const int32_t* d_lin_succ = nullptr;
   const I4* d_lin_nodes = nullptr;
+  const int32_t* d_lin_chain_nodes = nullptr;
+  const I4* d_lin_chains = nullptr;
 };
 
 namespace {
@@ -273,7 +275,9 @@ tree_attn_status_t device_plan(const int32_t* parent, const int32_t* seg_start,
   const size_t o_lp = o_sg + align256(bytes_of(hp.segments));
   const size_t o_ls = o_lp + align256(bytes_of(hp.lin_pieces));
   const size_t o_ln = o_ls + align256(bytes_of(hp.lin_succ));
-  const size_t total = o_ln + align256(bytes_of(hp.lin_nodes));
+  const size_t o_lcn = o_ln + align256(bytes_of(hp.lin_nodes));
+  const size_t o_lc = o_lcn + align256(bytes_of(hp.lin_chain_nodes));
+  const size_t total = o_lc + align256(bytes_of(hp.lin_chains));
   if (total > 0) {
     e = hipMalloc(reinterpret_cast<void**>(&p->dev_buf), total);
     if (e != hipSuccess) {
@@ -295,7 +299,9 @@ tree_attn_status_t device_plan(const int32_t* parent, const int32_t* seg_start,
                  {o_sg, hp.segments.data(), bytes_of(hp.segments)},
                  {o_lp, hp.lin_pieces.data(), bytes_of(hp.lin_pieces)},
                  {o_ls, hp.lin_succ.data(), bytes_of(hp.lin_succ)},
-                 {o_ln, hp.lin_nodes.data(), bytes_of(hp.lin_nodes)}};
+                 {o_ln, hp.lin_nodes.data(), bytes_of(hp.lin_nodes)},
+                 {o_lcn, hp.lin_chain_nodes.data(), bytes_of(hp.lin_chain_nodes)},
+                 {o_lc, hp.lin_chains.data(), bytes_of(hp.lin_chains)}};
     for (const Part& part : parts) {
       if (part.n == 0) continue;
       e = hipMemcpyAsync(p->dev_buf + part.off, part.src, part.n, hipMemcpyHostToDevice, stream);
@@ -318,6 +324,8 @@ tree_attn_status_t device_plan(const int32_t* parent, const int32_t* seg_start,
   p->d_lin_pieces = reinterpret_cast<const I8*>(p->dev_buf + o_lp);
   p->d_lin_succ = reinterpret_cast<const int32_t*>(p->dev_buf + o_ls);
   p->d_lin_nodes = reinterpret_cast<const I4*>(p->dev_buf + o_ln);
+  p->d_lin_chain_nodes = reinterpret_cast<const int32_t*>(p->dev_buf + o_lcn);
+  p->d_lin_chains = reinterpret_cast<const I4*>(p->dev_buf + o_lc);
   p->has_device = true;
   p->device = dev;
   *out = p;
@@ -617,6 +625,10 @@ tree_attn::LinArgs lin_args(tree_attn_plan_t plan, float scale) {
   a.pieces = plan->d_lin_pieces;
   a.succ = plan->d_lin_succ;
   a.lnodes = plan->d_lin_nodes;
+  a.chains = plan->d_lin_chains;
+  a.chain_nodes = plan->d_lin_chain_nodes;
+  a.phases = hp.lin_phases.data();
+  a.n_phases = static_cast<int>(hp.lin_phases.size());
   a.n_pieces = static_cast<int64_t>(hp.lin_pieces.size());
   a.n_nodes = static_cast<int64_t>(hp.lin_nodes.size());
   a.hq = static_cast<int>(hp.hq);
@@ -819,6 +831,22 @@ tree_attn_status_t tree_attn_plan_stats(tree_attn_plan_t plan, tree_attn_plan_st
   out->query_rows = hp.query_rows;
   out->fwd_split_tiles = static_cast<int64_t>(hp.fwd_combine.size());
   out->fwd_slots = hp.fwd_slots;
+  out->lin_chains = static_cast<int64_t>(hp.lin_chains.size());
+  out->lin_phases = static_cast<int64_t>(hp.lin_phases.size());
+  out->lin_nodes = static_cast<int64_t>(hp.lin_nodes.size());
+  return TREE_ATTN_OK;
+}
+
+tree_attn_status_t tree_attn_lin_plan_export_chains(tree_attn_plan_t plan, int32_t* chains,
+                                                    int32_t* chain_nodes, int32_t* phases) {
+  if (!plan) return report(Status::kInvalidArg, "null plan");
+  const HostPlan& hp = plan->hp;
+  if (chains && !hp.lin_chains.empty())
+    std::memcpy(chains, hp.lin_chains.data(), bytes_of(hp.lin_chains));
+  if (chain_nodes && !hp.lin_chain_nodes.empty())
+    std::memcpy(chain_nodes, hp.lin_chain_nodes.data(), bytes_of(hp.lin_chain_nodes));
+  if (phases && !hp.lin_phases.empty())
+    std::memcpy(phases, hp.lin_phases.data(), bytes_of(hp.lin_phases));
   return TREE_ATTN_OK;
 }
 

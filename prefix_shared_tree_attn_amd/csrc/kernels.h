@@ -88,6 +88,10 @@ struct LinArgs {
   const I8* pieces;      // (token0, len, pred, succ_begin, succ_end, node, flags, 0)
   const int32_t* succ;   // successor piece indices
   const I4* lnodes;      // (first piece, pieces, parent node, node) root first
+  const I4* chains;      // scans: heavy paths (begin, end, phase, 0) into chain_nodes
+  const int32_t* chain_nodes;  // lnodes indices, each chain's nodes from its head
+  const I4* phases;      // host array: (chain_begin, chain_end, 0, 0) per phase
+  int n_phases;
   int64_t n_pieces;
   int64_t n_nodes;
   int hq, hkv, gsize;

@@ -155,9 +155,14 @@ __global__ __launch_bounds__(256) void lin_outer_kernel(LinArgs a, int backward)
 }
 
 // (2) State scan, one thread per two neighbouring (kv head, state element)
-// pairs, accumulating in fp32.  Nodes go in root-first order (forward) or
-// its reverse (backward); inside a node the pieces form a chain, streamed
-// with their sums fetched LA pieces ahead.
+// pairs, accumulating in fp32, and one workgroup row (blockIdx.y) per heavy
+// path of the launch's phase: the path's nodes go head first (forward) or
+// tail first (backward), while the paths of one phase, which share no node,
+// run side by side; phases are launched in order (forward) or in reverse
+// (backward), so that a path's head finds its parent's end state, and a
+// node its light children's handed-up gradients, already written.  Inside a
+// node the pieces form a chain, streamed with their sums fetched LA pieces
+// ahead.
 //   Forward: the state entering a node's first piece is the state at its
 //   parent's end (zero at a root); each piece's entering state is stored,
 //   then its sum added; the node's end state goes to `ends`.
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(256) void lin_outer_kernel(LinArgs a, int backward)
 //   handed to the parent through `ends`.
 // The chunk kernels read the stored states as bf16.
 template <int D>
-__global__ __launch_bounds__(256) void lin_scan_kernel(LinArgs a, int backward) {
+__global__ __launch_bounds__(256) void lin_scan_kernel(LinArgs a, int backward, int chain0) {
   typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
   typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
   const int64_t per = static_cast<int64_t>(a.hkv) * D * D;  // one piece's states
@@ -177,9 +182,11 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(LinArgs a, int backward) 
   const __bf16* delta = static_cast<const __bf16*>(a.delta);
   __bf16* state = static_cast<__bf16*>(a.state);
   constexpr int LA = 16;
-  const int nn = static_cast<int>(a.n_nodes);
+  const I4 ch = load_plan4(a.chains, chain0 + static_cast<int>(blockIdx.y));
+  const int nn = ch.y - ch.x;
   for (int k = 0; k < nn; ++k) {
-    const I4 nd = load_plan4(a.lnodes, backward ? nn - 1 - k : k);
+    const I4 nd =
+        load_plan4(a.lnodes, load_plan1(a.chain_nodes, backward ? ch.y - 1 - k : ch.x + k));
     const int first = nd.x, count = nd.y;
     float s0 = 0.f, s1 = 0.f;
     if (!backward) {
@@ -453,8 +460,8 @@ template __global__ void lin_dkdv_kernel<128>(LinArgs);
 template __global__ void lin_dkdv_kernel<64>(LinArgs);
 template __global__ void lin_outer_kernel<128>(LinArgs, int);
 template __global__ void lin_outer_kernel<64>(LinArgs, int);
-template __global__ void lin_scan_kernel<128>(LinArgs, int);
-template __global__ void lin_scan_kernel<64>(LinArgs, int);
+template __global__ void lin_scan_kernel<128>(LinArgs, int, int);
+template __global__ void lin_scan_kernel<64>(LinArgs, int, int);
 template __global__ void lin_chunk_kernel<128, 0>(LinArgs);
 template __global__ void lin_chunk_kernel<128, 1>(LinArgs);
 template __global__ void lin_chunk_kernel<64, 0>(LinArgs);
@@ -490,9 +497,20 @@ hipError_t lin_outer_t(const LinArgs& a, int backward, hipStream_t s) {
 template <int D>
 hipError_t lin_scan_t(const LinArgs& a, int backward, hipStream_t s) {
   const int64_t per = static_cast<int64_t>(a.hkv) * D * D;
-  hipLaunchKernelGGL(lin_scan_kernel<D>, dim3(static_cast<unsigned>((per / 2 + 255) / 256)),
-                     dim3(256), 0, s, a, backward);
-  return hipGetLastError();
+  constexpr int kMaxRows = 65535;  // grid y limit
+  for (int k = 0; k < a.n_phases; ++k) {
+    const I4 ph = a.phases[backward ? a.n_phases - 1 - k : k];
+    for (int c0 = ph.x; c0 < ph.y; c0 += kMaxRows) {
+      const int rows = ph.y - c0 < kMaxRows ? ph.y - c0 : kMaxRows;
+      hipLaunchKernelGGL(lin_scan_kernel<D>,
+                         dim3(static_cast<unsigned>((per / 2 + 255) / 256),
+                              static_cast<unsigned>(rows)),
+                         dim3(256), 0, s, a, backward, c0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 template <int D, int MODE>

@@ -64,6 +64,55 @@ void build_lin_pieces(const int32_t* parent, const int32_t* seg_start, const int
     out->lin_nodes.push_back({first[i], pred - first[i] + 1,
                               parent[i] >= 0 ? parent[i] : -1, i});
   }
+  // heavy paths for the state scans: chains of nodes run one after another
+  // in one thread, while the chains of a phase run side by side
+  {
+    std::vector<int64_t> below(m, 0);  // pieces in a node's subtree, indexed by node
+    for (size_t k = m; k-- > 0;) {
+      const int32_t i = order[k];
+      below[i] += last[i] - first[i] + 1;
+      if (parent[i] >= 0) below[parent[i]] += below[i];
+    }
+    std::vector<int32_t> pos(m, -1), heavy(m, -1), phase(m, 0);
+    for (size_t k = 0; k < m; ++k) pos[order[k]] = static_cast<int32_t>(k);
+    for (int32_t i : order) {
+      int64_t best = -1;
+      for (int32_t c : children[i])
+        if (below[c] > best) {
+          best = below[c];
+          heavy[i] = c;
+        }
+    }
+    struct Chain {
+      int32_t phase;
+      std::vector<int32_t> nodes;
+    };
+    std::vector<Chain> chains;
+    for (int32_t i : order) {  // chain heads in root-first order
+      const int32_t pa = parent[i];
+      if (pa >= 0 && heavy[pa] == i) continue;
+      Chain c;
+      c.phase = pa >= 0 ? phase[pa] + 1 : 0;
+      for (int32_t j = i; j >= 0; j = heavy[j]) {
+        phase[j] = c.phase;
+        c.nodes.push_back(pos[j]);
+      }
+      chains.push_back(std::move(c));
+    }
+    std::stable_sort(chains.begin(), chains.end(),
+                     [](const Chain& x, const Chain& y) { return x.phase < y.phase; });
+    for (const Chain& c : chains) {
+      const int32_t b = static_cast<int32_t>(out->lin_chain_nodes.size());
+      out->lin_chain_nodes.insert(out->lin_chain_nodes.end(), c.nodes.begin(), c.nodes.end());
+      out->lin_chains.push_back(
+          {b, static_cast<int32_t>(out->lin_chain_nodes.size()), c.phase, 0});
+      const int32_t ci = static_cast<int32_t>(out->lin_chains.size()) - 1;
+      if (out->lin_phases.empty() || c.phase != static_cast<int32_t>(out->lin_phases.size()) - 1)
+        out->lin_phases.push_back({ci, ci + 1, 0, 0});
+      else
+        out->lin_phases.back().y = ci + 1;
+    }
+  }
   std::vector<int32_t>& sc = out->lin_succ;
   for (size_t j = 0; j < pc.size(); ++j) {
     const int32_t node = pc[j].v[5];

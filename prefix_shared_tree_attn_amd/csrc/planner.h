@@ -102,6 +102,14 @@ struct HostPlan {
   // nodes in the same root-first order: (first piece, pieces, parent node or
   // -1, node)
   std::vector<I4> lin_nodes;
+  // the state scans' order: heavy paths (each node followed by its child with
+  // the most pieces below it) as runs of lin_nodes indices, lin_chains
+  // (begin, end, phase, 0) into lin_chain_nodes; phase p holds the chains
+  // whose head hangs off a chain of phase p - 1 (roots: phase 0), and
+  // lin_phases (chain_begin, chain_end, 0, 0) lists them phase by phase
+  std::vector<int32_t> lin_chain_nodes;
+  std::vector<I4> lin_chains;
+  std::vector<I4> lin_phases;
 };
 
 // Validates the table and fills `out`.  `query_nodes` (num_query_nodes

@@ -2,8 +2,9 @@
 
 GPU: two calls in a row through the C ABI, the second on a smaller tree,
 each checked against tree_attn_bwd with a caller workspace (same kernels and
-plan, so the results must agree bit for bit) and the first also against the
-fp64 oracle at the parity bar.  CPU: the size, plan-kind and null checks
+plan, so the results must agree bit for bit) and against the fp64 oracle at
+the parity bar; then a plan whose query tiles are cut into key parts, whose
+partial dQ also lives in the fixed scratch.  CPU: the size, plan-kind and null checks
 that run before any device work.
 """
 
@@ -15,7 +16,7 @@ import pytest
 import oracle
 import prefix_shared_tree_attn_amd as ta
 from prefix_shared_tree_attn_amd import _ffi
-from tree_inputs import binary_tree, star_tree
+from tree_inputs import binary_tree, chain_tree, star_tree
 from gpu_util import LSE_ABS, REL_L2, device_inputs, make, rel_l2
 
 STATIC_BYTES = 64 << 20
@@ -84,3 +85,12 @@ def test_noalloc_two_calls_second_smaller():
     _one_call(star_tree(1024, 16, 64), 4, 2, 128, "bf16", check_oracle=True)
     # second: a smaller, ragged tree on the same (now dirty) scratch
     _one_call(binary_tree(129, 97, 3), 4, 2, 128, "bf16", check_oracle=True)
+
+
+@pytest.mark.gpu
+def test_noalloc_with_key_parts():
+    t = chain_tree([3500, 300])
+    p = ta.plan(t.parent, t.seg_start, t.seg_len, t.num_tokens, 4, 2, 128, "bf16")
+    assert p.stats()["fwd_split_tiles"] > 0
+    p.close()
+    _one_call(t, 4, 2, 128, "bf16", check_oracle=True)
