@@ -99,9 +99,12 @@ __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 
 // out[p, g] = sum over heads j < nh of A_j^T B_j over the piece's tokens, a
 // D x D matrix accumulated in fp32 and stored as bf16.  Forward: A = K, B = V of head g (nh = 1).  Backward:
 // A = Q, B = dO of the group's query heads.  Both are staged row-major and
-// read as transposed operands (the reduction runs over the tokens).
+// read as transposed operands (the reduction runs over the tokens).  The
+// staging is not overlapped inside a workgroup; three resident workgroups
+// per CU (at most 170 registers a lane, with the accumulators kept in
+// ordinary VGPRs) overlap one another's loads instead.
 template <int D>
-__global__ __launch_bounds__(256) void lin_outer_kernel(LinArgs a, int backward) {
+__global__ __launch_bounds__(256, 3) void lin_outer_kernel(LinArgs a, int backward) {
   using T = Tile<D, CH>;
   constexpr int NBD = D / 32, NB = NBD * NBD, PER = (NB + 3) / 4;
   extern __shared__ __attribute__((aligned(16))) char smem_dyn[];
