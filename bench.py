@@ -15,9 +15,12 @@ workload trees.  The host baseline times the fp64 oracle on a bounded sample
 (whole root-to-leaf paths, one query head) and scales it; the line says so.  ``--workload linear`` times the chunkwise linear-attention pass over
 the same tree instead (plan + linear forward + linear backward per step),
 with its own metric line.  ``--workload dfs`` runs the same softmax
-attention as a depth-first walk of the tree, one node per call (forward in
-preorder, accumulating backward in reverse), with the per-node plans built
-before the timed region, and reports it beside the one-call pass.  Only one
+attention as a depth-first walk of the tree (forward calls in preorder,
+accumulating backward calls in reverse), with the calls' plans built before
+the timed region, and reports it beside the one-call pass: by default each
+call takes a run of consecutive preorder nodes whose root paths fit in the
+longest root-to-leaf path (tree_attn_walk_runs), with ``--walk node`` one
+node per call.  Only one
 GPU is used; ``--gpus`` above 1 is refused.
 """
 
@@ -62,7 +65,10 @@ def _args():
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--workload", choices=["softmax", "linear", "dfs"], default="softmax",
                     help="softmax tree attention (default), chunkwise linear attention, or "
-                         "softmax tree attention as a depth-first walk, one node per call")
+                         "softmax tree attention as a depth-first walk")
+    ap.add_argument("--walk", choices=["runs", "node"], default="runs",
+                    help="depth-first walk: runs of preorder nodes within the deepest path's "
+                         "rows per call (default), or one node per call")
     return ap.parse_args()
 
 
@@ -384,12 +390,17 @@ def main_dfs(args) -> int:
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     acc = torch.empty((2, n, hkv, d), dtype=torch.float32, device=dev)
-    order = dfs_preorder(t.parent)
+    if args.walk == "node":
+        calls = [[i] for i in dfs_preorder(t.parent)]
+    else:
+        calls = ta.walk_runs(t.parent, t.seg_len)
+    log(f"walk: {len(calls)} calls ({args.walk})")
     t0 = time.perf_counter()
-    plans = [ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype, query_nodes=[i])
-             for i in order]
+    plans = [ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype, query_nodes=c)
+             for c in calls]
     torch.cuda.synchronize()
     plan_ms = 1e3 * (time.perf_counter() - t0)
+    has_limit = any(bool((p.export()["bwd_entries"][:, 3] < 0).any()) for p in plans)
     ws = torch.empty(max(p.workspace_size()[1] for p in plans), dtype=torch.uint8, device=dev)
     # split query tiles keep their key parts' partial results here
     ws_f = torch.empty(max(1, max(p.workspace_size()[0] for p in plans)), dtype=torch.uint8,
@@ -441,9 +452,11 @@ def main_dfs(args) -> int:
                  "bwd_dq": 2.0 * d * hq * pairs}
     kern_exec = {"fwd": 1.0, "bwd_dkdv": 1.0, "bwd_dq": 3.0}
     pipe = dtype == "bf16"
-    # one-node query-subset plans keep one node per run: no key-limit entries
+    # key-limit entries (key tiles crossing from a parent into the child
+    # stored after it) need the pipelined kernel's other variant
     kern_name = {"fwd": f"tree_attn_fwd_kernel<{'bf16' if pipe else 'float'}, {d}>",
-                 "bwd_dkdv": (f"tree_attn_dkdv_pipe_kernel<{d}, false>" if pipe
+                 "bwd_dkdv": (f"tree_attn_dkdv_pipe_kernel<{d}, {str(has_limit).lower()}>"
+                              if pipe
                               else f"tree_attn_dkdv_kernel<float, {d}>"),
                  "bwd_dq": f"tree_attn_dq_kernel<{'bf16' if pipe else 'float'}, {d}>"}
 
@@ -475,7 +488,9 @@ def main_dfs(args) -> int:
         "dtype": dtype,
         "data": "synthetic",
         "config": {
-            "workload": f"{spec['name']} tree, depth-first walk, one node per call",
+            "workload": f"{spec['name']} tree, depth-first walk, " + (
+                "one node per call" if args.walk == "node" else
+                f"{len(calls)} calls of preorder runs within the deepest path's rows"),
             "unique_tokens": n, "nodes": t.num_nodes, "pairs": pairs, "heads_q": hq,
             "heads_kv": hkv, "head_dim": d, "softmax_scale": scale, "global_batch": 1,
             "seq_len": st["max_path"], "parallelism": "none (1 GPU)",

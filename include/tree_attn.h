@@ -224,6 +224,32 @@ tree_attn_status_t tree_attn_bwd_noalloc(tree_attn_plan_t plan, const void* q, c
  */
 
 /*
+ * tree_attn_walk_runs -- the calls of a memory-bounded depth-first walk.
+ * The walk visits the nodes in depth-first preorder (roots, and the
+ * children of each node, in index order); what it must keep resident for a
+ * call is the rows of the root paths of the call's query nodes.  This cuts
+ * the preorder into runs of consecutive nodes, one query-subset call each:
+ * a run takes the next node while the union of its nodes' root paths holds
+ * at most `budget` tokens, and a node whose own root path is longer runs
+ * alone.  budget <= 0 means the longest root-to-leaf path's token count:
+ * then no call keeps more rows resident than the deepest call of a walk
+ * with one node per call.
+ *   parent, seg_len [num_nodes]: the node table (host memory, as in
+ *                   tree_attn_plan; segment starts play no part);
+ *   order     [num_nodes] (out): the preorder;
+ *   run_start [num_nodes + 1] (out): run r is order[run_start[r] ..
+ *                   run_start[r + 1]); run_start[num_runs] = num_nodes;
+ *   num_runs  (out): 0 for an empty table.
+ * Host memory only, owned by the caller; no GPU call.  Errors: INVALID_ARG
+ * (negative num_nodes, null pointer), BAD_TREE (a parent outside
+ * [-1, num_nodes), a node its own parent, a cycle), LAYOUT (a segment
+ * length below 1).  On error the outputs are unspecified.
+ */
+tree_attn_status_t tree_attn_walk_runs(const int32_t* parent, const int32_t* seg_len,
+                                       int32_t num_nodes, int64_t budget, int32_t* order,
+                                       int32_t* run_start, int32_t* num_runs);
+
+/*
  * tree_attn_plan_subset -- a plan whose queries are the tokens of
  * query_nodes[0 .. num_query_nodes) (node indices of the table; repeats are
  * ignored; an empty list gives a plan that does nothing).  Keys are unchanged:

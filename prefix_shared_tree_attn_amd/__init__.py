@@ -20,7 +20,8 @@ from ._ffi import TreeAttnError, PlanStats  # noqa: F401
 __all__ = ["Plan", "plan", "plan_host", "fwd", "bwd", "bwd_noalloc", "bwd_accum", "accum_cast", "positions",
            "workspace",
            "TreeAttnError", "timing_enable", "timing_read", "PrefixTree", "build_tree",
-           "gather_rows", "scatter_sum_rows", "rope", "lin_fwd", "lin_bwd", "lin_workspace"]
+           "gather_rows", "scatter_sum_rows", "rope", "lin_fwd", "lin_bwd", "lin_workspace",
+           "walk_runs"]
 
 
 def _i32(a) -> np.ndarray:
@@ -384,6 +385,24 @@ class PrefixTree:
     @property
     def num_tokens(self) -> int:
         return int(self.unique_tokens.shape[0])
+
+
+def walk_runs(parent, seg_len, budget: int = 0):
+    """tree_attn_walk_runs: the query-node lists of a memory-bounded
+    depth-first walk's calls, in preorder (budget <= 0: the longest
+    root-to-leaf path's token count)."""
+    parent, seg_len = _i32(parent).reshape(-1), _i32(seg_len).reshape(-1)
+    m = parent.shape[0]
+    if seg_len.shape[0] != m:
+        raise ValueError("parent and seg_len differ in length")
+    order = np.zeros(max(m, 1), np.int32)
+    starts = np.zeros(m + 1, np.int32)
+    runs = ctypes.c_int32(0)
+    _ffi.check(_ffi.lib().tree_attn_walk_runs(_ptr(parent), _ptr(seg_len), m, int(budget),
+                                              _ptr(order), _ptr(starts), ctypes.byref(runs)),
+               "walk_runs")
+    r = runs.value
+    return [order[starts[i]:starts[i + 1]].tolist() for i in range(r)]
 
 
 def build_tree(trajectories) -> PrefixTree:

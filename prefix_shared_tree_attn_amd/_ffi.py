@@ -27,7 +27,7 @@ EXPORTS = (
     "tree_attn_lin_fwd", "tree_attn_lin_bwd", "tree_attn_lin_plan_export",
     "tree_attn_plan_subset", "tree_attn_plan_host_subset", "tree_attn_bwd_accum",
     "tree_attn_accum_cast", "tree_attn_bwd_noalloc", "tree_attn_plan_export_split",
-    "tree_attn_lin_plan_export_chains",
+    "tree_attn_lin_plan_export_chains", "tree_attn_walk_runs",
 )
 
 
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.tree_attn_positions.argtypes = [vp, vp, vp, vp]
     i64p = ctypes.POINTER(ctypes.c_int64)
     L.tree_attn_build_tree.argtypes = [i32p, i64p, ctypes.c_int32] + [i32p] * 10
+    L.tree_attn_walk_runs.argtypes = [i32p, i32p, ctypes.c_int32, ctypes.c_int64, i32p, i32p,
+                                      i32p]
     L.tree_attn_gather_rows.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
     L.tree_attn_scatter_sum_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64,
                                              ctypes.c_int, vp]
@@ -121,7 +123,7 @@ def lib() -> ctypes.CDLL:
                "tree_attn_lin_bwd", "tree_attn_lin_plan_export", "tree_attn_plan_subset",
                "tree_attn_plan_host_subset", "tree_attn_bwd_accum", "tree_attn_accum_cast",
                "tree_attn_bwd_noalloc", "tree_attn_plan_export_split",
-               "tree_attn_lin_plan_export_chains"):
+               "tree_attn_lin_plan_export_chains", "tree_attn_walk_runs"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L

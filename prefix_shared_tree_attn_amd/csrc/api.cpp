@@ -732,6 +732,16 @@ tree_attn_status_t tree_attn_positions(tree_attn_plan_t plan, int32_t* node_id,
   return TREE_ATTN_OK;
 }
 
+tree_attn_status_t tree_attn_walk_runs(const int32_t* parent, const int32_t* seg_len,
+                                       int32_t num_nodes, int64_t budget, int32_t* order,
+                                       int32_t* run_start, int32_t* num_runs) {
+  std::string err;
+  const Status s =
+      tree_attn::walk_runs(parent, seg_len, num_nodes, budget, order, run_start, num_runs, &err);
+  if (s != Status::kOk) return report(s, err);
+  return TREE_ATTN_OK;
+}
+
 tree_attn_status_t tree_attn_build_tree(const int32_t* tokens, const int64_t* traj_offsets,
                                         int32_t num_traj, int32_t* parent, int32_t* seg_start,
                                         int32_t* seg_len, int32_t* unique_tokens,

@@ -638,4 +638,80 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
   return Status::kOk;
 }
 
+// AReaL-DTA (abstract) walks the tree depth first with one root-to-leaf path
+// resident at a time.  Nodes that follow one another in preorder share most
+// of their root paths, so several of them fit in the rows one deep path
+// needs; each run is one query-subset call of the walk.
+Status walk_runs(const int32_t* parent, const int32_t* seg_len, int32_t num_nodes,
+                 int64_t budget, int32_t* order, int32_t* run_start, int32_t* num_runs,
+                 std::string* err) {
+  if (num_nodes < 0 || !num_runs || !run_start ||
+      (num_nodes > 0 && (!parent || !seg_len || !order)))
+    return fail(err, Status::kInvalidArg, "null pointer or negative node count");
+  const int64_t m = num_nodes;
+  for (int64_t i = 0; i < m; ++i) {
+    if (parent[i] < -1 || parent[i] >= m || parent[i] == i) {
+      std::ostringstream os;
+      os << "node " << i << " has invalid parent " << parent[i];
+      return fail(err, Status::kBadTree, os.str());
+    }
+    if (seg_len[i] < 1) {
+      std::ostringstream os;
+      os << "node " << i << " has segment length " << seg_len[i];
+      return fail(err, Status::kLayout, os.str());
+    }
+  }
+  // children in index order; preorder by an explicit stack
+  std::vector<int32_t> first(m + 1, 0), kids(m);
+  for (int64_t i = 0; i < m; ++i)
+    if (parent[i] >= 0) ++first[parent[i] + 1];
+  for (int64_t i = 0; i < m; ++i) first[i + 1] += first[i];
+  {
+    std::vector<int32_t> fill(first.begin(), first.end() - 1);
+    for (int64_t i = 0; i < m; ++i)
+      if (parent[i] >= 0) kids[fill[parent[i]]++] = static_cast<int32_t>(i);
+  }
+  std::vector<int32_t> stack;
+  for (int64_t i = m - 1; i >= 0; --i)
+    if (parent[i] < 0) stack.push_back(static_cast<int32_t>(i));
+  std::vector<int64_t> path(m, 0);  // tokens on the root path, the node's own included
+  int64_t n_order = 0, longest = 0;
+  while (!stack.empty()) {
+    const int32_t v = stack.back();
+    stack.pop_back();
+    order[n_order++] = v;
+    path[v] = (parent[v] >= 0 ? path[parent[v]] : 0) + seg_len[v];
+    longest = std::max(longest, path[v]);
+    for (int32_t c = first[v + 1] - 1; c >= first[v]; --c) stack.push_back(kids[c]);
+  }
+  if (n_order != m) return fail(err, Status::kBadTree, "parent pointers contain a cycle");
+  if (budget <= 0) budget = longest;
+
+  // greedy cut: mark[v] = the run whose resident set holds v.  In preorder
+  // the resident set is closed under taking parents, so the part of a new
+  // node's root path not yet resident is the stretch below its deepest
+  // resident ancestor.
+  std::vector<int32_t> mark(m, -1);
+  int32_t runs = 0;
+  int64_t resident = 0;
+  run_start[0] = 0;
+  for (int64_t j = 0; j < m; ++j) {
+    const int32_t v = order[j];
+    int64_t add = 0;
+    for (int32_t u = v; u >= 0 && mark[u] != runs - 1; u = parent[u]) add += seg_len[u];
+    if (runs == 0 || resident + add > budget) {
+      // close the current run (if any) and open one at v
+      if (runs > 0) run_start[runs] = static_cast<int32_t>(j);
+      ++runs;
+      resident = 0;
+      add = path[v];
+    }
+    for (int32_t u = v; u >= 0 && mark[u] != runs - 1; u = parent[u]) mark[u] = runs - 1;
+    resident += add;
+  }
+  run_start[runs] = static_cast<int32_t>(m);
+  *num_runs = runs;
+  return Status::kOk;
+}
+
 }  // namespace tree_attn

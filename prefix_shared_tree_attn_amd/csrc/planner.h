@@ -122,4 +122,16 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
                   HostPlan* out, std::string* err, const int32_t* query_nodes = nullptr,
                   int32_t num_query_nodes = 0);
 
+// The calls of a memory-bounded depth-first walk: the nodes in preorder
+// (roots, and each node's children, in index order) in order[num_nodes], cut
+// into runs of consecutive nodes, run r = order[run_start[r] ..
+// run_start[r + 1]), *num_runs of them.  A run takes the next node while the
+// union of its nodes' root paths holds at most `budget` tokens; a node whose
+// own root path is longer starts a run and closes it.  budget <= 0: the
+// longest root-to-leaf path's token count.  Checks parents (kBadTree) and
+// segment lengths (kLayout) only.
+Status walk_runs(const int32_t* parent, const int32_t* seg_len, int32_t num_nodes,
+                 int64_t budget, int32_t* order, int32_t* run_start, int32_t* num_runs,
+                 std::string* err);
+
 }  // namespace tree_attn

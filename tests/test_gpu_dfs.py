@@ -25,14 +25,16 @@ from gpu_util import FP32_LSE_ABS, FP32_REL_L2, LSE_ABS, REL_L2, device_inputs, 
 pytestmark = pytest.mark.gpu
 
 
-def _walk(t, dev, hq, hkv, d, dtype, scale):
-    """Depth-first walk, one node per call; returns device outputs."""
+def _walk(t, dev, hq, hkv, d, dtype, scale, calls=None):
+    """Depth-first walk, one node per call unless ``calls`` lists the query
+    nodes of each call (in walk order); returns device outputs."""
     import torch
     import prefix_shared_tree_attn_amd as ta
     n = t.num_tokens
-    order = dfs_preorder(t.parent)
-    plans = [ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype, query_nodes=[i])
-             for i in order]
+    if calls is None:
+        calls = [[i] for i in dfs_preorder(t.parent)]
+    plans = [ta.plan(t.parent, t.seg_start, t.seg_len, n, hq, hkv, d, dtype, query_nodes=c)
+             for c in calls]
     tdt = dev["q"].dtype
     o = torch.empty((n, hq, d), dtype=tdt, device="cuda")
     lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
@@ -103,6 +105,33 @@ def test_depth_first_walk_equals_whole_tree(name):
     for k in ("o", "dq", "dk", "dv"):
         assert rel_l2(_host(got[k]), _host(whole[k])) <= close, k
     assert float((got["lse"] - whole["lse"]).abs().max()) <= 1e-4
+
+
+@pytest.mark.parametrize("name,budget", [(name, 0) for name in WALK_CASES] +
+                         [("forest", 400), ("binary-ragged", 300)])
+def test_walk_in_runs_equals_whole_tree(name, budget):
+    """The walk with one call per run of preorder nodes (tree_attn_walk_runs;
+    budget 0: the deepest root path's rows).  A run holding a parent and the
+    child stored after it has query tiles and key tiles that cross the node
+    boundary (key-limit entries on the backward side)."""
+    import prefix_shared_tree_attn_amd as ta
+    t, hq, hkv, d, dtype = WALK_CASES[name]
+    scale = 1.0 / np.sqrt(d)
+    calls = ta.walk_runs(t.parent, t.seg_len, budget)
+    print(f"case {name}: N={t.num_tokens} nodes={t.num_nodes} budget={budget} "
+          f"runs={[len(c) for c in calls]}", flush=True)
+    assert len(calls) < t.num_nodes  # some run holds several nodes
+    x = make(t, hq, hkv, d, dtype, do_std=1.0 if dtype == "fp32" else 1e-2)
+    dev = device_inputs(x, dtype)
+    got = _walk(t, dev, hq, hkv, d, dtype, scale, calls)
+    ref = oracle.tree_attention(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len, scale)
+    errs = {k: rel_l2(_host(got[k]), ref[k]) for k in ("o", "dq", "dk", "dv")}
+    errs["lse"] = float(np.abs(_host(got["lse"]) - ref["lse"]).max())
+    print("errors:", errs, flush=True)
+    rel_bar, lse_bar = (FP32_REL_L2, FP32_LSE_ABS) if dtype == "fp32" else (REL_L2, LSE_ABS)
+    for k in ("o", "dq", "dk", "dv"):
+        assert errs[k] <= rel_bar, (k, errs)
+    assert errs["lse"] <= lse_bar
 
 
 def test_one_call_on_a_node_subset():
@@ -188,21 +217,25 @@ def test_plan_kind_checks_and_empty_subset():
         p.close()
 
 
-@pytest.mark.parametrize("cfg", [2, 4])
-def test_full_size_walk(cfg):
-    """The GRPO-star (17 nodes) and segment-search (127 nodes) workloads at
-    full size, one node per call: sampled rows and keys against the oracle,
-    whole tensors against the one-call path to rounding (the walk's query
-    tiles are the one call's on these trees, every node a multiple of 128
-    tokens, but a one-node call cuts their keys into parts)."""
+@pytest.mark.parametrize("cfg,walk", [(2, "node"), (4, "node"), (3, "runs"), (4, "runs")])
+def test_full_size_walk(cfg, walk):
+    """The GRPO-star (17 nodes), agent (config 3) and segment-search (127
+    nodes) workloads at full size, one node per call or one run of preorder
+    nodes per call (tree_attn_walk_runs): sampled rows and keys against the
+    oracle, whole tensors against the one-call path to rounding (a walk's
+    call has fewer query tiles than the one call, so the planner may cut
+    their keys into parts)."""
     import torch
+    import prefix_shared_tree_attn_amd as ta
     t = config_tree(cfg)
     sp = config_spec(cfg)
     hq, hkv, d, dtype, scale = sp["heads_q"], sp["heads_kv"], sp["head_dim"], sp["dtype"], sp["scale"]
-    print(f"config {cfg} walk: N={t.num_tokens} nodes={t.num_nodes}", flush=True)
+    calls = ta.walk_runs(t.parent, t.seg_len) if walk == "runs" else None
+    print(f"config {cfg} walk ({walk}): N={t.num_tokens} nodes={t.num_nodes} "
+          f"calls={len(calls) if calls else t.num_nodes}", flush=True)
     x = make(t, hq, hkv, d, dtype, do_std=sp["do_std"])
     dev = device_inputs(x, dtype)
-    got = _walk(t, dev, hq, hkv, d, dtype, scale)
+    got = _walk(t, dev, hq, hkv, d, dtype, scale, calls)
     print("walk done", flush=True)
     whole = _whole(t, dev, hq, hkv, d, dtype, scale)
     for k in ("o", "dq", "dk", "dv"):
@@ -214,7 +247,7 @@ def test_full_size_walk(cfg):
     rows = sorted(set([0, t.num_tokens - 1] + [int(r) for r in rng.integers(0, t.num_tokens, 10)]))
     heads = [int(rng.integers(0, hq))]
     g = heads[0] // (hq // hkv)
-    prompt = int(t.seg_len[0])  # node 0 is the root on both trees
+    prompt = int(t.seg_len[0])  # node 0 is the root, stored first, on these trees
     keys = [0, prompt - 1, prompt + 5, t.num_tokens - 1]
     o, lse, dq = oracle.query_rows(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len, scale,
                                    rows, heads)

@@ -15,7 +15,7 @@ import pytest
 import prefix_shared_tree_attn_amd as ta
 from prefix_shared_tree_attn_amd import _ffi
 from tree_inputs import (NodeTable, binary_tree, caterpillar_tree, chain_tree, config_tree,
-                         random_tree, star_tree, tree_stats)
+                         dfs_preorder, random_tree, star_tree, tree_stats)
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tree_attn.h")
 
@@ -525,3 +525,122 @@ def test_large_plans_do_not_split_forward_tiles():
         assert st["fwd_split_tiles"] == 0 and st["fwd_slots"] == 0
         assert np.all(ex["fwd_part"] == -1)
         assert p.workspace_size()[0] == 0
+
+
+# ---- runs of a memory-bounded depth-first walk (tree_attn_walk_runs)
+
+def _root_path(parent, v):
+    s = set()
+    while v >= 0:
+        s.add(int(v))
+        v = int(parent[v])
+    return s
+
+
+def _greedy_runs(parent, seg_len, budget):
+    """The cut written out with sets: walk the preorder, keep the union of
+    the current run's root paths, and open a new run when the next node's
+    path would take it past the budget."""
+    order = dfs_preorder(parent)
+    tok = lambda nodes: sum(int(seg_len[u]) for u in nodes)
+    if budget <= 0:
+        budget = max((tok(_root_path(parent, v)) for v in order), default=0)
+    runs, cur, res = [], [], set()
+    for v in order:
+        grown = res | _root_path(parent, v)
+        if cur and tok(grown) > budget:
+            runs.append(cur)
+            cur, res = [v], _root_path(parent, v)
+        else:
+            cur.append(v)
+            res = grown
+    if cur:
+        runs.append(cur)
+    return runs, budget
+
+
+def _walk_trees():
+    rng = np.random.default_rng(77)
+    trees = [("chain", chain_tree([5, 1, 9])), ("star", star_tree(300, 5, 257)),
+             ("binary", binary_tree(129, 97, 3)),
+             ("caterpillar", caterpillar_tree([1 + (7 * i) % 3 for i in range(40)], 5))]
+    for i in range(12):
+        trees.append((f"random-{i}", random_tree(rng, int(rng.integers(1, 40)),
+                                                 max_len=int(rng.choice([3, 50, 400])), min_len=1,
+                                                 n_roots=int(rng.integers(1, 4)),
+                                                 shuffle=bool(i % 2))))
+    trees += [(f"config-{c}", config_tree(c)) for c in (2, 3, 4, 5)]
+    return trees
+
+
+WALK_TREES = _walk_trees()
+
+
+@pytest.mark.parametrize("idx", range(len(WALK_TREES)))
+def test_walk_runs_follow_the_greedy_cut(idx):
+    name, t = WALK_TREES[idx]
+    seg = np.asarray(t.seg_len)
+    longest = max(sum(int(seg[u]) for u in _root_path(t.parent, v)) for v in range(t.num_nodes))
+    for budget in (0, 1, longest // 2, longest, 3 * longest, 1 << 40):
+        got = ta.walk_runs(t.parent, t.seg_len, budget)
+        want, used = _greedy_runs(t.parent, t.seg_len, budget)
+        assert got == want, (name, budget)
+        # a partition of the preorder into consecutive runs
+        assert [v for r in got for v in r] == dfs_preorder(t.parent)
+        for r in got:
+            res = set().union(*(_root_path(t.parent, v) for v in r))
+            rt = sum(int(seg[u]) for u in res)
+            # within the budget, or one node whose own path is longer
+            assert rt <= used or len(r) == 1, (name, budget, r)
+        # no two neighbouring runs could have been one
+        for a, b in zip(got, got[1:]):
+            res = set().union(*(_root_path(t.parent, v) for v in a + b[:1]))
+            assert sum(int(seg[u]) for u in res) > used
+    # the default budget keeps a run's resident rows within the deepest path
+    assert _greedy_runs(t.parent, t.seg_len, 0)[1] == longest
+    assert len(ta.walk_runs(t.parent, t.seg_len, 1)) == t.num_nodes
+    assert len(ta.walk_runs(t.parent, t.seg_len, 1 << 40)) == 1
+
+
+def test_walk_runs_on_the_grpo_star():
+    """Prompt and first response fill the deepest path; every later
+    response shares the prompt and runs on its own."""
+    t = config_tree(2)
+    runs = ta.walk_runs(t.parent, t.seg_len)
+    assert runs[0] == [0, 1] and all(len(r) == 1 for r in runs[1:])
+    assert len(runs) == t.num_nodes - 1
+
+
+@pytest.mark.parametrize("parent,seg_len,status", [
+    ([1, 0], [2, 3], "BAD_TREE"),        # a cycle
+    ([-1, 5], [2, 3], "BAD_TREE"),       # parent out of range
+    ([-1, 1], [2, 3], "BAD_TREE"),       # its own parent
+    ([-2, 0], [2, 3], "BAD_TREE"),
+    ([-1, 0], [2, 0], "LAYOUT"),         # an empty segment
+])
+def test_walk_runs_rejects_bad_tables(parent, seg_len, status):
+    with pytest.raises(ta.TreeAttnError) as ei:
+        ta.walk_runs(parent, seg_len)
+    assert ei.value.status == status
+
+
+def test_walk_runs_raw_abi():
+    lib = _ffi.lib()
+    two = (ctypes.c_int32 * 2)(-1, 0)
+    lens = (ctypes.c_int32 * 2)(4, 4)
+    order = (ctypes.c_int32 * 2)()
+    starts = (ctypes.c_int32 * 3)()
+    runs = ctypes.c_int32(-1)
+    st = lib.tree_attn_walk_runs(None, lens, 2, 0, order, starts, ctypes.byref(runs))
+    assert _ffi.STATUS[st] == "INVALID_ARG"
+    st = lib.tree_attn_walk_runs(two, lens, -1, 0, order, starts, ctypes.byref(runs))
+    assert _ffi.STATUS[st] == "INVALID_ARG"
+    st = lib.tree_attn_walk_runs(two, lens, 2, 0, order, starts, None)
+    assert _ffi.STATUS[st] == "INVALID_ARG"
+    st = lib.tree_attn_walk_runs(two, lens, 2, 0, order, starts, ctypes.byref(runs))
+    assert _ffi.STATUS[st] == "OK" and runs.value == 1
+    assert list(order) == [0, 1] and list(starts)[:2] == [0, 2]
+    # an empty table: no runs
+    st = lib.tree_attn_walk_runs(None, None, 0, 0, None, starts, ctypes.byref(runs))
+    assert _ffi.STATUS[st] == "OK" and runs.value == 0 and starts[0] == 0
+    assert ta.walk_runs([], []) == []
