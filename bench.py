@@ -43,7 +43,7 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_FP32_TFLOPS = 157.3    # dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0
 METRIC = "tree-attn fwd+bwd unique tokens/s and TFLOP/s (% of bf16 MFMA peak), 1 GPU"
-DFS_METRIC = ("tree-attn fwd+bwd unique tokens/s, depth-first walk (one node per call, "
+DFS_METRIC = ("tree-attn fwd+bwd unique tokens/s, depth-first walk (query-subset calls, "
               "accumulated K/V gradients), 1 GPU")
 LIN_METRIC = "tree linear-attn fwd+bwd unique tokens/s (chunkwise, state handoffs), 1 GPU"
 LIN_CHUNK = 64

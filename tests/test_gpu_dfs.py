@@ -2,13 +2,14 @@
 accumulating backward and the final cast, through the C ABI.
 
 A depth-first walk (AReaL-DTA, abstract: one root-to-leaf path resident at a
-time, each shared prefix computed once) runs one forward call per node in
-preorder and one accumulating backward call per node in reverse preorder.
-Summed over the walk, the results must be the whole tree's: checked against
-the fp64 oracle (whole tensors on small trees, sampled rows and keys on the
-GRPO-star and segment-search workloads at full size) and against the
-one-call library path, to rounding: a one-node call has few query tiles, so
-the planner cuts their keys into parts that run side by side and merges the
+time, each shared prefix computed once) runs forward calls in preorder and
+accumulating backward calls in reverse order, one node per call or one run
+of preorder nodes per call (tree_attn_walk_runs).  Summed over the walk,
+the results must be the whole tree's: checked against the fp64 oracle
+(whole tensors on small trees, sampled rows and keys on the GRPO-star,
+agent and segment-search workloads at full size) and against the one-call
+library path, to rounding: a walk's call has few query tiles, so the
+planner cuts their keys into parts that run side by side and merges the
 parts' partial results, where the whole-tree pass may not (another
 summation order, then one rounding).  One call on a
 random set of nodes is checked against ``oracle.tree_attention_subset``.
