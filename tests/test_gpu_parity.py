@@ -258,6 +258,38 @@ def _sample_keys(t: NodeTable, rng, cfg: int):
     return sorted(set(keys))
 
 
+def _closed_forms(got, dev, hq, hkv):
+    """Closed forms over whole tensors, in fp64 on the device: every softmax
+    row sums to one and is shift invariant, so per kv group sum dV = sum dO
+    over the group's heads and sum dK = 0; scores depend on q.k only, so
+    <dQ, Q> = <dK, K>."""
+    import torch
+    gs = hq // hkv
+    for gg in range(hkv):
+        want = dev["do"][:, gg * gs:(gg + 1) * gs].double().sum((0, 1))
+        have = got["dv"][:, gg].double().sum(0)
+        assert float((have - want).norm() / want.norm()) <= REL_L2
+        dkg = got["dk"][:, gg].double()
+        assert float(dkg.sum(0).norm()) <= 1e-2 * float(dkg.norm())
+    # <dQ, Q> = <dK, K> cancels heavily; each bf16 output element carries a
+    # rounding error of up to 2^-9 relative, so the two sums may differ by a
+    # few standard deviations u / sqrt(3) * ||x * y||_2 of that noise
+    lhs = rhs = n_l = n_r = 0.0
+    for h in range(hq):
+        pr = got["dq"][:, h].double() * dev["q"][:, h].double()
+        lhs += float(pr.sum())
+        n_l += float((pr * pr).sum())
+    for g_ in range(hkv):
+        pr = got["dk"][:, g_].double() * dev["k"][:, g_].double()
+        rhs += float(pr.sum())
+        n_r += float((pr * pr).sum())
+    noise = (2.0 ** -9 / np.sqrt(3.0)) * np.sqrt(n_l + n_r)
+    print(f"<dQ,Q>={lhs:.6e} <dK,K>={rhs:.6e} rounding-noise std={noise:.3e}", flush=True)
+    assert abs(lhs - rhs) <= 6.0 * noise + 1e-2 * max(abs(lhs), abs(rhs))
+    for name in ("o", "dq", "dk", "dv", "lse"):
+        assert bool(torch.isfinite(got[name]).all()), name
+
+
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_full_size_sampled(cfg):
     import torch
@@ -295,33 +327,48 @@ def test_full_size_sampled(cfg):
           f"dv={e_dv:.2e}", flush=True)
     assert max(e_o, e_dq, e_dk, e_dv) <= REL_L2
     assert e_lse <= LSE_ABS
-    # closed forms over whole tensors, in fp64 on the device: every softmax
-    # row sums to one and is shift invariant; scores depend on q.k only
-    gs = hq // hkv
-    for gg in range(hkv):
-        want = dev["do"][:, gg * gs:(gg + 1) * gs].double().sum((0, 1))
-        have = got["dv"][:, gg].double().sum(0)
-        assert float((have - want).norm() / want.norm()) <= REL_L2
-        dkg = got["dk"][:, gg].double()
-        assert float(dkg.sum(0).norm()) <= 1e-2 * float(dkg.norm())
-    # <dQ, Q> = <dK, K> cancels heavily; each bf16 output element carries a
-    # rounding error of up to 2^-9 relative, so the two sums may differ by a
-    # few standard deviations u / sqrt(3) * ||x * y||_2 of that noise
-    lhs = rhs = n_l = n_r = 0.0
-    for h in range(hq):
-        pr = got["dq"][:, h].double() * dev["q"][:, h].double()
-        lhs += float(pr.sum())
-        n_l += float((pr * pr).sum())
-    for g_ in range(hkv):
-        pr = got["dk"][:, g_].double() * dev["k"][:, g_].double()
-        rhs += float(pr.sum())
-        n_r += float((pr * pr).sum())
-    noise = (2.0 ** -9 / np.sqrt(3.0)) * np.sqrt(n_l + n_r)
-    print(f"<dQ,Q>={lhs:.6e} <dK,K>={rhs:.6e} rounding-noise std={noise:.3e}", flush=True)
-    assert abs(lhs - rhs) <= 6.0 * noise + 1e-2 * max(abs(lhs), abs(rhs))
-    for name in ("o", "dq", "dk", "dv", "lse"):
-        assert bool(torch.isfinite(got[name]).all()), name
+    _closed_forms(got, dev, hq, hkv)
     _check_split_tiles(cfg, t, x, got)
+
+
+def test_deep_chain_sampled():
+    """One 98,304-token chain (2 query heads on one kv head, D 128, bf16):
+    its last rows attend to 2.8 times as many keys as the deepest row of the
+    workload trees (1,536 key steps for a query tile, the online softmax
+    carried across all of them), and most of its key tiles split into
+    partial slots.  Sampled rows, the last included, and keys of the last
+    1,024 positions against the oracle; whole-tensor closed forms for the
+    rest."""
+    import torch
+    from gpu_util import run_library_device
+    n, hq, hkv, d = 98304, 2, 1, 128
+    scale = 1.0 / np.sqrt(d)
+    t = chain_tree([n])
+    x = make(t, hq, hkv, d, "bf16")
+    print(f"deep chain: N={n} hq={hq} hkv={hkv} d={d}", flush=True)
+    got, dev = run_library_device(t, x, hq, hkv, d, "bf16", scale)
+    print("library done", flush=True)
+    rng = np.random.default_rng(11)
+    rows = sorted(set([0, 1, 4095, n - 1] + [int(r) for r in rng.integers(0, n, 8)]))
+    heads = [0, 1]
+    keys = [n - 1024, n - 700, n - 129, n - 128, n - 2, n - 1]
+    ri, hi, ki = (torch.tensor(a, device="cuda") for a in (rows, heads, keys))
+    o, lse, dq = oracle.query_rows(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len,
+                                   scale, rows, heads)
+    print("oracle rows done", flush=True)
+    dk, dv = oracle.key_rows(x.q, x.k, x.v, x.do, t.parent, t.seg_start, t.seg_len, scale,
+                             keys, 0, row_block=256)
+    print("oracle keys done", flush=True)
+    errs = {"o": rel_l2(got["o"][ri][:, hi].double().cpu().numpy(), o),
+            "dq": rel_l2(got["dq"][ri][:, hi].double().cpu().numpy(), dq),
+            "dk": rel_l2(got["dk"][ki, 0].double().cpu().numpy(), dk),
+            "dv": rel_l2(got["dv"][ki, 0].double().cpu().numpy(), dv),
+            "lse": float(np.abs(got["lse"][hi][:, ri].double().cpu().numpy() - lse).max())}
+    print("sampled errors:", errs, flush=True)
+    for k in ("o", "dq", "dk", "dv"):
+        assert errs[k] <= REL_L2, (k, errs)
+    assert errs["lse"] <= LSE_ABS
+    _closed_forms(got, dev, hq, hkv)
 
 
 def _split_slots(t: NodeTable, sp, key: int, g: int):
