@@ -264,6 +264,17 @@ def main_linear(args) -> int:
         p.close()
     plans.clear()
     log(f"timed {args.steps} steps: {wall:.3f} s")
+    # the same steps again without the per-kernel events (a few microseconds
+    # per launch), for reference
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_plain = time.perf_counter() - t0
+    for p in plans:
+        p.close()
+    plans.clear()
     if args.copy_probe_mib > 0:
         nb = args.copy_probe_mib << 20
         a = torch.ones(nb // 4, dtype=torch.float32, device=dev)
@@ -328,6 +339,7 @@ def main_linear(args) -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_without_events": 1e3 * wall_plain / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -433,14 +445,19 @@ def main_dfs(args) -> int:
     for _ in range(args.warmup):
         walk()
         one_call()
+    # both passes timed without per-kernel events (each event pair costs a
+    # few microseconds per launch, which a walk of many small calls would
+    # feel); the per-kernel split comes from a second, instrumented walk
     ms_one = timed(one_call, args.steps)
     log(f"one call: {ms_one:.3f} ms")
+    ms_step = timed(walk, args.steps)
+    log(f"walk: {ms_step:.3f} ms")
     ta.timing_read(reset=True)
     ta.timing_enable(True)
-    ms_step = timed(walk, args.steps)
+    ms_events = timed(walk, args.steps)
     ta.timing_enable(False)
     kt = ta.timing_read(reset=True)
-    log(f"walk: {ms_step:.3f} ms")
+    log(f"walk with per-kernel events: {ms_events:.3f} ms")
     for p in plans + [whole]:
         p.close()
 
@@ -499,6 +516,7 @@ def main_dfs(args) -> int:
         "frac_of_peak": step_flop / (ms_step * 1e-3) / 1e12 / peak,
         "one_call_ms": ms_one,
         "walk_over_one_call": ms_step / ms_one,
+        "ms_per_step_with_events": ms_events,
         "plans_ms_host": plan_ms,
         "kernels_ms_per_step": {kk: kt[kk]["total_ms"] / args.steps for kk in kt
                                 if kt[kk]["launches"]},
@@ -667,6 +685,17 @@ def main() -> int:
         p.close()
     plans.clear()
     log(f"timed {args.steps} steps: {wall:.3f} s")
+    # the same steps again without the per-kernel events (a few microseconds
+    # per launch), for reference
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_plain = time.perf_counter() - t0
+    for p in plans:
+        p.close()
+    plans.clear()
 
     if args.copy_probe_mib > 0:
         # a plain elementwise kernel of known traffic, to calibrate HBM byte
@@ -733,6 +762,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_without_events": 1e3 * wall_plain / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
