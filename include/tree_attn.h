@@ -29,6 +29,14 @@
  *   never frees or retains them past the call.  Calls enqueue work on the
  *   given HIP stream and return without synchronising; kernel faults surface
  *   at the caller's next synchronisation.
+ *   Graph capture: with timing off (tree_attn_timing_enable), the passes on
+ *   an existing plan -- tree_attn_fwd, tree_attn_bwd, tree_attn_bwd_accum,
+ *   tree_attn_accum_cast and their linear-attention counterparts -- enqueue
+ *   only kernel launches on `stream`: no allocation, copy, memset or host
+ *   synchronisation.  They may therefore be recorded into a HIP graph while
+ *   `stream` is capturing, and each replay reruns the same kernels on the
+ *   same buffers.  Creating or destroying a plan allocates, copies and
+ *   frees, and stays outside any capture.
  *
  * Errors: every entry point returns a tree_attn_status_t.  Invalid arguments
  * are rejected before any device work is enqueued; the reason is available
