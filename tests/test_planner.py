@@ -644,3 +644,96 @@ def test_walk_runs_raw_abi():
     st = lib.tree_attn_walk_runs(None, None, 0, 0, None, starts, ctypes.byref(runs))
     assert _ffi.STATUS[st] == "OK" and runs.value == 0 and starts[0] == 0
     assert ta.walk_runs([], []) == []
+
+
+# ---- randomised coverage: forests, query subsets, CU counts
+
+def _visible_matrix(t: NodeTable, rows_mask):
+    """V[q, key] = 1 where query row q (a row of a listed node) sees key."""
+    n = t.num_tokens
+    node_of = np.empty(n, np.int64)
+    for i in range(t.num_nodes):
+        node_of[t.seg_start[i]:t.seg_start[i] + t.seg_len[i]] = i
+    v = np.zeros((n, n), np.int32)
+    for q in np.nonzero(rows_mask)[0]:
+        nd = int(node_of[q])
+        a = int(t.parent[nd])
+        while a >= 0:
+            v[q, t.seg_start[a]:t.seg_start[a] + t.seg_len[a]] = 1
+            a = int(t.parent[a])
+        v[q, t.seg_start[nd]:q + 1] = 1
+    return v
+
+
+def _check_cover(t: NodeTable, hq, hkv, num_cus, query_nodes):
+    n = t.num_tokens
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, n, hq, hkv, 64, "bf16", num_cus=num_cus,
+                     query_nodes=query_nodes)
+    ex = p.export()
+    rows = np.zeros(n, bool)
+    for i in (range(t.num_nodes) if query_nodes is None else query_nodes):
+        rows[t.seg_start[i]:t.seg_start[i] + t.seg_len[i]] = True
+    vis = _visible_matrix(t, rows)
+    fwd = np.zeros((n, n), np.int32)
+    for q0, q1, rb, re_ in ex["fwd_tiles"]:
+        for k0, k1, causal, _ in ex["fwd_ranges"][rb:re_]:
+            blk = np.ones((q1 - q0, k1 - k0), np.int32)
+            if causal:
+                blk = (np.arange(k0, k1)[None, :] <= np.arange(q0, q1)[:, None]).astype(np.int32)
+            fwd[q0:q1, k0:k1] += blk
+    assert np.array_equal(fwd, vis), np.argwhere(fwd != vis)[:5]
+    bwd = np.zeros((hq, n, n), np.int32)
+    for it in ex["bwd_items"]:
+        k0, k1, g, eb, ee = it[:5]
+        for h, q0, q1, mask in ex["bwd_entries"][eb:ee]:
+            assert h // (hq // hkv) == g
+            ke = min(k1, -int(mask) - 1) if mask < 0 else k1
+            if ke <= k0 or q1 <= q0:
+                continue
+            blk = np.ones((q1 - q0, ke - k0), np.int32)
+            if mask == 1:
+                blk = (np.arange(k0, ke)[None, :] <= np.arange(q0, q1)[:, None]).astype(np.int32)
+            bwd[h, q0:q1, k0:ke] += blk
+    for h in range(hq):
+        assert np.array_equal(bwd[h], vis), (h, np.argwhere(bwd[h] != vis)[:5])
+    split = p.stats()["fwd_split_tiles"]
+    assert p.stats()["pairs"] == int(vis.sum())
+    p.close()
+    return split
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_plans_cover_every_visible_pair_once(seed):
+    """Seeded random forests and caterpillars (packed depth first or in a
+    random order), 1-24 query heads on 1-4 kv heads, 1-256 CUs, and the
+    whole tree, no node or a random set of query nodes: every (query row,
+    key) pair that a listed row sees is in exactly one forward tile (key
+    parts of split tiles included) and, for every head, in exactly one
+    backward item, and in no other."""
+    rng = np.random.default_rng(900 + seed)
+    for _ in range(60):
+        if rng.random() < 0.15:
+            t = caterpillar_tree([int(x) for x in rng.integers(1, 30, int(rng.integers(2, 30)))],
+                                 int(rng.integers(1, 150)))
+        else:
+            t = random_tree(rng, int(rng.integers(1, 25)),
+                            max_len=int(rng.choice([5, 60, 300])), min_len=1,
+                            n_roots=int(rng.integers(1, 4)), shuffle=bool(rng.random() < 0.5))
+        hkv = int(rng.choice([1, 2, 4]))
+        hq = hkv * int(rng.choice([1, 2, 3, 6]))
+        r = rng.random()
+        qn = None if r < 0.3 else [] if r < 0.4 else sorted(
+            set(int(x) for x in rng.integers(0, t.num_nodes, int(rng.integers(1, t.num_nodes + 1)))))
+        _check_cover(t, hq, hkv, int(rng.choice([1, 4, 16, 256])), qn)
+
+
+@pytest.mark.parametrize("t,query_nodes", [
+    (chain_tree([3500, 300]), None),
+    (chain_tree([3300]), [0]),
+    (star_tree(3200, 3, 200), [0, 2]),
+    (caterpillar_tree([1200, 1100, 1000, 900], 150), None),
+])
+def test_key_parts_cover_every_visible_pair_once(t, query_nodes):
+    """Few query tiles for 256 CUs, long enough to be cut into key parts: the
+    parts' key ranges together still cover each visible pair exactly once."""
+    assert _check_cover(t, 2, 1, 256, query_nodes) > 0
