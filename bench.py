@@ -72,6 +72,20 @@ def _args():
     return ap.parse_args()
 
 
+def _inputs_sha256(t, x, dtype: str) -> str:
+    """SHA-256 over the node table (parent, seg_start, seg_len as int32) and
+    the Q, K, V, dO tensors exactly as uploaded (bf16 bit patterns, or fp32),
+    so that a run's inputs can be checked against a regeneration from the
+    seeds."""
+    h = hashlib.sha256()
+    for a in (t.parent, t.seg_start, t.seg_len):
+        h.update(np.ascontiguousarray(a, np.int32).tobytes())
+    for name in ("q", "k", "v", "do"):
+        a = x.bits[name] if dtype == "bf16" else getattr(x, name)
+        h.update(memoryview(np.ascontiguousarray(a)).cast("B"))
+    return h.hexdigest()
+
+
 def _traffic_from_profile(kernel: str, workload: str):
     """HBM bytes per launch of a kernel from the committed counter summary,
     if it was taken on the current kernel sources."""
@@ -609,6 +623,7 @@ def main() -> int:
     import torch
     import prefix_shared_tree_attn_amd as ta
     from tree_inputs import config_spec, config_tree, make_inputs, tree_stats
+    from tree_inputs.tensors import SEEDS as INPUT_SEEDS
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -625,6 +640,7 @@ def main() -> int:
 
     x = make_inputs(n, hq, hkv, d, dtype=dtype, do_std=spec["do_std"])
     log("inputs generated")
+    inputs_sha = _inputs_sha256(t, x, dtype)
 
     def up(name):
         if dtype == "bf16":
@@ -779,6 +795,8 @@ def main() -> int:
             "heads_q": hq, "heads_kv": hkv, "head_dim": d, "softmax_scale": scale,
             "global_batch": 1, "seq_len": st["max_path"], "parallelism": "none (1 GPU)",
         },
+        "inputs": {"tensor_seeds": dict(INPUT_SEEDS), "tree_seed": 0,
+                   "sha256": inputs_sha},
         "tflops": tflops,
         "frac_of_peak": tflops / peak,
         "dense_per_path_flop_ratio": st["dense_ratio"],

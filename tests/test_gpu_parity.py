@@ -33,11 +33,31 @@ def _compare_full(t: NodeTable, hq, hkv, d, dtype, scale=None, do_std=1e-2, seed
     errs = {k: rel_l2(got[k], ref[k], zero.get(k, 0.0)) for k in ("o", "dq", "dk", "dv")}
     errs["lse"] = float(np.abs(got["lse"] - ref["lse"]).max())
     print("errors:", errs, flush=True)
+    _per_node(t, got, ref)
     rel_bar, lse_bar = (FP32_REL_L2, FP32_LSE_ABS) if dtype == "fp32" else (REL_L2, LSE_ABS)
     for k in ("o", "dq", "dk", "dv"):
         assert errs[k] <= rel_bar, (k, errs)
     assert errs["lse"] <= lse_bar, errs
     return errs
+
+
+def _per_node(t: NodeTable, got, ref):
+    """Diagnostic only: the node with the largest relative L2 error of each
+    output over that node's rows (a wrong ancestor list or branch sum shows
+    up on one node long before it moves the whole-tensor error)."""
+    worst = {}
+    for k in ("o", "dq", "dk", "dv"):
+        e_max, n_max = 0.0, -1
+        for i in range(t.num_nodes):
+            r0, r1 = int(t.seg_start[i]), int(t.seg_start[i] + t.seg_len[i])
+            den = float(np.linalg.norm(ref[k][r0:r1]))
+            if den == 0.0:
+                continue
+            e = float(np.linalg.norm(np.asarray(got[k][r0:r1], np.float64) - ref[k][r0:r1])) / den
+            if e > e_max:
+                e_max, n_max = e, i
+        worst[k] = (n_max, round(e_max, 6))
+    print("worst node per output (node, rel-L2):", worst, flush=True)
 
 
 def _random(seed, nodes, max_len, roots=1):

@@ -737,3 +737,57 @@ def test_key_parts_cover_every_visible_pair_once(t, query_nodes):
     """Few query tiles for 256 CUs, long enough to be cut into key parts: the
     parts' key ranges together still cover each visible pair exactly once."""
     assert _check_cover(t, 2, 1, 256, query_nodes) > 0
+
+
+# ---- longest-first order and the split cap
+
+def _fwd_costs(ex):
+    """Cost of each forward tile in launch order: rows x keys of its ranges
+    (the causal range counted whole), the planner's sort key."""
+    out = []
+    for q0, q1, rb, re_ in ex["fwd_tiles"]:
+        keys = sum(int(k1 - k0) for k0, k1, _, _ in ex["fwd_ranges"][rb:re_])
+        out.append(int(q1 - q0) * keys)
+    return np.array(out, np.int64)
+
+
+def _bwd_costs(ex):
+    """Cost of each backward item in launch order (rows x keys over its
+    entries); XCD of each item (-1 for the empty items that pad queues)."""
+    cost, xcd = [], []
+    for it in ex["bwd_items"]:
+        k0, k1, g, eb, ee, slot, x = (int(v) for v in it[:7])
+        cost.append(sum(int(q1 - q0) * (k1 - k0) for _, q0, q1, _ in ex["bwd_entries"][eb:ee]))
+        xcd.append(x)
+    return np.array(cost, np.int64), np.array(xcd)
+
+
+@pytest.mark.parametrize("t", [config_tree(c) for c in (2, 3, 4, 5)] +
+                         [random_tree(np.random.default_rng(s), 30, max_len=700, n_roots=2)
+                          for s in range(3)])
+def test_longest_first_order_and_split_cap(t):
+    """Forward tiles run longest first.  No backward item exceeds the split
+    cap, max(total / (8 num_cus), 128 * 32 * 64), by more than the 32-row
+    rounding of its last chunk.  Items go to XCD b % 8 in launch order, and
+    the last 40% of each XCD's work runs longest first, so that every XCD
+    ends on its shortest items."""
+    hq, hkv, ncus = 8, 2, 256
+    p = ta.plan_host(t.parent, t.seg_start, t.seg_len, t.num_tokens, hq, hkv, 128, "bf16",
+                     num_cus=ncus)
+    ex = p.export()
+    fc = _fwd_costs(ex)
+    if p.stats()["fwd_split_tiles"] == 0:
+        assert np.all(fc[:-1] >= fc[1:])
+    bc, xcd = _bwd_costs(ex)
+    total = int(bc.sum())
+    cap = max(total // (8 * ncus), 128 * 32 * 64)
+    assert int(bc.max()) <= cap + 32 * 128
+    assert np.array_equal(xcd[xcd >= 0], (np.arange(len(xcd)) % 8)[xcd >= 0])
+    for x in range(8):
+        q = bc[xcd == x]
+        load = int(q.sum())
+        acc = np.cumsum(q)
+        cut = int(np.argmax(acc * 100 >= load * 60)) + 1 if load else len(q)
+        tail = q[cut:]
+        assert np.all(tail[:-1] >= tail[1:]), x
+    p.close()
