@@ -60,7 +60,7 @@ typedef enum {
   TREE_ATTN_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad plan  */
   TREE_ATTN_ERR_BAD_TREE = 2,     /* parent out of range, self loop, cycle  */
   TREE_ATTN_ERR_LAYOUT = 3,       /* segments overlap, leave gaps, len < 1  */
-  TREE_ATTN_ERR_UNSUPPORTED = 4,  /* head_dim, dtype or head counts         */
+  TREE_ATTN_ERR_UNSUPPORTED = 4,  /* head_dim, dtype, head counts, plan size */
   TREE_ATTN_ERR_WORKSPACE = 5,    /* workspace missing or too small         */
   TREE_ATTN_ERR_HIP = 6,          /* a HIP runtime call failed              */
   TREE_ATTN_ERR_NO_DEVICE_PLAN = 7, /* host-only plan passed to fwd/bwd     */
@@ -103,14 +103,20 @@ typedef struct tree_attn_plan_s* tree_attn_plan_t; /* opaque, immutable */
  * stored right after its parent continues the parent's run, and tiles are
  * cut over runs rather than single nodes, so packing the nodes in
  * depth-first preorder (as tree_attn_build_tree does) leaves fewer
- * part-filled tiles; any packing order gives the same results.  Its small
+ * part-filled tiles; any packing order gives the same results.  Another
+ * order costs plan size, though: a node's ancestor ranges merge only where
+ * they are stored back to back, and each side subtree adds a range to the
+ * key tiles above it, so a deep tree stored out of order needs about its
+ * depth in entries per tile.  Its small
  * device arrays are copied asynchronously on `stream`; the plan may be used
  * on any stream once `stream` has passed this point, and reused by any
  * number of fwd/bwd calls (e.g. every layer of a model).
  *
  * Returns BAD_TREE or LAYOUT for an invalid table, UNSUPPORTED when
  * head_dim is not 64 or 128, dtype is unknown, or num_q_heads is not a
- * positive multiple of num_kv_heads; INVALID_ARG for null pointers or
+ * positive multiple of num_kv_heads, and when the plan would hold more
+ * than 2^27 key-range entries (counted before anything is built: a deep
+ * tree stored out of depth-first order); INVALID_ARG for null pointers or
  * negative sizes; HIP when device allocation or copy fails.  *out is set
  * only on success.
  */

@@ -218,6 +218,66 @@ Status build_plan(const int32_t* parent, const int32_t* seg_start, const int32_t
   if (static_cast<int64_t>(order.size()) != m)
     return fail(err, Status::kBadTree, "parent pointers contain a cycle");
 
+  // ---- size guard.  Ancestor ranges merge only where a parent's segment
+  // ends where the next ancestor's begins, and a node's side subtrees (all
+  // children but the one stored right after it) each add a query range to
+  // the key tiles of its run.  Stored depth first, a tree needs a few
+  // entries per tile; stored in another order, a deep tree needs its depth
+  // per tile, quadratic in the node count.  Count the entries (O(M)) before
+  // building anything and refuse plans beyond kMaxRangeEntries.
+  {
+    std::vector<int64_t> nanc(m, 0), anc_end(m, -1), act_sub(m, 0);
+    for (int32_t i : order) {  // root first: ancestor range counts
+      const int32_t pa = parent[i];
+      if (pa < 0) continue;
+      const bool merged = nanc[pa] > 0 && anc_end[pa] == seg_start[pa];
+      nanc[i] = nanc[pa] + (merged ? 0 : 1);
+      anc_end[i] = static_cast<int64_t>(seg_start[pa]) + seg_len[pa];
+    }
+    for (size_t h = order.size(); h-- > 0;) {  // leaves first: query nodes below
+      const int32_t i = order[h];
+      act_sub[i] += active[i] ? 1 : 0;
+      if (parent[i] >= 0) act_sub[parent[i]] += act_sub[i];
+    }
+    int64_t fwd_entries = 0, bwd_ranges = 0;
+    std::vector<int64_t> side_cnt(m, 0);
+    for (int64_t i = 0; i < m; ++i) {
+      const int64_t end = static_cast<int64_t>(seg_start[i]) + seg_len[i];
+      for (int32_t c : children[i])
+        if (p.subset || seg_start[c] != end) side_cnt[i] += act_sub[c];
+      if (active[i])
+        fwd_entries += ((static_cast<int64_t>(seg_len[i]) + kFwdRows - 1) / kFwdRows) * (nanc[i] + 1);
+    }
+    // a key tile of a run collects the side ranges of the run's nodes from
+    // its own on: bounded by the run's tiles times the run's side ranges
+    for (int32_t r : order) {
+      const int32_t pa = parent[r];
+      const bool cont = !p.subset && pa >= 0 &&
+                        static_cast<int64_t>(seg_start[pa]) + seg_len[pa] == seg_start[r];
+      if (cont) continue;  // not the start of a run
+      int64_t len = 0, sides = 0;
+      for (int32_t c = r; c >= 0;) {
+        len += seg_len[c];
+        sides += side_cnt[c];
+        const int64_t end = static_cast<int64_t>(seg_start[c]) + seg_len[c];
+        int32_t nx = -1;
+        if (!p.subset)
+          for (int32_t cc : children[c])
+            if (seg_start[cc] == end) nx = cc;
+        c = nx;
+      }
+      bwd_ranges += ((len + kBwdKeys - 1) / kBwdKeys) * (sides + 1);
+      if (bwd_ranges > kMaxRangeEntries) break;
+    }
+    if (fwd_entries > kMaxRangeEntries || bwd_ranges * num_q_heads > kMaxRangeEntries) {
+      std::ostringstream os;
+      os << "the plan would hold " << std::max(fwd_entries, bwd_ranges * num_q_heads)
+         << " key-range entries (limit " << kMaxRangeEntries
+         << "): store each node's segment after its parent's (depth-first preorder)";
+      return fail(err, Status::kUnsupported, os.str());
+    }
+  }
+
   // ---- ancestor key ranges (root first, merged when contiguous) and depth
   // offsets, in root-first order so a parent is done before its children
   std::vector<std::vector<Range>> anc(m);

@@ -40,6 +40,10 @@ constexpr int kFwdFill = 1;      // forward workgroups per CU a split launch may
 constexpr int kFwdMaxParts = 16; // most parts one query tile's keys are split into
 constexpr int kFwdMinPartSteps = 16;  // fewest key steps a part of a split tile keeps
 constexpr int kFwdSplitSteps = 48;    // a plan splits only if a tile has this many key steps
+// Most key-range entries a plan may hold (forward ranges, backward entries).
+// A tree stored depth first needs a few per tile; one whose children are
+// not stored after their parents needs as many as its depth per tile.
+constexpr int64_t kMaxRangeEntries = int64_t{1} << 27;
 
 struct I4 {
   int32_t x, y, z, w;

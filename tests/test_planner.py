@@ -791,3 +791,35 @@ def test_longest_first_order_and_split_cap(t):
         tail = q[cut:]
         assert np.all(tail[:-1] >= tail[1:]), x
     p.close()
+
+
+def _two_token_chain(m, shuffle):
+    parent = np.arange(-1, m - 1, dtype=np.int32)
+    seg_len = np.full(m, 2, np.int32)
+    order = np.random.default_rng(5).permutation(m) if shuffle else np.arange(m)
+    seg_start = np.empty(m, np.int32)
+    seg_start[order] = 2 * np.arange(m, dtype=np.int32)
+    return parent, seg_start, seg_len, 2 * m
+
+
+def test_deep_tree_stored_out_of_order_is_refused_before_planning():
+    """A 40,000-node chain stored depth first plans in milliseconds; the same
+    chain in a shuffled order would need about 10^9 key-range entries (its
+    depth per tile) and is refused with UNSUPPORTED from an O(M) count,
+    before any list is built.  A 3,000-node shuffled chain is still
+    planned, and covered exactly (quadratic, but within the limit)."""
+    import time
+    par, st, ln, n = _two_token_chain(40000, False)
+    p = ta.plan_host(par, st, ln, n, 8, 2, 128, "bf16")
+    p.close()
+    par, st, ln, n = _two_token_chain(40000, True)
+    t0 = time.perf_counter()
+    with pytest.raises(ta.TreeAttnError) as ei:
+        ta.plan_host(par, st, ln, n, 8, 2, 128, "bf16")
+    assert ei.value.status == "UNSUPPORTED" and "depth-first" in str(ei.value)
+    assert time.perf_counter() - t0 < 5.0
+    par, st, ln, n = _two_token_chain(300, True)
+    _check_cover(NodeTable(par, st, ln, n, "shuffled-chain"), 2, 1, 256, None)
+    par, st, ln, n = _two_token_chain(3000, True)
+    p = ta.plan_host(par, st, ln, n, 2, 1, 128, "bf16")
+    p.close()
