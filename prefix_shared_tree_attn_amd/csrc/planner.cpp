@@ -747,18 +747,31 @@ Status walk_runs(const int32_t* parent, const int32_t* seg_len, int32_t num_node
   if (n_order != m) return fail(err, Status::kBadTree, "parent pointers contain a cycle");
   if (budget <= 0) budget = longest;
 
-  // greedy cut: mark[v] = the run whose resident set holds v.  In preorder
-  // the resident set is closed under taking parents, so the part of a new
-  // node's root path not yet resident is the stretch below its deepest
-  // resident ancestor.
-  std::vector<int32_t> mark(m, -1);
+  // greedy cut.  The nodes of a run are consecutive in preorder, so the
+  // part of a new node's root path that the run already holds is the root
+  // path of its lowest common ancestor with the previous node: no earlier
+  // node shares a deeper ancestor with it.  Walking up from the new node to
+  // that ancestor visits only nodes that preorder enters there, O(M) in all.
+  std::vector<int32_t> tin(m), sub(m, 0);
+  for (int64_t j = 0; j < m; ++j) tin[order[j]] = static_cast<int32_t>(j);
+  for (int64_t j = m - 1; j >= 0; --j) {
+    const int32_t v = order[j];
+    sub[v] += 1;
+    if (parent[v] >= 0) sub[parent[v]] += sub[v];
+  }
+  auto holds = [&](int32_t a, int32_t v) { return tin[a] <= tin[v] && tin[v] < tin[a] + sub[a]; };
   int32_t runs = 0;
   int64_t resident = 0;
   run_start[0] = 0;
   for (int64_t j = 0; j < m; ++j) {
     const int32_t v = order[j];
-    int64_t add = 0;
-    for (int32_t u = v; u >= 0 && mark[u] != runs - 1; u = parent[u]) add += seg_len[u];
+    int64_t add = path[v];
+    if (runs > 0) {
+      const int32_t prev = order[j - 1];
+      int32_t u = parent[v];
+      while (u >= 0 && !holds(u, prev)) u = parent[u];
+      add = path[v] - (u >= 0 ? path[u] : 0);
+    }
     if (runs == 0 || resident + add > budget) {
       // close the current run (if any) and open one at v
       if (runs > 0) run_start[runs] = static_cast<int32_t>(j);
@@ -766,7 +779,6 @@ Status walk_runs(const int32_t* parent, const int32_t* seg_len, int32_t num_node
       resident = 0;
       add = path[v];
     }
-    for (int32_t u = v; u >= 0 && mark[u] != runs - 1; u = parent[u]) mark[u] = runs - 1;
     resident += add;
   }
   run_start[runs] = static_cast<int32_t>(m);
