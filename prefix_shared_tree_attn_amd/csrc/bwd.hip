@@ -668,12 +668,20 @@ __global__ __launch_bounds__(256, 1) void tree_attn_dkdv_pipe_kernel(BwdArgs a) 
         static_cast<unsigned>(reinterpret_cast<__SIZE_TYPE__>(p)));
   };
   auto issue = [&](const LoadStep& l, int boff) __attribute__((always_inline)) {
-    const int rows = l.s.e < ee ? (l.s.qe - l.s.r0 < 32 ? l.s.qe - l.s.r0 : 32) : 0;
+    // rows of the step, at most 32; a step past the item's last entry has
+    // r0 = qe = 0 (step_at), and a cursor never stands at r0 > qe, so this
+    // is never negative and needs no test of the entry index
+    const uint32_t rows = static_cast<uint32_t>(min(l.s.qe - l.s.r0, 32));
+    const uint32_t nq = rows * row_bytes32;
     step_loads<TPER, C::TILE - (TPER - 1) * 1024>(
         lds_addr(lds + boff + C::Q_OFF + tl.lds0),
         lds_addr(wave < 2 ? lds + boff + rterm_off : lds + C::SPARE_OFF), tl.voff, 4 * lane,
-        tile_rsrc(l.q, rows, row_bytes32), tile_rsrc(l.d, rows, row_bytes32),
-        tile_rsrc(l.t, rows, 4));
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(l.q), static_cast<short>(0),
+                                          static_cast<int>(nq), kRsrcFlags),
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(l.d), static_cast<short>(0),
+                                          static_cast<int>(nq), kRsrcFlags),
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(l.t), static_cast<short>(0),
+                                          static_cast<int>(4 * rows), kRsrcFlags));
   };
 
   // this wave's K / V operands (B operands of S = Q K^T and dP = dO V^T)

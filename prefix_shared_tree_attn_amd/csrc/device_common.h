@@ -151,10 +151,16 @@ template <class TL>
 __device__ __forceinline__ bf16x8 tr_operand(const LDS_PTR(char) base, int row0, int col0,
                                              int lane) {
   const int grp = lane >> 4, L = lane & 15;
-  const int r = row0 + 8 * (grp >> 1) + (L >> 2);
-  const int c = col0 + 16 * (grp & 1) + 4 * (L & 3);
-  const bf16x4 lo = lds_read_tr(base, TL::elem_off(r, c));
-  const bf16x4 hi = lds_read_tr(base, TL::elem_off(r + 4, c));
+  // The lane's own row and column inside the 16 x 32 block, and the block's
+  // place: row0 (a multiple of 16) adds whole 64-byte rows without touching
+  // the swizzle, which depends on bits 2-3 of the row only, and col0 (a
+  // multiple of 32) whole sub-tiles.  Kept apart, the block's part folds
+  // into the reads' immediate offsets and the lane's part is computed once.
+  const int r = 8 * (grp >> 1) + (L >> 2);
+  const int c = 16 * (grp & 1) + 4 * (L & 3);
+  const LDS_PTR(char) b = base + row0 * 64 + (col0 >> 5) * TL::SUB;
+  const bf16x4 lo = lds_read_tr(b, TL::elem_off(r, c));
+  const bf16x4 hi = lds_read_tr(b, TL::elem_off(r + 4, c));
   bf16x8 out;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {

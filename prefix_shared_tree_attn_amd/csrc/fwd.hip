@@ -248,13 +248,13 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_kernel(FwdArgs a) {
     float pr[2][16], blk[4];
     auto soft = [&](float neg_m) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) blk[i] = 0.f;
-#pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           pr[kb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][v], a.scale_log2, neg_m));
-          blk[v & 3] += pr[kb][v];
+          // the four chains start from their first term, not from 0 + term
+          if (kb == 0 && v < 4) blk[v] = pr[kb][v];
+          else blk[v & 3] += pr[kb][v];
         }
     };
     soft(-m);

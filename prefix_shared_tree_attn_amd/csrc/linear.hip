@@ -102,7 +102,8 @@ __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 
 // read as transposed operands (the reduction runs over the tokens).  The
 // staging is not overlapped inside a workgroup; three resident workgroups
 // per CU (at most 170 registers a lane, with the accumulators kept in
-// ordinary VGPRs) overlap one another's loads instead.
+// ordinary VGPRs; the launch's LDS request keeps it from four) overlap one
+// another's loads instead.
 template <int D>
 __global__ __launch_bounds__(256, 3) void lin_outer_kernel(LinArgs a, int backward) {
   using T = Tile<D, CH>;
@@ -485,7 +486,12 @@ hipError_t launch_dyn(Kern kern, int64_t blocks, int bytes, hipStream_t s, const
 
 template <int D>
 hipError_t lin_outer_t(const LinArgs& a, int backward, hipStream_t s) {
-  const int bytes = 2 * Tile<D, CH>::BYTES;
+  // at D = 128 the kernel's registers would admit four workgroups per CU,
+  // which measured slower than three: the LDS request holds it to three
+  // (3 x 48 KiB fits the CU's 160 KiB, 4 x 48 KiB does not)
+  constexpr int kThreePerCu = 48 * 1024;
+  const int bytes = D == 128 ? kThreePerCu : 2 * Tile<D, CH>::BYTES;
+  static_assert(2 * Tile<128, CH>::BYTES <= kThreePerCu, "tiles fit the request");
   auto kern = lin_outer_kernel<D>;
   if (bytes > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
