@@ -75,6 +75,9 @@ CASES = {
     "forest": (_random(3, 10, 260, roots=3), 6, 2, 128, "bf16"),
     "gqa7": (_random(4, 7, 300), 7, 1, 128, "bf16"),
     "mha": (_random(5, 6, 250), 3, 3, 128, "bf16"),
+    # groups wider than the workloads' (16 query heads on one kv head)
+    "mqa16": (_random(9, 7, 260), 16, 1, 128, "bf16"),
+    "gqa12-d64": (_random(10, 6, 200), 24, 2, 64, "bf16"),
     "d64-bf16": (_random(6, 9, 300), 4, 2, 64, "bf16"),
     "d64-fp32": (_random(7, 8, 200), 2, 1, 64, "fp32"),
     "d128-fp32": (_random(8, 6, 200), 2, 2, 128, "fp32"),
